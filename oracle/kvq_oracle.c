@@ -1,0 +1,466 @@
+/*
+ * kvq_oracle.c -- plain, slow CPU oracle for the block-scaled 8-bit paged KV
+ * cache (quantize-on-store, dequantize, paged decode attention).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call this file:
+ * only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg load
+ * it.  It shares no code, header, table or constant with the HIP library.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [PR103]  "feat(kvcache): 8-bit KV cache (q8_0 / fp8_e4m3) behind
+ *            --kv-cache-dtype" (FreeToken pull request #103), and the
+ *            review comment on it ("A bug on sm_89: the fp8 store does not
+ *            round to nearest", "End-to-end numbers").
+ *   [PR113]  "feat(kvcache): 8-bit DSV4 window/compressed KV behind
+ *            --kv-cache-dtype" (FreeToken pull request #113).
+ *   [PR126]  "Add fp8 KV-cache quantization (--kv-dtype)" (FreeToken #126).
+ *   [PR25]   "Experimental FP8 KV Cache" (llama.cpp fork pull request #25).
+ *
+ * Precision: the pages fix the storage formats (e4m3 / int8 codes, an IEEE
+ * binary16 scale per 32 elements) but not the arithmetic of the quotient.
+ * The reading taken: the block max-abs is divided by the format maximum in
+ * IEEE fp32, rounded once more to fp16; each element is divided by that fp16
+ * scale in IEEE fp32 and the quotient is rounded onto the code grid.  Attention
+ * is computed in double over exactly dequantized K/V.
+ *
+ * Every rounding here goes through one definition, round_to_grid(), which is
+ * IEEE round-to-nearest-even onto a binary floating-point grid with p
+ * fraction bits and minimum normal exponent emin, done with exact double
+ * arithmetic and rint().  Build without -ffast-math and with
+ * -ffp-contract=off so that every float operation rounds as written.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define KVO_BF16 0
+#define KVO_FP8_E4M3 1
+#define KVO_Q8_0 2
+
+/* Quantization block length along head_dim, and the two format maxima:
+ * 448 is the largest finite e4m3 magnitude, 127 the int8 limit [PR103 §What;
+ * PR113 §What this adds]. */
+#define KVO_BLOCK 32
+#define KVO_E4M3_MAX 448.0f
+#define KVO_Q8_MAX 127.0f
+#define KVO_F16_MAX 65504.0
+
+/* ------------------------------------------------------------------------ */
+/* Rounding onto a binary floating-point grid.                               */
+/* ------------------------------------------------------------------------ */
+
+/* Round a >= 0 to the nearest value of a binary format with p fraction bits
+ * and minimum normal exponent emin (no upper limit is applied here), ties to
+ * the value whose last fraction bit is 0.  Below 2^emin the grid spacing is
+ * fixed at 2^(emin-p) (subnormals).  a / quantum is exact in double because
+ * the quantum is a power of two; rint() rounds half to even. */
+static double round_to_grid(double a, int p, int emin) {
+  if (a == 0.0) return 0.0;
+  int e;
+  frexp(a, &e); /* a = f * 2^e, f in [0.5, 1) */
+  e -= 1;       /* a = g * 2^e, g in [1, 2)   */
+  if (e < emin) e = emin;
+  double quantum = ldexp(1.0, e - p);
+  return rint(a / quantum) * quantum;
+}
+
+/* ---- IEEE binary16 ------------------------------------------------------ */
+
+/* fp16 bits -> value (exact). */
+double kvo_f16_value(uint16_t h) {
+  int s = h >> 15, e = (h >> 10) & 0x1f, m = h & 0x3ff;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24);
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp(1.0 + m / 1024.0, e - 15);
+  return s ? -v : v;
+}
+
+/* value -> fp16 bits, round to nearest even, overflow to infinity. */
+uint16_t kvo_f16_from_double(double x) {
+  uint16_t s = signbit(x) ? 0x8000 : 0;
+  double a = fabs(x);
+  if (isnan(x)) return 0x7e00;
+  double r = round_to_grid(a, 10, -14);
+  if (r >= 65536.0) return s | 0x7c00; /* rounds past the largest finite */
+  if (r < ldexp(1.0, -14)) return s | (uint16_t)(r * 16777216.0); /* m*2^-24 */
+  int e;
+  double f = frexp(r, &e); /* r = f*2^e, f in [0.5,1) */
+  int E = e - 1 + 15;
+  uint16_t m = (uint16_t)((f * 2.0 - 1.0) * 1024.0);
+  return s | (uint16_t)(E << 10) | m;
+}
+
+/* ---- bfloat16 (8-bit exponent, 7 fraction bits) -------------------------- */
+
+double kvo_bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* finite value -> bf16 bits, round to nearest even. */
+uint16_t kvo_bf16_from_double(double x) {
+  uint16_t s = signbit(x) ? 0x8000 : 0;
+  if (isnan(x)) return 0x7fc0;
+  double r = round_to_grid(fabs(x), 7, -126);
+  if (r >= ldexp(1.0, 128)) return s | 0x7f80;
+  if (r < ldexp(1.0, -126)) return s | (uint16_t)(r * ldexp(1.0, 133));
+  int e;
+  double f = frexp(r, &e);
+  int E = e - 1 + 127;
+  uint16_t m = (uint16_t)((f * 2.0 - 1.0) * 128.0);
+  return s | (uint16_t)(E << 7) | m;
+}
+
+/* ---- OCP fp8 e4m3fn ------------------------------------------------------
+ * Bias 7, 3 fraction bits, no infinities, 0x7F/0xFF are NaN, so the largest
+ * finite magnitude is 0x7E = 1.75*2^8 = 448 [PR103 §What: s = max/448].
+ * Normal codes: (1 + m/8) * 2^(e-7), e = 1..15; subnormal: m * 2^-9. */
+double kvo_e4m3_value(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 0xf, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Encode v (|v| <= 448, finite) as the nearest e4m3fn code, ties to the code
+ * with an even last fraction bit (round-to-nearest-even, the rounding the
+ * review comment on [PR103] says a correct store must do, §"A bug on sm_89").
+ * The sign is kept, so a negative value that rounds to zero encodes as 0x80. */
+uint8_t kvo_e4m3_encode(float v) {
+  uint8_t s = signbit(v) ? 0x80 : 0;
+  double r = round_to_grid(fabs((double)v), 3, -6);
+  if (r < ldexp(1.0, -6)) return s | (uint8_t)(r * 512.0); /* m * 2^-9 */
+  int e;
+  double f = frexp(r, &e);
+  int E = e - 1 + 7;
+  uint8_t m = (uint8_t)((f * 2.0 - 1.0) * 8.0);
+  return s | (uint8_t)(E << 3) | m;
+}
+
+/* ---- q8_0 ----------------------------------------------------------------
+ * Round half away from zero (the GGUF Q8_0 convention the review comment on
+ * [PR103] names, §"A bug on sm_89"), for |v| <= 127.  |v| + 0.5 is exact in
+ * double, so floor() gives the exact half-away result. */
+int8_t kvo_q8_encode(float v) {
+  double a = floor(fabs((double)v) + 0.5);
+  return (int8_t)(signbit(v) ? -a : a);
+}
+
+/* ---- block scale -----------------------------------------------------------
+ * s = max-abs / 448 (e4m3) or / 127 (q8_0), held as IEEE fp16 [PR103 §What;
+ * PR113 §What this adds].  Reading: fp32 division, then fp16 round-to-nearest-
+ * even; a quotient beyond the largest finite fp16 is held at 65504 so that
+ * the block saturates rather than becoming infinite.  Returns fp16 bits. */
+uint16_t kvo_block_scale(int qtype, float amax) {
+  float M = (qtype == KVO_Q8_0) ? KVO_Q8_MAX : KVO_E4M3_MAX;
+  float q = amax / M; /* IEEE fp32 division */
+  if ((double)q > KVO_F16_MAX) return 0x7bff;
+  return kvo_f16_from_double((double)q);
+}
+
+/* Quantize one block of n (= 32) bf16 values: the per-block max-abs gives the
+ * scale, each element is divided by the stored scale in fp32, clamped to the
+ * format maximum and rounded onto the code grid [PR103 §What and review
+ * §"A bug on sm_89" (clamp, then round)].  A zero scale (all-zero block, or a
+ * max-abs too small for fp16) stores all-zero codes. */
+void kvo_quantize_block(int qtype, const uint16_t* x, int n, uint8_t* codes,
+                        uint16_t* scale_out) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    float a = fabsf((float)kvo_bf16_value(x[i]));
+    if (a > amax) amax = a;
+  }
+  uint16_t sh = kvo_block_scale(qtype, amax);
+  *scale_out = sh;
+  float s = (float)kvo_f16_value(sh);
+  for (int i = 0; i < n; ++i) {
+    if (s == 0.0f) {
+      codes[i] = 0;
+      continue;
+    }
+    float xi = (float)kvo_bf16_value(x[i]);
+    float v = xi / s; /* IEEE fp32 division by the stored scale */
+    if (qtype == KVO_Q8_0) {
+      if (v > KVO_Q8_MAX) v = KVO_Q8_MAX;
+      if (v < -KVO_Q8_MAX) v = -KVO_Q8_MAX;
+      codes[i] = (uint8_t)kvo_q8_encode(v);
+    } else {
+      if (v > KVO_E4M3_MAX) v = KVO_E4M3_MAX;
+      if (v < -KVO_E4M3_MAX) v = -KVO_E4M3_MAX;
+      codes[i] = kvo_e4m3_encode(v);
+    }
+  }
+}
+
+/* Exact value of one stored element: decoded code times the fp16 scale.
+ * Both factors have few significant bits, so the product is exact in double
+ * (and in fp32).  bf16 pools store the value itself. */
+double kvo_element_value(int qtype, uint8_t code, uint16_t scale) {
+  if (qtype == KVO_Q8_0) return (double)(int8_t)code * kvo_f16_value(scale);
+  return kvo_e4m3_value(code) * kvo_f16_value(scale);
+}
+
+/* ------------------------------------------------------------------------ */
+/* A plain parallel-for over independent work units.                        */
+/* ------------------------------------------------------------------------ */
+
+typedef void (*kvo_unit_fn)(void* ctx, int64_t unit);
+typedef struct {
+  kvo_unit_fn fn;
+  void* ctx;
+  int64_t begin, end;
+} kvo_range;
+
+static void* kvo_run_range(void* p) {
+  kvo_range* r = (kvo_range*)p;
+  for (int64_t u = r->begin; u < r->end; ++u) r->fn(r->ctx, u);
+  return NULL;
+}
+
+static void kvo_parallel_for(int64_t n, int threads, kvo_unit_fn fn, void* ctx) {
+  if (threads < 1) threads = 1;
+  if (threads > 256) threads = 256;
+  if (threads == 1 || n < 2) {
+    for (int64_t u = 0; u < n; ++u) fn(ctx, u);
+    return;
+  }
+  pthread_t tid[256];
+  kvo_range rg[256];
+  int64_t per = (n + threads - 1) / threads;
+  int used = 0;
+  for (int t = 0; t < threads; ++t) {
+    int64_t b = t * per, e = b + per < n ? b + per : n;
+    if (b >= e) break;
+    rg[t].fn = fn;
+    rg[t].ctx = ctx;
+    rg[t].begin = b;
+    rg[t].end = e;
+    if (pthread_create(&tid[t], NULL, kvo_run_range, &rg[t]) != 0) {
+      kvo_run_range(&rg[t]); /* run inline if a thread cannot be made */
+      tid[t] = 0;
+    }
+    used = t + 1;
+  }
+  for (int t = 0; t < used; ++t)
+    if (tid[t]) pthread_join(tid[t], NULL);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Store: quantize rows of new tokens into the paged pool.                   */
+/* ------------------------------------------------------------------------ */
+/* Pool layout: codes [num_pages][n_heads][page_size][head_dim] (1 byte per
+ * element; 2 bytes of bf16 for KVO_BF16), scales [num_pages][n_heads]
+ * [page_size][head_dim/32] fp16 beside it [PR103 §What: parallel scale
+ * buffers; PR113 §What this adds: a single scale array beside the slab].
+ * A slot is page*page_size + offset; slot < 0 or >= capacity is skipped. */
+
+typedef struct {
+  int qtype;
+  const uint16_t* src;
+  int64_t token_stride;
+  const int32_t* slots;
+  int n_heads, head_dim, page_size;
+  int64_t num_pages;
+  uint8_t* pool;
+  uint16_t* scales;
+} kvo_store_ctx;
+
+static void kvo_store_unit(void* p, int64_t n) {
+  kvo_store_ctx* c = (kvo_store_ctx*)p;
+  int64_t slot = c->slots[n];
+  if (slot < 0 || slot >= c->num_pages * (int64_t)c->page_size) return;
+  int64_t page = slot / c->page_size, off = slot % c->page_size;
+  int nb = c->head_dim / KVO_BLOCK;
+  for (int h = 0; h < c->n_heads; ++h) {
+    const uint16_t* row = c->src + n * c->token_stride + (int64_t)h * c->head_dim;
+    int64_t r = (page * c->n_heads + h) * c->page_size + off; /* row index */
+    if (c->qtype == KVO_BF16) {
+      memcpy(c->pool + r * c->head_dim * 2, row, (size_t)c->head_dim * 2);
+      continue;
+    }
+    for (int j = 0; j < nb; ++j)
+      kvo_quantize_block(c->qtype, row + j * KVO_BLOCK, KVO_BLOCK,
+                         c->pool + r * c->head_dim + j * KVO_BLOCK, c->scales + r * nb + j);
+  }
+}
+
+void kvo_store(int qtype, const uint16_t* src, int64_t token_stride, const int32_t* slots,
+               int64_t n_tokens, int n_heads, int head_dim, int page_size, int64_t num_pages,
+               uint8_t* pool, uint16_t* scales, int threads) {
+  kvo_store_ctx c = {qtype, src, token_stride, slots, n_heads, head_dim, page_size,
+                     num_pages, pool, scales};
+  kvo_parallel_for(n_tokens, threads, kvo_store_unit, &c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dequantize rows gathered by slot: exact value, returned as double, or      */
+/* rounded once to bf16.  An invalid slot yields zeros.                       */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int qtype;
+  const uint8_t* pool;
+  const uint16_t* scales;
+  const int32_t* slots;
+  int n_heads, head_dim, page_size;
+  int64_t num_pages;
+  double* out_f64;
+  uint16_t* out_bf16;
+} kvo_deq_ctx;
+
+static double kvo_pool_value(int qtype, const uint8_t* pool, const uint16_t* scales,
+                             int64_t row, int head_dim, int d) {
+  if (qtype == KVO_BF16) {
+    uint16_t b;
+    memcpy(&b, pool + (row * head_dim + d) * 2, 2);
+    return kvo_bf16_value(b);
+  }
+  int nb = head_dim / KVO_BLOCK;
+  return kvo_element_value(qtype, pool[row * head_dim + d], scales[row * nb + d / KVO_BLOCK]);
+}
+
+static void kvo_deq_unit(void* p, int64_t n) {
+  kvo_deq_ctx* c = (kvo_deq_ctx*)p;
+  int64_t slot = c->slots[n];
+  int valid = slot >= 0 && slot < c->num_pages * (int64_t)c->page_size;
+  int64_t page = valid ? slot / c->page_size : 0, off = valid ? slot % c->page_size : 0;
+  for (int h = 0; h < c->n_heads; ++h) {
+    int64_t r = (page * c->n_heads + h) * c->page_size + off;
+    for (int d = 0; d < c->head_dim; ++d) {
+      double v = valid ? kvo_pool_value(c->qtype, c->pool, c->scales, r, c->head_dim, d) : 0.0;
+      int64_t o = (n * c->n_heads + h) * (int64_t)c->head_dim + d;
+      if (c->out_f64) c->out_f64[o] = v;
+      if (c->out_bf16) c->out_bf16[o] = kvo_bf16_from_double(v);
+    }
+  }
+}
+
+void kvo_dequant(int qtype, const uint8_t* pool, const uint16_t* scales, const int32_t* slots,
+                 int64_t n_tokens, int n_heads, int head_dim, int page_size, int64_t num_pages,
+                 double* out_f64, uint16_t* out_bf16, int threads) {
+  kvo_deq_ctx c = {qtype, pool, scales, slots, n_heads, head_dim, page_size, num_pages,
+                   out_f64, out_bf16};
+  kvo_parallel_for(n_tokens, threads, kvo_deq_unit, &c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Paged decode attention, one query token per sequence.                      */
+/* ------------------------------------------------------------------------ */
+/* For sequence b and query head h (kv head g = h / (Hq/Hkv)): the valid tokens
+ * are t < seq_len[b] whose page-table entry is a page id in [0, num_pages);
+ * a -1 (or any out-of-range) entry removes the whole page [PR113 §Testing:
+ * masked (-1) columns].  K and V rows are dequantized exactly (the scale runs
+ * along head_dim, the reduction dimension, so the values are formed before
+ * the dot product [PR103 §What]); z_t = sm_scale * q . k_t;
+ * o = sum_t softmax(z)_t v_t; lse = log sum_t exp(z_t).  For the shared MLA
+ * slab (v_pool == k_pool) V is the first head_dim_v elements of the same row
+ * [PR113 §What this adds; PR25, the SPARSE_MLA_DECODE shape D=576, Dv=512].
+ * No valid token: o = 0, lse = -inf.  Everything in double. */
+
+typedef struct {
+  int qtype;
+  const uint16_t* q;
+  const uint8_t *k_pool, *v_pool;
+  const uint16_t *k_scales, *v_scales;
+  const int32_t* page_table;
+  int64_t pt_stride;
+  const int32_t* seq_lens;
+  int batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, page_size, max_pages;
+  int64_t num_pages;
+  double sm_scale;
+  const int32_t* rows;
+  double* out;
+  double* lse;
+} kvo_dec_ctx;
+
+static void kvo_dec_unit(void* p, int64_t i) {
+  kvo_dec_ctx* c = (kvo_dec_ctx*)p;
+  int64_t row = c->rows ? c->rows[i] : i; /* row = b * Hq + h */
+  int b = (int)(row / c->n_q_heads), h = (int)(row % c->n_q_heads);
+  int g = h / (c->n_q_heads / c->n_kv_heads);
+  int64_t L = c->seq_lens[b];
+  int64_t cap = (int64_t)c->max_pages * c->page_size;
+  if (L > cap) L = cap;
+  if (L < 0) L = 0;
+  int shared = (c->v_pool == c->k_pool);
+  int v_row_dim = shared ? c->head_dim_qk : c->head_dim_v;
+  const uint16_t* qrow = c->q + row * (int64_t)c->head_dim_qk;
+  double* z = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  char* ok = (char*)malloc((size_t)(L > 0 ? L : 1));
+  double zmax = -INFINITY;
+  /* pass 1: scores */
+  for (int64_t t = 0; t < L; ++t) {
+    int64_t page = c->page_table[(int64_t)b * c->pt_stride + t / c->page_size];
+    ok[t] = page >= 0 && page < c->num_pages;
+    if (!ok[t]) continue;
+    int64_t r = (page * c->n_kv_heads + g) * c->page_size + t % c->page_size;
+    double dot = 0.0;
+    for (int d = 0; d < c->head_dim_qk; ++d)
+      dot += kvo_bf16_value(qrow[d]) *
+             kvo_pool_value(c->qtype, c->k_pool, c->k_scales, r, c->head_dim_qk, d);
+    z[t] = c->sm_scale * dot;
+    if (z[t] > zmax) zmax = z[t];
+  }
+  double* o = c->out + i * (int64_t)c->head_dim_v;
+  for (int d = 0; d < c->head_dim_v; ++d) o[d] = 0.0;
+  if (zmax == -INFINITY) { /* no valid token */
+    if (c->lse) c->lse[i] = -INFINITY;
+    free(z);
+    free(ok);
+    return;
+  }
+  /* pass 2: weights and the weighted sum of V */
+  double denom = 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    if (!ok[t]) continue;
+    int64_t page = c->page_table[(int64_t)b * c->pt_stride + t / c->page_size];
+    int64_t r = (page * c->n_kv_heads + g) * c->page_size + t % c->page_size;
+    double w = exp(z[t] - zmax);
+    denom += w;
+    for (int d = 0; d < c->head_dim_v; ++d)
+      o[d] += w * kvo_pool_value(c->qtype, c->v_pool, c->v_scales, r, v_row_dim, d);
+  }
+  for (int d = 0; d < c->head_dim_v; ++d) o[d] /= denom;
+  if (c->lse) c->lse[i] = zmax + log(denom);
+  free(z);
+  free(ok);
+}
+
+/* rows: optional list of (b * n_q_heads + h) to compute (NULL = all rows, in
+ * order); out: double [n_rows][head_dim_v]; lse: double [n_rows] or NULL. */
+void kvo_paged_decode(int qtype, const uint16_t* q, const uint8_t* k_pool,
+                      const uint16_t* k_scales, const uint8_t* v_pool, const uint16_t* v_scales,
+                      const int32_t* page_table, int64_t pt_stride, const int32_t* seq_lens,
+                      int batch, int n_q_heads, int n_kv_heads, int head_dim_qk, int head_dim_v,
+                      int page_size, int max_pages, int64_t num_pages, double sm_scale,
+                      const int32_t* rows, int64_t n_rows, double* out, double* lse, int threads) {
+  kvo_dec_ctx c = {qtype,      q,          k_pool,     v_pool,     k_scales,  v_scales,
+                   page_table, pt_stride,  seq_lens,   batch,      n_q_heads, n_kv_heads,
+                   head_dim_qk, head_dim_v, page_size, max_pages,  num_pages, sm_scale,
+                   rows,       out,        lse};
+  if (!rows) n_rows = (int64_t)batch * n_q_heads;
+  kvo_parallel_for(n_rows, threads, kvo_dec_unit, &c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Bulk helpers for tests: apply the scalar encoders to arrays.               */
+/* ------------------------------------------------------------------------ */
+
+void kvo_e4m3_encode_array(const float* v, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = kvo_e4m3_encode(v[i]);
+}
+void kvo_q8_encode_array(const float* v, int64_t n, int8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = kvo_q8_encode(v[i]);
+}

@@ -1,0 +1,425 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+None of these tests re-types the oracle's formulas.  The references are:
+closed forms of the formats, library routines (numpy's float16, torch's
+bfloat16 and float8_e4m3fn conversions), exact rational arithmetic
+(``fractions.Fraction``), exhaustive brute-force sweeps written independently
+in ``tests/pins/sweep.c``, and numbers the pages print (``tests/golden``).
+
+Page keys used in citations:
+  [PR103] "feat(kvcache): 8-bit KV cache (q8_0 / fp8_e4m3) behind --kv-cache-dtype"
+  [PR113] "feat(kvcache): 8-bit DSV4 window/compressed KV behind --kv-cache-dtype"
+"""
+import ctypes
+import math
+import os
+import subprocess
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = os.path.join(HERE, "golden", "page_facts.txt")
+
+
+def page_facts():
+    facts = {}
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = line.split()
+                facts[k] = float(v)
+    return facts
+
+
+FACTS = page_facts()
+
+
+# ---------------------------------------------------------------------------------
+# helpers (library conversions only)
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns via torch (round to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def e4m3_lib_value(codes: np.ndarray) -> np.ndarray:
+    """Decode e4m3fn codes with torch's float8_e4m3fn dtype."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def e4m3_lib_encode(v: np.ndarray) -> np.ndarray:
+    """Round fp32 values (|v| <= 448) to e4m3fn codes with torch's cast."""
+    t = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def f16_value(bits: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+@pytest.fixture(scope="module")
+def sweep_lib():
+    d = tempfile.mkdtemp(prefix="kvq_pins_")
+    so = os.path.join(d, "libsweep.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                    "-ffp-contract=off", "-o", so, os.path.join(HERE, "pins", "sweep.c"), "-lm"],
+                   check=True)
+    L = ctypes.CDLL(so)
+    L.sweep_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32)]
+    L.sweep_e4m3.restype = ctypes.c_int64
+    L.sweep_q8.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32)]
+    L.sweep_q8.restype = ctypes.c_int64
+    L.sweep_grid.argtypes = [ctypes.c_void_p]
+    return L
+
+
+def _fnptr(name):
+    return ctypes.cast(getattr(oracle.lib(), name), ctypes.c_void_p)
+
+
+# ---------------------------------------------------------------------------------
+# P1: the e4m3fn grid (closed form, library decoder, exhaustive encoder sweep)
+
+def test_e4m3_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = e4m3_lib_value(codes)
+    got = np.array([oracle.e4m3_value(int(c)) for c in codes])
+    nan = np.isnan(ref)
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_e4m3_grid_closed_form(sweep_lib):
+    vals = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
+    # 127 non-negative finite values, strictly increasing in code order
+    assert np.all(np.diff(vals) > 0)
+    assert vals[0x7E] == FACTS["fp8_scale_divisor"] == 448.0
+    assert vals[0x08] == 2.0 ** -6 and vals[0x01] == 2.0 ** -9
+    grid = np.zeros(127, dtype=np.float32)
+    sweep_lib.sweep_grid(grid.ctypes.data)
+    assert np.array_equal(grid.astype(np.float64), vals)
+
+
+def test_e4m3_encoder_exhaustive_over_fp32(sweep_lib):
+    """Every fp32 in [-448, 448] against the brute-force nearest-grid sweep."""
+    first = ctypes.c_uint32(0)
+    bad = sweep_lib.sweep_e4m3(_fnptr("kvo_e4m3_encode"), oracle.default_threads(),
+                               ctypes.byref(first))
+    assert bad == 0, "first mismatch at fp32 bits 0x%08x" % first.value
+
+
+def test_e4m3_encoder_targeted_cases():
+    enc = oracle.lib().kvo_e4m3_encode
+    # exact midpoints tie to the even code; one fp32 ulp either side goes to the nearer
+    for c in range(0x7E):
+        lo, hi = oracle.e4m3_value(c), oracle.e4m3_value(c + 1)
+        mid = np.float32((lo + hi) / 2)
+        even = c if c % 2 == 0 else c + 1
+        assert enc(float(mid)) == even
+        assert enc(float(np.nextafter(mid, np.float32(0)))) == c
+        assert enc(float(np.nextafter(mid, np.float32(1e9)))) == c + 1
+        assert enc(float(-mid)) == 0x80 | even
+    assert enc(0.0) == 0x00 and enc(-0.0) == 0x80
+    assert enc(448.0) == 0x7E and enc(-448.0) == 0xFE
+    assert enc(2.0 ** -10) == 0x00          # half the smallest subnormal: ties to 0
+    assert enc(2.0 ** -6) == 0x08           # smallest normal
+    assert enc(float(np.float32(2.0 ** -6 - 2.0 ** -10))) == 0x08  # subnormal rounds up into it
+
+
+def test_e4m3_encoder_matches_torch_cast_random():
+    rng = np.random.default_rng(11)
+    mag = np.exp2(rng.uniform(-12, np.log2(448.0), 400_000)).astype(np.float32)
+    v = np.where(rng.random(mag.size) < 0.5, -mag, mag).astype(np.float32)
+    v = np.clip(v, -448, 448).astype(np.float32)
+    assert np.array_equal(oracle.e4m3_encode(v), e4m3_lib_encode(v))
+
+
+# ---------------------------------------------------------------------------------
+# q8_0: round half away from zero [PR103 review, "A bug on sm_89"]
+
+def test_q8_encoder_exhaustive_over_fp32(sweep_lib):
+    first = ctypes.c_uint32(0)
+    bad = sweep_lib.sweep_q8(_fnptr("kvo_q8_encode"), oracle.default_threads(),
+                             ctypes.byref(first))
+    assert bad == 0, "first mismatch at fp32 bits 0x%08x" % first.value
+
+
+def test_q8_encoder_half_cases():
+    enc = oracle.lib().kvo_q8_encode
+    for k in range(127):
+        assert enc(k + 0.5) == k + 1 and enc(-(k + 0.5)) == -(k + 1)
+    # just below one half: 0, never 1 (the floor(q + 0.5) form would give 1 here)
+    assert enc(float(np.nextafter(np.float32(0.5), np.float32(0)))) == 0
+    assert enc(127.0) == 127 and enc(-127.0) == -127
+
+
+# ---------------------------------------------------------------------------------
+# fp16 and bf16 conversions against numpy / torch
+
+def test_f16_value_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = f16_value(bits)
+    got = np.array([oracle.f16_value(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_f16_rounding_matches_numpy():
+    L = oracle.lib()
+    rng = np.random.default_rng(5)
+    xs = list(np.exp2(rng.uniform(-26, 16.5, 20_000)) * rng.choice([-1, 1], 20_000))
+    # every midpoint between neighbouring positive fp16 values, and one double ulp either side
+    pos = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = (pos[:-1] + pos[1:]) / 2
+    sel = mids[:: 7]
+    xs += list(sel) + list(np.nextafter(sel, 0)) + list(np.nextafter(sel, np.inf))
+    xs = np.array(xs, dtype=np.float64)
+    ref = xs.astype(np.float16).view(np.uint16)
+    got = np.array([L.kvo_f16_from_double(float(x)) for x in xs], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_value_and_rounding_match_torch():
+    L = oracle.lib()
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([L.kvo_bf16_value(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and np.array_equal(got[~nan], ref[~nan])
+    rng = np.random.default_rng(6)
+    x = (np.exp2(rng.uniform(-130, 120, 50_000)) * rng.choice([-1, 1], 50_000)).astype(np.float32)
+    ref_b = bf16_bits(x)
+    got_b = np.array([L.kvo_bf16_from_double(float(v)) for v in x], dtype=np.uint16)
+    assert np.array_equal(got_b, ref_b)
+
+
+# ---------------------------------------------------------------------------------
+# P7: the block scale against exact rational rounding, for every bf16 max-abs
+
+def _exact_f16_rne(q: Fraction) -> Fraction:
+    if q == 0:
+        return Fraction(0)
+    e = math.floor(math.log2(q))
+    while Fraction(2) ** e > q:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= q:
+        e += 1
+    e = max(e, -14)
+    quantum = Fraction(2) ** (e - 10)
+    return round(q / quantum) * quantum  # Fraction.__round__ ties to even
+
+
+@pytest.mark.parametrize("qtype,M", [("fp8_e4m3", 448), ("q8_0", 127)])
+def test_block_scale_exact_for_every_bf16_max(qtype, M):
+    assert M == FACTS["fp8_scale_divisor" if qtype == "fp8_e4m3" else "q8_scale_divisor"]
+    L = oracle.lib()
+    qt = oracle.QTYPES[qtype]
+    bits = np.arange(1, 0x7F80, dtype=np.uint32).astype(np.uint16)  # positive finite bf16
+    amax = bf16_to_f32(bits)
+    mismatches = 0
+    for a in amax:
+        s_bits = L.kvo_block_scale(qt, float(a))
+        exact = _exact_f16_rne(Fraction(float(a)) / M)
+        if exact > 65504:
+            exact = Fraction(65504)  # saturating scale (the reading taken for overflow)
+        if Fraction(L.kvo_f16_value(s_bits)) != exact:
+            mismatches += 1
+    assert mismatches == 0
+
+
+# ---------------------------------------------------------------------------------
+# Block-level properties P2..P6, P9
+
+def _normal_blocks(n_blocks, seed):
+    rng = np.random.default_rng(seed)
+    return bf16_bits(rng.standard_normal((n_blocks, 32)).astype(np.float32))
+
+
+def _quantize_blocks(qtype, blocks_bf16):
+    n = blocks_bf16.shape[0]
+    pool = np.zeros((n, 32), dtype=np.uint8)
+    scales = np.zeros((n, 1), dtype=np.uint16)
+    oracle.store(qtype, blocks_bf16, np.arange(n, dtype=np.int32), 1, 32, 1, n, pool, scales)
+    return pool, scales[:, 0]
+
+
+def test_double_round_bug_is_caught_at_the_stated_rate():
+    """[PR103 review, "A bug on sm_89"]: a store that truncates fp32 -> fp16 and
+    then rounds to e4m3 collapses values just above a grid midpoint onto the
+    midpoint, which then ties to even: always downward, on about 0.4% of
+    elements.  Emulate that path with library conversions and measure it
+    against the oracle on the N(0,1) blocks the tests use."""
+    blocks = _normal_blocks(40_000, 3)
+    codes, s_bits = _quantize_blocks("fp8_e4m3", blocks)
+    x = bf16_to_f32(blocks)
+    s = f16_value(s_bits).astype(np.float32)[:, None]
+    v = np.clip(x / s, -448, 448).astype(np.float32)
+    h = v.astype(np.float16)  # round to nearest ...
+    over = np.abs(h.astype(np.float32)) > np.abs(v)  # ... then undo any step away from zero
+    h = np.where(over, np.nextafter(h, np.float16(0)), h)
+    bug = e4m3_lib_encode(h.astype(np.float32))
+    differ = bug != codes
+    rate = differ.mean() * 100
+    assert abs(rate - FACTS["double_round_disagree_pct"]) < 0.1, rate
+    # every disagreement is one code toward zero
+    mag_ok = (codes[differ] & 0x7F).astype(int) - (bug[differ] & 0x7F).astype(int)
+    assert np.all(mag_ok == 1)
+    assert np.all((codes[differ] & 0x80) == (bug[differ] & 0x80))
+
+
+@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0"])
+def test_block_max_encodes_to_format_max(qtype):
+    blocks = _normal_blocks(20_000, 4)
+    codes, s_bits = _quantize_blocks(qtype, blocks)
+    x = bf16_to_f32(blocks)
+    imax = np.argmax(np.abs(x), axis=1)
+    cmax = codes[np.arange(len(codes)), imax]
+    neg = x[np.arange(len(codes)), imax] < 0
+    if qtype == "fp8_e4m3":
+        assert np.all(cmax == np.where(neg, 0xFE, 0x7E))
+        sat = np.abs(x / f16_value(s_bits)[:, None]).max(axis=1) > 448
+    else:
+        c = cmax.view(np.int8)
+        assert np.all(c == np.where(neg, -127, 127))
+        sat = np.abs(x / f16_value(s_bits)[:, None]).max(axis=1) > 127
+    # the clamp is active whenever the fp16 scale rounded down: a sizeable share
+    assert 0.3 < sat.mean() < 0.6
+
+
+@pytest.mark.parametrize("qtype,M", [("fp8_e4m3", 448), ("q8_0", 127)])
+def test_constant_and_zero_blocks(qtype, M):
+    rng = np.random.default_rng(7)
+    cs = rng.standard_normal(2000).astype(np.float32)
+    cs = cs[np.abs(cs) > 0.03]
+    blocks = bf16_bits(np.repeat(cs[:, None], 32, axis=1))
+    blocks = np.concatenate([blocks, np.zeros((3, 32), np.uint16),
+                             np.full((1, 32), 0x8000, np.uint16)])  # +0 and -0 blocks
+    codes, s_bits = _quantize_blocks(qtype, blocks)
+    x = bf16_to_f32(blocks[:, 0]).astype(np.float64)
+    n = len(cs)
+    top = 0x7E if qtype == "fp8_e4m3" else 127
+    exp_code = np.where(x[:n] < 0, (0x80 | top) if qtype == "fp8_e4m3" else (-top) & 0xFF, top)
+    assert np.all(codes[:n] == exp_code[:, None])
+    expect_s = (np.abs(x[:n]).astype(np.float32) / np.float32(M)).astype(np.float16)
+    assert np.array_equal(s_bits[:n], expect_s.view(np.uint16))
+    assert np.all(codes[n:] == 0) and np.all(s_bits[n:] == 0)
+
+
+def test_on_grid_blocks_round_trip_exactly():
+    """Values already on the e4m3 grid times a power-of-two block scale, with
+    the block's max at 448 * scale, come back unchanged [PR113 §Why the
+    precision cost is small]; same for integers with a 127 on q8_0."""
+    rng = np.random.default_rng(8)
+    grid = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
+    for qtype in ("fp8_e4m3", "q8_0"):
+        blocks = []
+        for _ in range(500):
+            e = int(rng.integers(-10, 6))
+            if qtype == "fp8_e4m3":
+                g = rng.choice(grid, 32) * rng.choice([-1, 1], 32)
+                g[rng.integers(32)] = 448.0 * rng.choice([-1, 1])
+            else:
+                g = rng.integers(-127, 128, 32).astype(np.float64)
+                g[rng.integers(32)] = 127.0 * rng.choice([-1, 1])
+            blocks.append(np.ldexp(g, e))
+        x = np.array(blocks, dtype=np.float32)
+        bits = bf16_bits(x)
+        assert np.array_equal(bf16_to_f32(bits), x)  # exact in bf16
+        n = len(blocks)
+        pool = np.zeros((n, 32), np.uint8)
+        sc = np.zeros((n, 1), np.uint16)
+        slots = np.arange(n, dtype=np.int32)
+        oracle.store(qtype, bits, slots, 1, 32, 1, n, pool, sc)
+        back, _ = oracle.dequant(qtype, pool, sc, slots, 1, 32, 1, n)
+        assert np.array_equal(back[:, 0, :], x.astype(np.float64))
+
+
+@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0"])
+def test_error_bounds(qtype):
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((20_000, 32)).astype(np.float32)
+    x[rng.random(x.shape) < 0.002] *= 1e4
+    blocks = bf16_bits(x)
+    codes, s_bits = _quantize_blocks(qtype, blocks)
+    xs = bf16_to_f32(blocks).astype(np.float64)
+    s = f16_value(s_bits)[:, None]
+    n = len(codes)
+    back, _ = oracle.dequant(qtype, codes, s_bits[:, None].copy(), np.arange(n, dtype=np.int32),
+                             1, 32, 1, n)
+    err = np.abs(back[:, 0, :] - xs)
+    if qtype == "fp8_e4m3":
+        q = np.abs(e4m3_lib_value(codes))
+        normal = q >= 2.0 ** -6
+        sat_excess = np.maximum(np.abs(xs) - 448 * s, 0)
+        bound = np.where(normal, 2.0 ** -4 * q * s, 2.0 ** -10 * s) + sat_excess
+    else:
+        bound = s / 2 + 127 * 2.0 ** -11 * s
+    assert np.all(err <= bound * (1 + 1e-12))
+
+
+def test_bytes_per_element_from_the_format():
+    """1 code byte + 2 scale bytes per 32 elements = 17/16 = 1.0625 B [PR103 §What]."""
+    per = Fraction(1) + Fraction(int(FACTS["scale_bits"]) // 8, int(FACTS["block_elems"]))
+    assert per == Fraction(int(FACTS["bytes_per_elem_num"]), int(FACTS["bytes_per_elem_den"]))
+    # measured pool growth bf16 -> 8-bit [PR103 review, "End-to-end numbers"]: the ratio
+    # 2 / (17/16) predicts the 8-bit token count to within one 16-token page
+    pred = FACTS["pool_tokens_bf16"] * Fraction(2) / per
+    assert abs(float(pred) - FACTS["pool_tokens_8bit"]) < 16
+
+
+@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0"])
+def test_exact_ties_inside_blocks_round_to_even(qtype):
+    """Elements whose quotient x / s lands exactly on a midpoint between two
+    codes must take the even code (e4m3) or the code away from zero (q8_0).
+    For e4m3 the scale s = 1.5 * 2^k or 1.75 * 2^k has at most three
+    significant bits, so every m * s (m has at most 5) is exact in bf16 and
+    the tie is exact, while 1/s is not exact (for 1.75 its fp32 rounding error
+    is 3/4 of an ulp), so a reciprocal-multiply shortcut misses some ties.
+    q8_0 midpoints have up to 8 significant bits, so there s = 2^k."""
+    rng = np.random.default_rng(12)
+    M = 448.0 if qtype == "fp8_e4m3" else 127.0
+    if qtype == "fp8_e4m3":
+        grid = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
+        mids = (grid[:-1] + grid[1:]) / 2
+        lower_codes = np.arange(0x7E)
+    else:
+        mids = np.arange(127) + 0.5
+        lower_codes = np.arange(127)
+    blocks, expect = [], []
+    for _ in range(400):
+        k = int(rng.integers(-12, 4))
+        s = (rng.choice([1.5, 1.75]) if qtype == "fp8_e4m3" else 1.0) * 2.0 ** k
+        idx = rng.integers(0, len(mids), 31)
+        sign = rng.choice([-1.0, 1.0], 31)
+        # the block max must make the fp16 scale exactly s: amax = M * s
+        x = np.concatenate([[M * s], sign * mids[idx] * s])
+        blocks.append(x)
+        if qtype == "fp8_e4m3":
+            c = lower_codes[idx] + (lower_codes[idx] % 2)  # even neighbour
+            c = np.where(sign < 0, 0x80 | c, c)
+            expect.append(np.concatenate([[0x7E], c]).astype(np.uint8))
+        else:
+            c = (lower_codes[idx] + 1) * sign  # away from zero
+            expect.append(np.concatenate([[127], c]).astype(np.int8).view(np.uint8))
+    x = np.array(blocks, dtype=np.float32)
+    bits = bf16_bits(x)
+    assert np.array_equal(bf16_to_f32(bits), x)
+    codes, s_bits = _quantize_blocks(qtype, bits)
+    assert np.all(f16_value(s_bits) == x[:, 0] / M)
+    assert np.array_equal(codes, np.array(expect))
