@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the block-scaled 8-bit paged KV cache on one MI355X.
+
+One step = one decode token for every sequence through a 28-layer attention
+stack of the Qwen3-1.7B shape (16 query / 8 KV heads, head_dim 128): for each
+layer, the quantize-on-store of the new token's K and V (one fused kvq_store)
+followed by paged decode attention over that layer's pool (kvq_paged_decode),
+batch 8 x 16384-token contexts, page size 16, random-permutation page tables,
+fp8_e4m3 block-32 codes with fp16 scales.  The 28 layers are 28 distinct
+copies of one layer's pool (7.99 GB in all), so every step streams the whole
+KV cache from HBM rather than from the 256 MB Infinity Cache.
+
+Prints one JSON line: `value` is the step's algorithmic bytes (codes + scales
+of every token read, Q, O, page-table entries, and the store's bf16 reads and
+code/scale writes) per second, in GB/s; `roofline` is the decode call (split
+kernel + combine) against the 8 TB/s HBM peak, timed with HIP events on the
+stream the kernels run on; `cpu_baseline` is the CPU oracle on one layer of
+the same workload, timed on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0
+METRIC = "fp8 paged-decode effective HBM GB/s (% of peak) + store GB/s, 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def store_bytes(n_tokens, n_heads, head_dim, qtype, tensors=2):
+    per = {"bf16": 2.0, "fp8_e4m3": 1 + 1 / 16, "q8_0": 1 + 1 / 16}[qtype]
+    return int(tensors * n_tokens * n_heads * head_dim * (2 + per)) + 4 * n_tokens
+
+
+def cpu_baseline(wl, qtype, k_rows, v_rows, q_bits):
+    """The oracle, as it stands, on one layer of the workload: store every slot
+    of the pool, then decode all rows.  Reports the decode part in GB/s."""
+    import oracle
+    from paged_decode_attention_amd import workloads as W
+    threads = oracle.default_threads()
+    H, D = wl.n_kv_heads, wl.head_dim_qk
+    slots = np.arange(wl.n_slots, dtype=np.int32)
+    code_t = np.uint16 if qtype == "bf16" else np.uint8
+    kp = np.zeros((wl.num_pages, H, W.PAGE, D), code_t)
+    vp = np.zeros_like(kp)
+    ks = None if qtype == "bf16" else np.zeros((wl.num_pages, H, W.PAGE, D // 32), np.uint16)
+    vs = None if ks is None else np.zeros_like(ks)
+    t0 = time.perf_counter()
+    oracle.store(qtype, k_rows, slots, H, D, W.PAGE, wl.num_pages, kp, ks, threads=threads)
+    oracle.store(qtype, v_rows, slots, H, D, W.PAGE, wl.num_pages, vp, vs, threads=threads)
+    t1 = time.perf_counter()
+    oracle.paged_decode(qtype, q_bits, kp, ks, vp, vs, wl.page_table, wl.seq_lens, H, D, D,
+                        W.PAGE, wl.num_pages, wl.sm_scale, threads=threads)
+    t2 = time.perf_counter()
+    dec_bytes = wl.algorithmic_bytes(qtype)
+    fill_bytes = store_bytes(wl.n_slots, H, D, qtype)
+    return {
+        "value": round(dec_bytes / (t2 - t1) / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": ("one of the 28 layers: decode of all %d sequences x %d heads over %d tokens "
+                   "each (%.3f s, %.1f MB algorithmic); the oracle's fill of that layer's pool "
+                   "took %.3f s (%.3f GB/s)" % (wl.batch, wl.n_q_heads, int(wl.seq_lens[0]),
+                                                t2 - t1, dec_bytes / 1e6, t1 - t0,
+                                                fill_bytes / (t1 - t0) / 1e9)),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--qtype", default="fp8_e4m3", choices=["fp8_e4m3", "q8_0", "bf16"])
+    ap.add_argument("--layers", type=int, default=28)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU form (each GPU would "
+              "run the same kernels on its own sequences or KV heads); run with --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from paged_decode_attention_amd import kvq
+    from paged_decode_attention_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    qtype = args.qtype
+    wl = W.qwen3(replicas=args.layers)
+    L, B, H, D = wl.layer_replicas, wl.batch, wl.n_kv_heads, wl.head_dim_qk
+    log("workload", wl.name, "layers", L, "qtype", qtype)
+
+    # ---- inputs, resident in HBM before timing ---------------------------------------
+    k_rows = wl.kv_rows(0, 0, wl.n_slots)
+    v_rows = wl.kv_rows(1, 0, wl.n_slots)
+    q_bits = wl.query()
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+
+    d_k, d_v = dev_bf16(k_rows), dev_bf16(v_rows)
+    d_slots = torch.arange(wl.n_slots, dtype=torch.int32, device=dev)
+    pools = []
+    for layer in range(L):
+        kp, ks = kvq.alloc_pool(qtype, wl.num_pages, H, D, device=dev)
+        vp, vs = kvq.alloc_pool(qtype, wl.num_pages, H, D, device=dev)
+        kvq.store(qtype, d_k, d_v, d_slots, kp, ks, vp, vs)
+        pools.append((kp, ks, vp, vs))
+    torch.cuda.synchronize()
+    del d_k, d_v, d_slots
+    q = dev_bf16(q_bits)
+    pt = torch.from_numpy(wl.page_table).to(dev)
+    sl = torch.from_numpy(wl.seq_lens).to(dev)
+    # the new token of each sequence is its last position; K/V rows per layer
+    rng = np.random.Generator(np.random.PCG64([wl.seed, 55]))
+    last = wl.seq_lens.astype(np.int64) - 1
+    new_slots = torch.from_numpy(
+        (wl.page_table[np.arange(B), last // W.PAGE].astype(np.int64) * W.PAGE + last % W.PAGE)
+        .astype(np.int32)).to(dev)
+    new_kv = [dev_bf16(W.to_bf16_bits(rng.standard_normal((2, B, H, D), dtype=np.float32)))
+              for _ in range(L)]
+    ws = None
+    stores, decodes = [], []
+    for layer in range(L):
+        kp, ks, vp, vs = pools[layer]
+        stores.append(kvq.PreparedStore(qtype, new_kv[layer][0], new_kv[layer][1], new_slots,
+                                        kp, ks, vp, vs))
+        d = kvq.PreparedDecode(qtype, q, kp, ks, vp, vs, pt, sl, wl.sm_scale, workspace=ws)
+        ws = d.workspace
+        decodes.append(d)
+
+    dec_bytes = wl.algorithmic_bytes(qtype)
+    st_bytes = store_bytes(B, H, D, qtype)
+    step_bytes = L * (dec_bytes + st_bytes)
+
+    def step(ev=None, s=None):
+        for layer in range(L):
+            if ev is not None:
+                ev[s][layer][0].record()
+            stores[layer]()
+            if ev is not None:
+                ev[s][layer][1].record()
+            decodes[layer]()
+            if ev is not None:
+                ev[s][layer][2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L)]
+          for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(K):
+        step(ev, s)
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / K
+    dec_ms = [ev[s][l][1].elapsed_time(ev[s][l][2]) for s in range(K) for l in range(L)]
+    st_ms = [ev[s][l][0].elapsed_time(ev[s][l][1]) for s in range(K) for l in range(L)]
+    dec_avg = float(np.mean(dec_ms))
+    st_avg = float(np.mean(st_ms))
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = dec_bytes / (dec_avg * 1e-3) / 1e9
+    log("step %.3f ms, decode call %.2f us, store call %.2f us" % (ms_step, dec_avg * 1e3,
+                                                                   st_avg * 1e3))
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode step, %d layers x (store 1 new token + paged decode), batch %d "
+                        "x %d-token contexts, %d q / %d kv heads, head_dim %d, page 16, "
+                        "random-permutation page tables (%s)" % (L, B, int(wl.seq_lens[0]),
+                                                                 wl.n_q_heads, H, D, wl.name),
+            "kv_storage": qtype + ("" if qtype == "bf16" else ", fp16 scale per 32 elements"),
+            "layers": L,
+            "batch": B,
+            "context": int(wl.seq_lens[0]),
+            "kv_bytes_per_step": L * dec_bytes,
+        },
+        "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
+        "tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "decode_call_us": round(dec_avg * 1e3, 3),
+        "store_call_us": round(st_avg * 1e3, 3),
+        "store_gbps": round(st_bytes / (st_avg * 1e-3) / 1e9, 3),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kvq_paged_decode (gqa_split_kernel + combine_kernel)",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": dec_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(wl, qtype, k_rows, v_rows, q_bits)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,194 @@
+/*
+ * kvq.h -- C ABI of libkvq.so: a block-scaled 8-bit paged KV cache for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * K/V rows are stored as 8-bit codes (OCP fp8 e4m3fn, or int8 "q8_0") with one
+ * IEEE fp16 scale per 32 consecutive elements along head_dim, 17/16 bytes per
+ * element against 2 for bf16; the quantize-on-store kernel writes them, and
+ * the paged decode-attention kernel reads them back through a page table,
+ * dequantizing before the dot products because the scale varies along the
+ * reduction dimension.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [PR103] "feat(kvcache): 8-bit KV cache (q8_0 / fp8_e4m3) behind
+ *           --kv-cache-dtype" (FreeToken #103) and the review comment on it.
+ *   [PR113] "feat(kvcache): 8-bit DSV4 window/compressed KV behind
+ *           --kv-cache-dtype" (FreeToken #113).
+ *   [PR126] "Add fp8 KV-cache quantization (--kv-dtype)" (FreeToken #126).
+ *   [PR25]  "Experimental FP8 KV Cache" (llama.cpp fork #25).
+ *
+ * Conventions for every call:
+ *   - Pointers marked "device" point to GPU memory the caller allocated and
+ *     owns; the library never allocates, frees or synchronizes, and keeps no
+ *     state between calls other than the thread-local error message.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs asynchronously; results are valid once the stream reaches it.
+ *   - Arguments are validated on the host before anything is launched; a call
+ *     that returns an error has enqueued nothing and written nothing.  The
+ *     message is available from kvq_last_error() on the calling thread.
+ *   - Values that live in device memory (slots, page ids, sequence lengths)
+ *     cannot be checked without a synchronization; the kernels instead skip
+ *     what is out of range, as documented per argument.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+/* A HIP stream (the same type as hipStream_t). */
+typedef struct ihipStream_t* kvq_stream_t;
+
+/* Storage type of a pool.  KVQ_BF16 stores rows unchanged (no scales); the
+ * two 8-bit types share one scale layout, store kernel and dequant path
+ * [PR103 §What]. */
+typedef enum {
+  KVQ_BF16 = 0,     /* 2 bytes per element, no scale buffer                     */
+  KVQ_FP8_E4M3 = 1, /* e4m3fn codes, scale = max|x| / 448 per 32-block          */
+  KVQ_Q8_0 = 2      /* int8 codes in [-127, 127], scale = max|x| / 127          */
+} kvq_dtype;
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = -1,         /* a bad argument (null pointer, bad size, ...)       */
+  KVQ_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement      */
+  KVQ_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required         */
+  KVQ_ERR_HIP = -4          /* the HIP runtime reported an error at launch        */
+} kvq_status;
+
+/* Elements per scale block along head_dim [PR103 §What; PR113 §What this adds]. */
+#define KVQ_BLOCK 32
+
+/* ---------------------------------------------------------------------------
+ * Pool layout (fixed; the pages give none):
+ *   codes : [num_pages][n_heads][page_size][head_dim], 1 byte per element
+ *           (2 bytes of bf16 for KVQ_BF16); each (page, head) chunk of
+ *           page_size rows is contiguous.
+ *   scales: [num_pages][n_heads][page_size][head_dim / 32] fp16 (IEEE binary16
+ *           bit patterns), a separate buffer beside the codes [PR103 §What:
+ *           parallel scale buffers; PR113 §What this adds: one scale array
+ *           beside the single MLA slab].
+ * A token lives at slot = page * page_size + offset.  For the MLA latent slab
+ * (one KV head, K and V the same row) n_heads = 1 and head_dim = 576.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of one pool (codes + scales) for one of K or V.  This is the cost
+ * model: the caller should size allocations and token budgets with this same
+ * function, so that the budget and the pool cannot disagree [PR113 §One
+ * ordering trap worth knowing about; PR103 §What: unit_bytes()/kv_cost() on
+ * effective bytes].  Host-only, pure.  *code_bytes and *scale_bytes (each
+ * nullable) receive the two parts; scale bytes are 0 for KVQ_BF16.
+ * Returns -1 (and sets the error message) on invalid arguments:
+ * num_pages < 0, page_size < 1, n_heads < 1, head_dim < 1, head_dim not a
+ * multiple of 32 for an 8-bit type, or an unknown dtype. */
+int64_t kvq_pool_bytes(kvq_dtype dtype, int64_t num_pages, int page_size, int n_heads,
+                       int head_dim, int64_t* code_bytes, int64_t* scale_bytes);
+
+/* Quantize-on-store [PR103 §What: store kernel, per-block max-abs -> codes +
+ * scales; review §"A bug on sm_89": clamp, then round to nearest even for
+ * e4m3, half away from zero for q8_0; PR113 §What this adds].
+ *
+ * For every token n with a valid slot and every head h, each 32-element block
+ * x of row src[n][h] is stored as
+ *     s = fp16_rne(fp32(max|x| / M)), M = 448 (e4m3) or 127 (q8_0),
+ *         held at 65504 if the quotient exceeds it;
+ *     code_i = round(clamp(fp32(x_i / s), -M, M)), e4m3: nearest even,
+ *         q8_0: half away from zero; s == 0 gives all-zero codes.
+ * Both quotients are IEEE fp32 divisions; the result is bit-exact and
+ * deterministic.  KVQ_BF16 copies the row unchanged.
+ *
+ *   k_src, v_src : device, bf16 [n_tokens][..] rows; head h of token n starts
+ *                  at element n * src_token_stride + h * head_dim.  v_src may
+ *                  be NULL (then v_pool / v_scales are ignored): this stores
+ *                  only K, e.g. the single MLA slab.  Both must be 16-byte
+ *                  aligned and src_token_stride a multiple of 8 elements,
+ *                  at least n_heads * head_dim.
+ *   slot_mapping : device int32 [n_tokens]; slot < 0 or >= num_pages *
+ *                  page_size is skipped.  Two tokens with the same slot in
+ *                  one call leave that slot undefined.
+ *   k_pool/v_pool, k_scales/v_scales : device, layout above; scales are
+ *                  ignored (may be NULL) for KVQ_BF16.
+ * Supported: head_dim a multiple of 32 (any multiple of 8 for KVQ_BF16) up
+ * to 1024, n_heads >= 1, page_size 1..1024, n_tokens >= 0 (0 is a no-op).
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_HIP. */
+int kvq_store(kvq_dtype dtype, const void* k_src, const void* v_src,
+              int64_t src_token_stride, const int32_t* slot_mapping, int64_t n_tokens,
+              int n_heads, int head_dim, int page_size, int64_t num_pages, void* k_pool,
+              uint16_t* k_scales, void* v_pool, uint16_t* v_scales, kvq_stream_t stream);
+
+/* Gather-dequantize rows to bf16 [PR103 §What: dequant path; PR126 §How it
+ * works: dequantize on read].  out[n][h][d] = bf16_rne(code * s) for the row
+ * at slot_mapping[n]; an invalid slot gives a row of zeros.  code * s is exact
+ * in fp32, so the only rounding is the final one to bf16.
+ *   pool, scales : device, layout above (scales ignored for KVQ_BF16).
+ *   out_bf16     : device bf16 [n_tokens][n_heads][head_dim], 16-byte aligned.
+ * Supported and errors as kvq_store. */
+int kvq_dequant(kvq_dtype dtype, const void* pool, const uint16_t* scales,
+                const int32_t* slot_mapping, int64_t n_tokens, int n_heads, int head_dim,
+                int page_size, int64_t num_pages, void* out_bf16, kvq_stream_t stream);
+
+/* Workspace bytes kvq_paged_decode needs for these shapes (split-K partial
+ * results).  0 if the shapes are invalid (see kvq_paged_decode). Host-only. */
+size_t kvq_paged_decode_workspace_bytes(kvq_dtype dtype, int batch, int n_q_heads,
+                                        int n_kv_heads, int head_dim_qk, int head_dim_v,
+                                        int page_size, int max_pages);
+
+/* Paged decode attention: one bf16 query token per sequence against the
+ * quantized pool [PR103 §What: dequant inside the attention kernels behind a
+ * QUANT switch, K/V dequantized before the dot because the scale runs along
+ * head_dim; PR113 §Testing: split-k decode kernel, masked (-1) columns].
+ *
+ * For sequence b and query head h, with kv head g = h / (n_q_heads /
+ * n_kv_heads), the valid tokens are t < min(seq_lens[b], max_pages *
+ * page_size) whose page id page_table[b][t / page_size] lies in
+ * [0, num_pages); any other id (-1 in particular) removes that page.  With
+ * k_t, v_t the dequantized rows of head g,
+ *     z_t = sm_scale * q[b][h] . k_t,
+ *     out[b][h] = sum_t softmax(z)_t v_t     (bf16),
+ *     lse[b][h] = log sum_t exp(z_t)         (fp32, natural log).
+ * No valid token: out = 0, lse = -inf.
+ *
+ *   q          : device bf16 [batch][n_q_heads][head_dim_qk], 16-byte aligned.
+ *   k_pool/v_pool, k_scales/v_scales : device, layout above, head_dim =
+ *                head_dim_qk for K and head_dim_v for V.  The shared MLA slab
+ *                [PR113 §What this adds; PR25, the SPARSE_MLA_DECODE shape]:
+ *                pass v_pool == k_pool and v_scales == k_scales with
+ *                n_kv_heads = 1; V is then the first head_dim_v elements of
+ *                each K row.
+ *   page_table : device int32 [batch][pt_stride]; columns >= max_pages are
+ *                never read.
+ *   seq_lens   : device int32 [batch]; negative counts as 0.
+ *   out_bf16   : device bf16 [batch][n_q_heads][head_dim_v].
+ *   lse        : device fp32 [batch][n_q_heads], or NULL.
+ *   workspace  : device, at least kvq_paged_decode_workspace_bytes() bytes,
+ *                256-byte aligned, zero-filled before its first use.  It
+ *                holds split-K partial results and per-(sequence, kv head)
+ *                arrival counters; every completed call leaves the counters
+ *                at zero again, so a workspace is zeroed once, not per call.
+ *                Calls that share a workspace must not overlap.
+ * Supported: page_size 16; separate K/V with head_dim_qk == head_dim_v in
+ * {32, 64, 128, 256} and any n_q_heads a multiple of n_kv_heads; the shared
+ * slab with head_dim_qk 576, head_dim_v 512, n_kv_heads 1 and n_q_heads a
+ * multiple of 16 up to 128; batch 1..4096; max_pages >= 1.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP. */
+int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
+                     const uint16_t* k_scales, const void* v_pool, const uint16_t* v_scales,
+                     const int32_t* page_table, int64_t pt_stride, const int32_t* seq_lens,
+                     int batch, int n_q_heads, int n_kv_heads, int head_dim_qk, int head_dim_v,
+                     int page_size, int max_pages, int64_t num_pages, float sm_scale,
+                     void* out_bf16, float* lse, void* workspace, size_t workspace_bytes,
+                     kvq_stream_t stream);
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,338 @@
+// kvq_api.cpp -- host entry points of libkvq.so: argument validation, split
+// planning, workspace layout and kernel launches.  Everything here runs on
+// the host; validation finishes before any HIP call, so a rejected call
+// touches neither the device nor the stream.
+//
+// Sources: [PR113] "feat(kvcache): 8-bit DSV4 window/compressed KV behind
+// --kv-cache-dtype" §Gating (reject up front with a clear message: head_dim a
+// multiple of the 32-element block) and §One ordering trap worth knowing
+// about (the cost model must agree with the pool); [PR103] "feat(kvcache):
+// 8-bit KV cache (q8_0 / fp8_e4m3) behind --kv-cache-dtype" §What (effective
+// bytes per element, gating) and its review comment §Gating; [PR126] "Add fp8
+// KV-cache quantization (--kv-dtype)" §Scope / limitations (refuse unsupported
+// requests with a clear error rather than corrupt the cache).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return KVQ_OK;
+}
+
+bool known_dtype(int d) { return d == KVQ_BF16 || d == KVQ_FP8_E4M3 || d == KVQ_Q8_0; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(KVQ_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+int num_cus_current() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Shared by kvq_store and kvq_dequant.
+int check_rows(int dtype, int64_t n_tokens, int n_heads, int head_dim, int page_size,
+               int64_t num_pages, const char* fn) {
+  if (!known_dtype(dtype)) return fail(KVQ_ERR_ARG, "%s: unknown dtype %d", fn, dtype);
+  if (n_tokens < 0) return fail(KVQ_ERR_ARG, "%s: n_tokens %lld < 0", fn, (long long)n_tokens);
+  if (n_heads < 1) return fail(KVQ_ERR_ARG, "%s: n_heads %d < 1", fn, n_heads);
+  if (head_dim < 1 || head_dim > 1024)
+    return fail(KVQ_ERR_ARG, "%s: head_dim %d outside 1..1024", fn, head_dim);
+  if (dtype != KVQ_BF16 && head_dim % KVQ_BLOCK != 0)
+    return fail(KVQ_ERR_ARG,
+                "%s: head_dim %d is not a multiple of the %d-element quantization block", fn,
+                head_dim, KVQ_BLOCK);
+  if (dtype == KVQ_BF16 && head_dim % 8 != 0)
+    return fail(KVQ_ERR_ARG, "%s: head_dim %d is not a multiple of 8", fn, head_dim);
+  if (page_size < 1 || page_size > 1024)
+    return fail(KVQ_ERR_ARG, "%s: page_size %d outside 1..1024", fn, page_size);
+  if (num_pages < 0) return fail(KVQ_ERR_ARG, "%s: num_pages < 0", fn);
+  if (num_pages * (int64_t)page_size > INT32_MAX)
+    return fail(KVQ_ERR_ARG, "%s: pool capacity exceeds 2^31-1 slots", fn);
+  return KVQ_OK;
+}
+
+}  // namespace
+
+namespace kvq {
+
+bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_dim_qk,
+                 int head_dim_v, int page_size, int max_pages, DecodePlan* plan,
+                 const char** why) {
+  static thread_local char msg[256];
+  auto no = [&](const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(msg, sizeof msg, fmt, ap);
+    va_end(ap);
+    *why = msg;
+    return false;
+  };
+  if (!known_dtype(qtype)) return no("unknown dtype %d", qtype);
+  if (batch < 1 || batch > kMaxBatch) return no("batch %d outside 1..%d", batch, kMaxBatch);
+  if (n_kv_heads < 1 || n_q_heads < 1) return no("head counts must be >= 1");
+  if (n_q_heads % n_kv_heads != 0)
+    return no("n_q_heads %d is not a multiple of n_kv_heads %d", n_q_heads, n_kv_heads);
+  if (max_pages < 1) return no("max_pages %d < 1", max_pages);
+  if (page_size != kPageSize) return no("page_size %d is not supported (only 16)", page_size);
+  if (qtype != KVQ_BF16 && (head_dim_qk % KVQ_BLOCK || head_dim_v % KVQ_BLOCK))
+    return no("head_dim %d/%d is not a multiple of the %d-element quantization block",
+              head_dim_qk, head_dim_v, KVQ_BLOCK);
+  if (head_dim_v > head_dim_qk) return no("head_dim_v %d > head_dim_qk %d", head_dim_v, head_dim_qk);
+  DecodePlan p{};
+  const int G = n_q_heads / n_kv_heads;
+  if (head_dim_qk == 576 && head_dim_v == 512 && n_kv_heads == 1) {
+    return no("the shared 576/512 latent slab is not supported by this build");
+  } else if (head_dim_qk == head_dim_v &&
+             (head_dim_qk == 32 || head_dim_qk == 64 || head_dim_qk == 128 || head_dim_qk == 256)) {
+    p.kind = DK_GQA;
+    p.gt = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+    p.n_hg = G / p.gt;
+    const int64_t units = (int64_t)batch * n_kv_heads * p.n_hg;
+    // Item length: about 8 work items per CU over the upper-bound context,
+    // a whole step of pages per wave, at most kMaxItemPages, and few enough
+    // chunks per sequence for the merge's weights to fit in LDS.
+    const int step = 4 * gqa_pages_per_step(qtype, head_dim_qk);
+    const int64_t target = 8 * (int64_t)kPlanCUs;
+    int64_t want = ((int64_t)max_pages * units + target - 1) / target;
+    const int64_t for_merge = ((int64_t)max_pages * p.gt + kMergeMaxWeights - 1) / kMergeMaxWeights;
+    if (want < for_merge) want = for_merge;
+    if (want < step) want = step;
+    want = (want + step - 1) / step * step;
+    const int cap = kMaxItemPages / step * step;
+    if (for_merge > cap) return no("max_pages %d is too large for the split-K merge", max_pages);
+    p.item_pages = (int)(want < cap ? want : cap);
+    p.fused_merge = true;
+    p.max_items = units * ((max_pages + p.item_pages - 1) / p.item_pages);
+  } else {
+    return no("head_dim %d/%d is not supported (separate K/V: 32, 64, 128 or 256 with equal "
+              "K and V widths; shared slab: 576/512 with one kv head)",
+              head_dim_qk, head_dim_v);
+  }
+  if (p.max_items >= ((int64_t)1 << 31)) return no("too many work items");
+  p.off_prefix = 0;
+  p.off_count = align256((size_t)(batch + 1) * sizeof(int));
+  p.off_ml = p.off_count + align256((size_t)batch * n_kv_heads * p.n_hg * sizeof(int));
+  p.off_acc = p.off_ml + align256((size_t)p.max_items * p.gt * 2 * sizeof(float));
+  p.bytes = p.off_acc + align256((size_t)p.max_items * p.gt * head_dim_v * sizeof(float));
+  *plan = p;
+  return true;
+}
+
+}  // namespace kvq
+
+extern "C" {
+
+const char* kvq_last_error(void) { return g_err.c_str(); }
+
+int64_t kvq_pool_bytes(kvq_dtype dtype, int64_t num_pages, int page_size, int n_heads,
+                       int head_dim, int64_t* code_bytes, int64_t* scale_bytes) {
+  if (!known_dtype(dtype)) return fail(-1, "kvq_pool_bytes: unknown dtype %d", (int)dtype);
+  if (num_pages < 0 || page_size < 1 || n_heads < 1 || head_dim < 1)
+    return fail(-1, "kvq_pool_bytes: sizes must be positive (num_pages may be 0)");
+  if (dtype != KVQ_BF16 && head_dim % KVQ_BLOCK != 0)
+    return fail(-1, "kvq_pool_bytes: head_dim %d is not a multiple of %d", head_dim, KVQ_BLOCK);
+  const int64_t elems = num_pages * page_size * (int64_t)n_heads * head_dim;
+  const int64_t codes = (dtype == KVQ_BF16) ? 2 * elems : elems;
+  const int64_t scales = (dtype == KVQ_BF16) ? 0 : (elems / KVQ_BLOCK) * 2;
+  if (code_bytes) *code_bytes = codes;
+  if (scale_bytes) *scale_bytes = scales;
+  g_err.clear();
+  return codes + scales;
+}
+
+int kvq_store(kvq_dtype dtype, const void* k_src, const void* v_src, int64_t src_token_stride,
+              const int32_t* slot_mapping, int64_t n_tokens, int n_heads, int head_dim,
+              int page_size, int64_t num_pages, void* k_pool, uint16_t* k_scales, void* v_pool,
+              uint16_t* v_scales, kvq_stream_t stream) {
+  int rc = check_rows(dtype, n_tokens, n_heads, head_dim, page_size, num_pages, "kvq_store");
+  if (rc != KVQ_OK) return rc;
+  if (n_tokens == 0) return ok();
+  if (!k_src || !slot_mapping || !k_pool) return fail(KVQ_ERR_ARG, "kvq_store: null pointer");
+  if (dtype != KVQ_BF16 && !k_scales) return fail(KVQ_ERR_ARG, "kvq_store: null k_scales");
+  if (v_src && (!v_pool || (dtype != KVQ_BF16 && !v_scales)))
+    return fail(KVQ_ERR_ARG, "kvq_store: v_src given without v_pool/v_scales");
+  if (src_token_stride < (int64_t)n_heads * head_dim || src_token_stride % 8 != 0)
+    return fail(KVQ_ERR_ARG,
+                "kvq_store: src_token_stride %lld must be >= n_heads*head_dim and a multiple of 8",
+                (long long)src_token_stride);
+  if (!aligned(k_src, 16) || (v_src && !aligned(v_src, 16)))
+    return fail(KVQ_ERR_ARG, "kvq_store: k_src/v_src must be 16-byte aligned");
+  if (!aligned(k_pool, 16) || (v_src && !aligned(v_pool, 16)))
+    return fail(KVQ_ERR_ARG, "kvq_store: pools must be 16-byte aligned");
+  if (dtype != KVQ_BF16 && (!aligned(k_scales, 2) || (v_src && !aligned(v_scales, 2))))
+    return fail(KVQ_ERR_ARG, "kvq_store: scales must be 2-byte aligned");
+  kvq::StoreArgs a;
+  a.qtype = dtype;
+  a.src[0] = static_cast<const uint16_t*>(k_src);
+  a.src[1] = static_cast<const uint16_t*>(v_src);
+  a.stride = src_token_stride;
+  a.slots = slot_mapping;
+  a.n_tokens = n_tokens;
+  a.n_heads = n_heads;
+  a.head_dim = head_dim;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  a.pool[0] = static_cast<uint8_t*>(k_pool);
+  a.pool[1] = static_cast<uint8_t*>(v_src ? v_pool : nullptr);
+  a.scales[0] = k_scales;
+  a.scales[1] = v_src ? v_scales : nullptr;
+  hipError_t e = kvq::launch_store(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "kvq_store");
+  return ok();
+}
+
+int kvq_dequant(kvq_dtype dtype, const void* pool, const uint16_t* scales,
+                const int32_t* slot_mapping, int64_t n_tokens, int n_heads, int head_dim,
+                int page_size, int64_t num_pages, void* out_bf16, kvq_stream_t stream) {
+  int rc = check_rows(dtype, n_tokens, n_heads, head_dim, page_size, num_pages, "kvq_dequant");
+  if (rc != KVQ_OK) return rc;
+  if (n_tokens == 0) return ok();
+  if (!pool || !slot_mapping || !out_bf16 || (dtype != KVQ_BF16 && !scales))
+    return fail(KVQ_ERR_ARG, "kvq_dequant: null pointer");
+  if (!aligned(pool, 16) || !aligned(out_bf16, 16))
+    return fail(KVQ_ERR_ARG, "kvq_dequant: pool and out must be 16-byte aligned");
+  kvq::DequantArgs a;
+  a.qtype = dtype;
+  a.pool = static_cast<const uint8_t*>(pool);
+  a.scales = scales;
+  a.slots = slot_mapping;
+  a.n_tokens = n_tokens;
+  a.n_heads = n_heads;
+  a.head_dim = head_dim;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  a.out = static_cast<uint16_t*>(out_bf16);
+  hipError_t e = kvq::launch_dequant(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "kvq_dequant");
+  return ok();
+}
+
+size_t kvq_paged_decode_workspace_bytes(kvq_dtype dtype, int batch, int n_q_heads,
+                                        int n_kv_heads, int head_dim_qk, int head_dim_v,
+                                        int page_size, int max_pages) {
+  kvq::DecodePlan p;
+  const char* why = nullptr;
+  if (!kvq::plan_decode(dtype, batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, page_size,
+                        max_pages, &p, &why)) {
+    fail(KVQ_ERR_UNSUPPORTED, "kvq_paged_decode_workspace_bytes: %s", why);
+    return 0;
+  }
+  g_err.clear();
+  return p.bytes;
+}
+
+int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
+                     const uint16_t* k_scales, const void* v_pool, const uint16_t* v_scales,
+                     const int32_t* page_table, int64_t pt_stride, const int32_t* seq_lens,
+                     int batch, int n_q_heads, int n_kv_heads, int head_dim_qk, int head_dim_v,
+                     int page_size, int max_pages, int64_t num_pages, float sm_scale,
+                     void* out_bf16, float* lse, void* workspace, size_t workspace_bytes,
+                     kvq_stream_t stream) {
+  if (!known_dtype(dtype)) return fail(KVQ_ERR_ARG, "kvq_paged_decode: unknown dtype %d", dtype);
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || max_pages < 1 || head_dim_qk < 1 ||
+      head_dim_v < 1 || page_size < 1)
+    return fail(KVQ_ERR_ARG, "kvq_paged_decode: sizes must be >= 1");
+  if (n_q_heads % n_kv_heads != 0)
+    return fail(KVQ_ERR_ARG, "kvq_paged_decode: n_q_heads %d is not a multiple of n_kv_heads %d",
+                n_q_heads, n_kv_heads);
+  if (dtype != KVQ_BF16 && (head_dim_qk % KVQ_BLOCK || head_dim_v % KVQ_BLOCK))
+    return fail(KVQ_ERR_ARG,
+                "kvq_paged_decode: head_dim %d/%d is not a multiple of the %d-element block",
+                head_dim_qk, head_dim_v, KVQ_BLOCK);
+  if (head_dim_v > head_dim_qk)
+    return fail(KVQ_ERR_ARG, "kvq_paged_decode: head_dim_v %d > head_dim_qk %d", head_dim_v,
+                head_dim_qk);
+  if (pt_stride < max_pages)
+    return fail(KVQ_ERR_ARG, "kvq_paged_decode: pt_stride %lld < max_pages %d",
+                (long long)pt_stride, max_pages);
+  if (num_pages < 0 || num_pages * (int64_t)page_size > INT32_MAX)
+    return fail(KVQ_ERR_ARG, "kvq_paged_decode: num_pages out of range");
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
+    return fail(KVQ_ERR_ARG, "kvq_paged_decode: sm_scale is not finite");
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out_bf16)
+    return fail(KVQ_ERR_ARG, "kvq_paged_decode: null pointer");
+  if (dtype != KVQ_BF16 && (!k_scales || !v_scales))
+    return fail(KVQ_ERR_ARG, "kvq_paged_decode: null scales");
+  const bool shared = (k_pool == v_pool);
+  if (shared != (k_scales == v_scales) && dtype != KVQ_BF16)
+    return fail(KVQ_ERR_ARG, "kvq_paged_decode: k_pool == v_pool requires k_scales == v_scales");
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out_bf16, 4))
+    return fail(KVQ_ERR_ARG, "kvq_paged_decode: q and pools must be 16-byte aligned");
+  kvq::DecodePlan plan;
+  const char* why = nullptr;
+  if (!kvq::plan_decode(dtype, batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, page_size,
+                        max_pages, &plan, &why))
+    return fail(KVQ_ERR_UNSUPPORTED, "kvq_paged_decode: %s", why);
+  if (shared && plan.kind != kvq::DK_MLA)
+    return fail(KVQ_ERR_UNSUPPORTED,
+                "kvq_paged_decode: k_pool == v_pool is only supported for the 576/512 slab");
+  if (!shared && plan.kind == kvq::DK_MLA)
+    return fail(KVQ_ERR_UNSUPPORTED, "kvq_paged_decode: the 576/512 shape needs the shared slab");
+  if (!workspace || workspace_bytes < plan.bytes)
+    return fail(KVQ_ERR_WORKSPACE, "kvq_paged_decode: workspace of %zu bytes needed, %zu given",
+                plan.bytes, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256))
+    return fail(KVQ_ERR_WORKSPACE, "kvq_paged_decode: workspace must be 256-byte aligned");
+  kvq::DecodeArgs a;
+  a.qtype = dtype;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = static_cast<const uint8_t*>(k_pool);
+  a.k_scales = k_scales;
+  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.v_scales = v_scales;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.head_dim_qk = head_dim_qk;
+  a.head_dim_v = head_dim_v;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.sm_scale = sm_scale;
+  a.out = static_cast<uint16_t*>(out_bf16);
+  a.lse = lse;
+  a.workspace = workspace;
+  const int cus = num_cus_current();
+  hipError_t e = (plan.kind == kvq::DK_MLA) ? kvq::launch_mla_decode(a, plan, cus, stream)
+                                            : kvq::launch_gqa_decode(a, plan, cus, stream);
+  if (e != hipSuccess) return hip_fail(e, "kvq_paged_decode");
+  return ok();
+}
+
+}  // extern "C"

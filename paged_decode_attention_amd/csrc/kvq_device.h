@@ -1,0 +1,93 @@
+// kvq_device.h -- small device helpers for the gfx950 kernels of libkvq.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- bf16 / fp16 bit conversions ----------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// ---- 8-bit code decoding --------------------------------------------------------
+// e4m3fn: the gfx950 packed conversion decodes two codes (bytes 0,1 or 2,3 of
+// a dword) to fp32 exactly.
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
+  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  o[0] = a.x;
+  o[1] = a.y;
+  o[2] = b.x;
+  o[3] = b.y;
+}
+
+// int8: sign-extend each byte.
+__device__ __forceinline__ void q8x4_to_f32(uint32_t w, float* o) {
+  o[0] = (float)(int32_t)(int8_t)(w & 0xff);
+  o[1] = (float)(int32_t)(int8_t)((w >> 8) & 0xff);
+  o[2] = (float)(int32_t)(int8_t)((w >> 16) & 0xff);
+  o[3] = (float)(int32_t)(int8_t)(w >> 24);
+}
+
+template <int QT>
+__device__ __forceinline__ void decode_dword(uint32_t w, float* o) {
+  if constexpr (QT == 1) {
+    fp8x4_to_f32(w, o);
+  } else if constexpr (QT == 2) {
+    q8x4_to_f32(w, o);
+  } else {
+    o[0] = bf16_lo(w);
+    o[1] = bf16_hi(w);
+  }
+}
+
+// ---- cross-lane ----------------------------------------------------------------
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+// quad_perm DPP swaps within groups of 4 lanes: xor 1 -> [1,0,3,2], xor 2 -> [2,3,0,1].
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+// ---- division by a runtime constant (unsigned 32-bit, exact) -------------------
+// n / d == umulhi(n, m) >> s for all n < 2^31 with m, s from the usual
+// round-up reciprocal construction.
+struct FastDiv {
+  uint32_t d, m, s;
+  __host__ __device__ FastDiv() : d(1), m(0), s(0) {}
+  __host__ explicit FastDiv(uint32_t div) : d(div) {
+    s = 0;
+    while ((1ull << s) < div) ++s;
+    m = (uint32_t)((((1ull << 32) * ((1ull << s) - div)) / div) + 1);
+  }
+  __host__ __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    return (uint32_t)((((uint64_t)n * m) >> 32) + n) >> s;
+  }
+};
+
+}  // namespace kvq

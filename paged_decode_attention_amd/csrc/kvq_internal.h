@@ -1,0 +1,112 @@
+// kvq_internal.h -- declarations shared by the host entry points (kvq_api.cpp)
+// and the HIP kernel files of libkvq.so.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+enum { QT_BF16 = 0, QT_FP8 = 1, QT_Q8 = 2 };
+
+// Token rows per page supported by the decode kernels.
+constexpr int kPageSize = 16;
+// Largest batch the decode kernels index through their on-chip work list.
+constexpr int kMaxBatch = 4096;
+// Compute units the split planner assumes (MI355X); the plan must not depend
+// on the device so that the workspace query and the call agree.
+constexpr int kPlanCUs = 256;
+// A work item spans at most this many pages (64 per wave of a 4-wave group).
+constexpr int kMaxItemPages = 256;
+// The last workgroup of a (sequence, kv head, head group) merges the chunk
+// partials itself when there are at most this many; otherwise a separate
+// merge kernel runs.
+constexpr int kFusedMergeMaxChunks = 64;
+// Chunk weights the merge keeps in LDS: chunks * heads per item.
+constexpr int kMergeMaxWeights = 4096;
+
+// GQA decode geometry shared by the planner and the kernels: bytes of one
+// (page, kv head) of codes and of scales, and how many pages a wave streams
+// through its LDS buffer per step (about 8.5 KB of K and V per step).
+__host__ __device__ constexpr int gqa_elem_bytes(int qtype) { return qtype == QT_BF16 ? 2 : 1; }
+__host__ __device__ constexpr int gqa_code_bytes(int qtype, int d) {
+  return kPageSize * d * gqa_elem_bytes(qtype);
+}
+__host__ __device__ constexpr int gqa_scale_bytes(int qtype, int d) {
+  return qtype == QT_BF16 ? 0 : kPageSize * (d / 32) * 2;
+}
+__host__ __device__ constexpr int gqa_pages_per_step(int qtype, int d) {
+  return (8704 / (2 * (gqa_code_bytes(qtype, d) + gqa_scale_bytes(qtype, d)))) < 1
+             ? 1
+             : 8704 / (2 * (gqa_code_bytes(qtype, d) + gqa_scale_bytes(qtype, d)));
+}
+
+struct StoreArgs {
+  int qtype;
+  const uint16_t* src[2];  // K, V (V may be null)
+  int64_t stride;          // elements between tokens
+  const int32_t* slots;
+  int64_t n_tokens;
+  int n_heads, head_dim, page_size;
+  int64_t num_pages;
+  uint8_t* pool[2];
+  uint16_t* scales[2];
+};
+
+struct DequantArgs {
+  int qtype;
+  const uint8_t* pool;
+  const uint16_t* scales;
+  const int32_t* slots;
+  int64_t n_tokens;
+  int n_heads, head_dim, page_size;
+  int64_t num_pages;
+  uint16_t* out;
+};
+
+hipError_t launch_store(const StoreArgs& a, hipStream_t s);
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
+
+// ---- paged decode --------------------------------------------------------------
+
+enum DecodeKind { DK_GQA = 0, DK_MLA = 1 };
+
+struct DecodePlan {
+  int kind;
+  int gt;             // query heads per work item
+  int n_hg;           // head groups per kv head (G / gt)
+  int item_pages;     // pages per split-K work item
+  bool fused_merge;   // merge inside the split kernel (else a merge kernel)
+  int64_t max_items;  // upper bound on work items (sizes the workspace)
+  size_t off_prefix, off_count, off_ml, off_acc, bytes;  // workspace layout
+};
+
+struct DecodeArgs {
+  int qtype;
+  const uint16_t* q;
+  const uint8_t* k_pool;
+  const uint16_t* k_scales;
+  const uint8_t* v_pool;
+  const uint16_t* v_scales;
+  const int32_t* page_table;
+  int64_t pt_stride;
+  const int32_t* seq_lens;
+  int batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, max_pages;
+  int64_t num_pages;
+  float sm_scale;
+  uint16_t* out;
+  float* lse;
+  void* workspace;
+};
+
+// Host-only planning: returns false (with a message) for unsupported shapes.
+bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_dim_qk,
+                 int head_dim_v, int page_size, int max_pages, DecodePlan* plan,
+                 const char** why);
+
+hipError_t launch_gqa_decode(const DecodeArgs& a, const DecodePlan& p, int num_cus,
+                             hipStream_t s);
+hipError_t launch_mla_decode(const DecodeArgs& a, const DecodePlan& p, int num_cus,
+                             hipStream_t s);
+
+}  // namespace kvq

@@ -1,0 +1,229 @@
+// kvq_store.hip -- quantize-on-store and gather-dequantize kernels (gfx950).
+//
+// Sources: [PR103] "feat(kvcache): 8-bit KV cache (q8_0 / fp8_e4m3) behind
+// --kv-cache-dtype" (§What; review comment §"A bug on sm_89"), [PR113]
+// "feat(kvcache): 8-bit DSV4 window/compressed KV behind --kv-cache-dtype"
+// (§What this adds).
+//
+// Mapping: four lanes own one 32-element block (8 bf16 = one 16-byte load
+// each).  The block max-abs is a 2-step DPP max inside the lane quad; every
+// lane then derives the same fp16 scale, quantizes its 8 elements and writes
+// 8 code bytes; lane 0 of the quad writes the 2-byte scale.  K and V of the
+// same (token, head, block) are handled by the same lane, so a thread keeps
+// two independent 16-byte loads in flight.
+//
+// Rounding: the quotient x / s is an IEEE fp32 division (correctly rounded,
+// as hipcc emits by default), and the code is the round-to-nearest-even e4m3
+// value of the clamped quotient from the hardware packed conversion, or the
+// half-away-from-zero integer for q8_0.  This is the store the review comment
+// on [PR103] asks for; a truncating intermediate fp16 step (the bug it
+// describes) is never taken.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct StoreGrid {
+  FastDiv per_token;  // lanes per token = n_heads * nb * 4
+  FastDiv per_head;   // lanes per head row = nb * 4
+  uint32_t n_lanes;
+};
+
+template <int QT>
+__device__ __forceinline__ void quantize8(const float* x, float s, uint32_t* out2) {
+  constexpr float M = (QT == QT_Q8) ? 127.0f : 448.0f;
+  if (s == 0.0f) {
+    out2[0] = 0u;
+    out2[1] = 0u;
+    return;
+  }
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float q = x[i] / s;  // IEEE fp32 division by the stored fp16 scale
+    v[i] = fminf(fmaxf(q, -M), M);
+  }
+  if constexpr (QT == QT_FP8) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w + 0], v[4 * w + 1], 0, false);
+      out2[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w + 2], v[4 * w + 3], lo, true);
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      uint32_t r = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        int c = (int)roundf(v[4 * w + k]);  // half away from zero, |c| <= 127
+        r |= ((uint32_t)c & 0xffu) << (8 * k);
+      }
+      out2[w] = r;
+    }
+  }
+}
+
+template <int QT>
+__global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs a, StoreGrid g) {
+  const uint32_t lane = blockIdx.x * kThreads + threadIdx.x;
+  // The quad of a block must stay together for the DPP max, so no early return
+  // before it; out-of-range lanes only skip their memory accesses.
+  const bool in_range = lane < g.n_lanes;
+  const uint32_t l = in_range ? lane : 0u;
+  const uint32_t token = g.per_token.div(l);
+  const uint32_t r0 = l - token * g.per_token.d;
+  const uint32_t h = g.per_head.div(r0);
+  const uint32_t r1 = r0 - h * g.per_head.d;  // (block, quarter) within the row
+  const uint32_t blk = r1 >> 2, quarter = r1 & 3u;
+  const int nb = a.head_dim >> 5;
+
+  const int32_t slot = in_range ? a.slots[token] : -1;
+  const int64_t cap = a.num_pages * (int64_t)a.page_size;
+  const bool valid = slot >= 0 && (int64_t)slot < cap;
+
+  const int64_t src_off = (int64_t)token * a.stride + (int64_t)h * a.head_dim + blk * 32 + quarter * 8;
+  const int64_t page = valid ? slot / a.page_size : 0;
+  const int64_t off = valid ? slot - page * a.page_size : 0;
+  const int64_t row = (page * a.n_heads + h) * a.page_size + off;
+
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (a.src[t] == nullptr) continue;  // uniform: V absent
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (valid) raw = *reinterpret_cast<const uint4*>(a.src[t] + src_off);
+    if constexpr (QT == QT_BF16) {
+      if (valid)
+        *reinterpret_cast<uint4*>(a.pool[t] + (row * a.head_dim + blk * 32 + quarter * 8) * 2) = raw;
+    } else {
+      float x[8];
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_lo(w[i]);
+        x[2 * i + 1] = bf16_hi(w[i]);
+        amax = fmaxf(amax, fmaxf(fabsf(x[2 * i]), fabsf(x[2 * i + 1])));
+      }
+      amax = fmaxf(amax, dpp_xor1(amax));
+      amax = fmaxf(amax, dpp_xor2(amax));
+      constexpr float M = (QT == QT_Q8) ? 127.0f : 448.0f;
+      float sq = amax / M;  // IEEE fp32 division
+      sq = fminf(sq, 65504.0f);  // a quotient past the fp16 range saturates
+      const _Float16 sh = (_Float16)sq;  // round to nearest even
+      const float s = (float)sh;
+      uint32_t codes[2];
+      quantize8<QT>(x, s, codes);
+      if (valid) {
+        *reinterpret_cast<uint2*>(a.pool[t] + row * a.head_dim + blk * 32 + quarter * 8) =
+            make_uint2(codes[0], codes[1]);
+        if (quarter == 0) a.scales[t][row * nb + blk] = __builtin_bit_cast(uint16_t, sh);
+      }
+    }
+  }
+}
+
+// ---- dequant: 8 codes per lane -> 8 bf16 (one 16-byte store) -------------------
+
+struct DequantGrid {
+  FastDiv per_token;  // lanes per token = n_heads * head_dim / 8
+  FastDiv per_head;   // head_dim / 8
+  uint32_t n_lanes;
+};
+
+template <int QT>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, DequantGrid g) {
+  const uint32_t lane = blockIdx.x * kThreads + threadIdx.x;
+  if (lane >= g.n_lanes) return;
+  const uint32_t token = g.per_token.div(lane);
+  const uint32_t r0 = lane - token * g.per_token.d;
+  const uint32_t h = g.per_head.div(r0);
+  const uint32_t e8 = r0 - h * g.per_head.d;  // which group of 8 elements
+  const int32_t slot = a.slots[token];
+  const int64_t cap = a.num_pages * (int64_t)a.page_size;
+  uint4 outv = make_uint4(0, 0, 0, 0);
+  if (slot >= 0 && (int64_t)slot < cap) {
+    const int64_t page = slot / a.page_size, off = slot - page * a.page_size;
+    const int64_t row = (page * a.n_heads + h) * a.page_size + off;
+    if constexpr (QT == QT_BF16) {
+      outv = *reinterpret_cast<const uint4*>(a.pool + (row * a.head_dim + e8 * 8) * 2);
+    } else {
+      const uint2 raw = *reinterpret_cast<const uint2*>(a.pool + row * a.head_dim + e8 * 8);
+      const float s = f16_bits_to_f32(a.scales[row * (a.head_dim >> 5) + (e8 >> 2)]);
+      float x[8];
+      decode_dword<QT>(raw.x, x);
+      decode_dword<QT>(raw.y, x + 4);
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = bf16_rne(x[2 * i] * s) | (bf16_rne(x[2 * i + 1] * s) << 16);  // products exact
+      outv = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+  *reinterpret_cast<uint4*>(a.out + ((int64_t)token * a.n_heads + h) * a.head_dim + e8 * 8) = outv;
+}
+
+}  // namespace
+
+hipError_t launch_store(const StoreArgs& a, hipStream_t s) {
+  if (a.n_tokens == 0) return hipSuccess;
+  const int nb = a.head_dim / 32;
+  // bf16 pools are copied in 16-byte pieces with the same lane layout: one
+  // "block" of 32 elements = 4 lanes of 8 elements.
+  const uint32_t per_head = (uint32_t)(a.qtype == QT_BF16 ? a.head_dim / 8 : nb * 4);
+  const uint32_t per_token = per_head * (uint32_t)a.n_heads;
+  // keep every launch below 2^31 lanes
+  const int64_t max_tokens = ((int64_t)1 << 31) / per_token;
+  for (int64_t t0 = 0; t0 < a.n_tokens; t0 += max_tokens) {
+    StoreArgs sub = a;
+    const int64_t n = (a.n_tokens - t0 < max_tokens) ? a.n_tokens - t0 : max_tokens;
+    sub.n_tokens = n;
+    sub.slots = a.slots + t0;
+    for (int t = 0; t < 2; ++t)
+      if (sub.src[t]) sub.src[t] = a.src[t] + t0 * a.stride;
+    StoreGrid g;
+    g.per_token = FastDiv(per_token);
+    g.per_head = FastDiv(per_head);
+    g.n_lanes = (uint32_t)(n * per_token);
+    const uint32_t blocks = (g.n_lanes + kThreads - 1) / kThreads;
+    switch (a.qtype) {
+      case QT_BF16: store_kernel<QT_BF16><<<blocks, kThreads, 0, s>>>(sub, g); break;
+      case QT_FP8: store_kernel<QT_FP8><<<blocks, kThreads, 0, s>>>(sub, g); break;
+      default: store_kernel<QT_Q8><<<blocks, kThreads, 0, s>>>(sub, g); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {
+  if (a.n_tokens == 0) return hipSuccess;
+  const uint32_t per_head = (uint32_t)(a.head_dim / 8);
+  const uint32_t per_token = per_head * (uint32_t)a.n_heads;
+  const int64_t max_tokens = ((int64_t)1 << 31) / per_token;
+  for (int64_t t0 = 0; t0 < a.n_tokens; t0 += max_tokens) {
+    DequantArgs sub = a;
+    const int64_t n = (a.n_tokens - t0 < max_tokens) ? a.n_tokens - t0 : max_tokens;
+    sub.n_tokens = n;
+    sub.slots = a.slots + t0;
+    sub.out = a.out + t0 * per_token * 8;
+    DequantGrid g;
+    g.per_token = FastDiv(per_token);
+    g.per_head = FastDiv(per_head);
+    g.n_lanes = (uint32_t)(n * per_token);
+    const uint32_t blocks = (g.n_lanes + kThreads - 1) / kThreads;
+    switch (a.qtype) {
+      case QT_BF16: dequant_kernel<QT_BF16><<<blocks, kThreads, 0, s>>>(sub, g); break;
+      case QT_FP8: dequant_kernel<QT_FP8><<<blocks, kThreads, 0, s>>>(sub, g); break;
+      default: dequant_kernel<QT_Q8><<<blocks, kThreads, 0, s>>>(sub, g); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace kvq

@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI (CPU only, no kernel launches): the library
+loads and exports every symbol the header declares, the cost model, and the
+argument validation that runs before anything is enqueued.
+
+Page keys: [PR103] "feat(kvcache): 8-bit KV cache (q8_0 / fp8_e4m3) behind
+--kv-cache-dtype" (§What: effective bytes per element; review §"End-to-end
+numbers": the pool grows by 2/1.0625); [PR113] "feat(kvcache): 8-bit DSV4
+window/compressed KV behind --kv-cache-dtype" (§Gating: head_dim a multiple of
+32, rejected up front with a clear message; §One ordering trap: the cost model
+and the pool must agree).
+"""
+import ctypes
+import os
+import re
+from fractions import Fraction
+
+import pytest
+
+from paged_decode_attention_amd import kvq
+from tests.test_oracle_pins import FACTS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    assert set(names) == set(kvq.EXPORTS)
+    for n in names:
+        assert ctypes.cast(getattr(kvq.LIB, n), ctypes.c_void_p).value
+
+
+def test_pool_bytes_is_17_16_per_element_and_32_17_vs_bf16():
+    for pages, H, D in [(1, 1, 32), (8192, 8, 128), (10240, 1, 576), (3, 2, 256)]:
+        t8, c8, s8 = kvq.pool_bytes("fp8_e4m3", pages, 16, H, D)
+        tq, cq, sq = kvq.pool_bytes("q8_0", pages, 16, H, D)
+        tb, cb, sb = kvq.pool_bytes("bf16", pages, 16, H, D)
+        elems = pages * 16 * H * D
+        assert (t8, c8, s8) == (tq, cq, sq)
+        assert Fraction(t8, elems) == Fraction(int(FACTS["bytes_per_elem_num"]),
+                                               int(FACTS["bytes_per_elem_den"]))
+        assert sb == 0 and Fraction(tb, t8) == Fraction(32, 17)
+    # same byte budget: the measured pool growth on the page (+88%)
+    budget = int(FACTS["pool_tokens_bf16"]) * kvq.pool_bytes("bf16", 1, 1, 1, 256)[0]
+    per_tok = kvq.pool_bytes("fp8_e4m3", 1, 1, 1, 256)[0]
+    assert abs(budget // per_tok - FACTS["pool_tokens_8bit"]) < 16
+
+
+@pytest.mark.parametrize("dtype", ["fp8_e4m3", "q8_0"])
+def test_head_dim_not_multiple_of_32_is_rejected_up_front(dtype):
+    with pytest.raises(ValueError, match="multiple of"):
+        kvq.pool_bytes(dtype, 4, 16, 1, 48)
+    rc = kvq.LIB.kvq_store(kvq.DTYPES[dtype], 16, 16, 48, 16, 1, 1, 48, 16, 4, 16, 16, 16, 16,
+                           None)
+    assert rc == kvq.ERR_ARG and "multiple of the 32-element" in kvq.last_error()
+    assert kvq.LIB.kvq_paged_decode_workspace_bytes(kvq.DTYPES[dtype], 1, 2, 1, 48, 48, 16, 4) == 0
+
+
+def test_validation_errors_before_any_launch():
+    L = kvq.LIB
+    # null pointers, bad strides, bad dtype: rejected with messages, nothing launched
+    assert L.kvq_store(1, None, None, 128, None, 4, 1, 128, 16, 4, None, None, None, None,
+                       None) == kvq.ERR_ARG
+    assert "null" in kvq.last_error()
+    assert L.kvq_store(1, 16, None, 100, 16, 4, 1, 128, 16, 4, 16, 16, None, None,
+                       None) == kvq.ERR_ARG
+    assert "src_token_stride" in kvq.last_error()
+    assert L.kvq_store(7, 16, None, 128, 16, 4, 1, 128, 16, 4, 16, 16, None, None,
+                       None) == kvq.ERR_ARG
+    assert L.kvq_store(1, 8, None, 128, 16, 4, 1, 128, 16, 4, 16, 16, None, None,
+                       None) == kvq.ERR_ARG
+    assert "aligned" in kvq.last_error()
+    # zero tokens is a no-op success
+    assert L.kvq_store(1, None, None, 128, None, 0, 1, 128, 16, 4, None, None, None, None,
+                       None) == kvq.OK
+    assert kvq.last_error() == ""
+
+
+def test_decode_validation():
+    L = kvq.LIB
+    args = dict(q=256, kp=256, ks=256, vp=512, vs=512, pt=256, sl=256, out=256, lse=None,
+                wsp=256)
+
+    def call(dtype=1, B=2, Hq=16, Hkv=8, D=128, Dv=128, ps=16, mp=8, pts=8, npg=64, ws=1 << 30,
+             sm=0.1, **kw):
+        a = dict(args, **kw)
+        return L.kvq_paged_decode(dtype, a["q"], a["kp"], a["ks"], a["vp"], a["vs"], a["pt"], pts,
+                                  a["sl"], B, Hq, Hkv, D, Dv, ps, mp, npg, sm, a["out"], a["lse"],
+                                  a["wsp"], ws, None)
+
+    assert call(Hq=12, Hkv=8) == kvq.ERR_ARG                 # not a multiple
+    assert call(ps=32) == kvq.ERR_UNSUPPORTED and "page_size" in kvq.last_error()
+    assert call(D=96, Dv=96) == kvq.ERR_UNSUPPORTED
+    assert call(Dv=256) == kvq.ERR_ARG                       # Dv > Dqk
+    assert call(pts=4) == kvq.ERR_ARG                        # stride < max_pages
+    assert call(ws=16) == kvq.ERR_WORKSPACE
+    assert call(wsp=None) == kvq.ERR_WORKSPACE
+    assert call(kp=None) == kvq.ERR_ARG
+    assert call(sm=float("nan")) == kvq.ERR_ARG
+    assert call(B=0) == kvq.ERR_ARG
+    assert call(B=5000) == kvq.ERR_UNSUPPORTED
+    # k_pool == v_pool is the shared-slab form, only for 576/512
+    assert call(vp=256, vs=256) == kvq.ERR_UNSUPPORTED
+    need = kvq.workspace_bytes("fp8_e4m3", 2, 16, 8, 128, 128, 16, 8)
+    assert call(ws=need - 1) == kvq.ERR_WORKSPACE
+
+
+def test_python_errors_are_typed():
+    with pytest.raises(ValueError):
+        kvq.pool_bytes("fp8_e4m3", -1, 16, 1, 32)
+    with pytest.raises(ValueError):
+        kvq.pool_bytes("int4", 1, 16, 1, 32)
+    with pytest.raises(NotImplementedError):
+        kvq.workspace_bytes("fp8_e4m3", 1, 8, 1, 64, 64, 8, 4)
