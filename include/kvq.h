@@ -174,7 +174,7 @@ size_t kvq_paged_decode_workspace_bytes(kvq_dtype dtype, int batch, int n_q_head
  * Supported: page_size 16; separate K/V with head_dim_qk == head_dim_v in
  * {32, 64, 128, 256} and any n_q_heads a multiple of n_kv_heads; the shared
  * slab with head_dim_qk 576, head_dim_v 512, n_kv_heads 1 and n_q_heads a
- * multiple of 16 up to 128; batch 1..4096; max_pages >= 1.
+ * multiple of 16 up to 128; batch 1..4096; max_pages >= 1; num_pages >= 1.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP. */
 int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
                      const uint16_t* k_scales, const void* v_pool, const uint16_t* v_scales,

@@ -17,7 +17,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/kvq.h"
+#include "kvq.h"
 #include "kvq_internal.h"
 
 namespace {
@@ -122,17 +122,17 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
     p.gt = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     p.n_hg = G / p.gt;
     const int64_t units = (int64_t)batch * n_kv_heads * p.n_hg;
-    // Item length: about 8 work items per CU over the upper-bound context,
+    // Item length: about 2 work items per CU over the upper-bound context,
     // a whole step of pages per wave, at most kMaxItemPages, and few enough
     // chunks per sequence for the merge's weights to fit in LDS.
-    const int step = 4 * gqa_pages_per_step(qtype, head_dim_qk);
-    const int64_t target = 8 * (int64_t)kPlanCUs;
+    const int step = kDecodeWaves * gqa_pages_per_step(qtype, head_dim_qk);
+    const int64_t target = 2 * (int64_t)kPlanCUs;
     int64_t want = ((int64_t)max_pages * units + target - 1) / target;
     const int64_t for_merge = ((int64_t)max_pages * p.gt + kMergeMaxWeights - 1) / kMergeMaxWeights;
     if (want < for_merge) want = for_merge;
     if (want < step) want = step;
     want = (want + step - 1) / step * step;
-    const int cap = kMaxItemPages / step * step;
+    const int cap = kMaxItemPages * kDecodeWaves / 4 / step * step;
     if (for_merge > cap) return no("max_pages %d is too large for the split-K merge", max_pages);
     p.item_pages = (int)(want < cap ? want : cap);
     p.fused_merge = true;
@@ -279,8 +279,8 @@ int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
   if (pt_stride < max_pages)
     return fail(KVQ_ERR_ARG, "kvq_paged_decode: pt_stride %lld < max_pages %d",
                 (long long)pt_stride, max_pages);
-  if (num_pages < 0 || num_pages * (int64_t)page_size > INT32_MAX)
-    return fail(KVQ_ERR_ARG, "kvq_paged_decode: num_pages out of range");
+  if (num_pages < 1 || num_pages * (int64_t)page_size > INT32_MAX)
+    return fail(KVQ_ERR_ARG, "kvq_paged_decode: num_pages must be in 1..2^31/page_size");
   if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
     return fail(KVQ_ERR_ARG, "kvq_paged_decode: sm_scale is not finite");
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out_bf16)

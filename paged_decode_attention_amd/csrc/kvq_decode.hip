@@ -34,8 +34,8 @@
 namespace kvq {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kWaves = kDecodeWaves;
+constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -89,25 +89,80 @@ __device__ __forceinline__ void decode_raw(const Raw<NDW>& r, float* o) {
   for (int i = 0; i < NDW; ++i) decode_dword<QT>(r.w[i], o + PER * i);
 }
 
-// Sum over aligned groups of W consecutive lanes.
+// DPP lane moves inside a row of 16 lanes (VALU, no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kRowMirror = 0x140;  // lane i <-> 15-i within 16
+template <int R>
+constexpr int kRowRor = 0x120 + R;  // rotate right by R within 16
+
+// Lane exchange across rows of 16 / halves of 32 (gfx950 permlane swaps,
+// VALU only): with both operands equal, the pair returned holds the value of
+// lane l and of lane l^16 (resp. l^32), so their sum is the 2-lane sum.
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Sum over aligned groups of W consecutive lanes (W a power of two <= 64):
+// each step adds the partner that holds the sum of the neighbouring half.
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < W; m <<= 1) v += shfl_xor_f(v, m);
+  if constexpr (W >= 2) v += dpp<kQuadXor1>(v);
+  if constexpr (W >= 4) v += dpp<kQuadXor2>(v);
+  if constexpr (W >= 8) v += dpp<kHalfMirror>(v);
+  if constexpr (W >= 16) v += dpp<kRowMirror>(v);
+  if constexpr (W >= 32) v = sum_xor16(v);
+  if constexpr (W >= 64) v = sum_xor32(v);
   return v;
 }
-// Sum / max over the lanes l, l^S, l^2S, ... (all lanes with equal l mod S).
+// Sum / max over the lanes with equal (lane mod S): rotations by S, 2S, ...
+// inside each row of 16 visit every such lane once, then across rows.
 template <int S>
 __device__ __forceinline__ float stride_sum(float v) {
-#pragma unroll
-  for (int m = S; m < 64; m <<= 1) v += shfl_xor_f(v, m);
+  if constexpr (S <= 1) v += dpp<kRowRor<1>>(v);
+  if constexpr (S <= 2) v += dpp<kRowRor<2>>(v);
+  if constexpr (S <= 4) v += dpp<kRowRor<4>>(v);
+  if constexpr (S <= 8) v += dpp<kRowRor<8>>(v);
+  if constexpr (S <= 16) v = sum_xor16(v);
+  if constexpr (S <= 32) v = sum_xor32(v);
   return v;
 }
 template <int S>
 __device__ __forceinline__ float stride_max(float v) {
-#pragma unroll
-  for (int m = S; m < 64; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  if constexpr (S <= 1) v = fmaxf(v, dpp<kRowRor<1>>(v));
+  if constexpr (S <= 2) v = fmaxf(v, dpp<kRowRor<2>>(v));
+  if constexpr (S <= 4) v = fmaxf(v, dpp<kRowRor<4>>(v));
+  if constexpr (S <= 8) v = fmaxf(v, dpp<kRowRor<8>>(v));
+  if constexpr (S <= 16) v = max_xor16(v);
+  if constexpr (S <= 32) v = max_xor32(v);
   return v;
+}
+
+// Split-K partials cross workgroups on different XCDs: agent-scope relaxed
+// accesses keep them coherent without flushing the L2.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ int clamped_len(const DecodeArgs& a, int b) {
@@ -148,9 +203,64 @@ __device__ void build_prefix(const DecodeArgs& a, int item_tokens, int units, in
   __syncthreads();
 }
 
-// exp2(x - m) that is 0 (not NaN) when both are -inf.
+// exp2(x - m) that is 0 (not NaN) when both are -inf.  The raw hardware
+// exp2 is enough here: arguments are <= 0 and tiny results may flush to 0.
 __device__ __forceinline__ float exp2_rel(float x, float m) {
-  return (x == -INFINITY) ? 0.0f : exp2f(x - m);
+  return (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - m);
+}
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
+constexpr int kNonTemporal = 2;         // cache policy: streaming (read once)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+}
+
+template <int NDW>
+__device__ __forceinline__ Raw<NDW> buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  Raw<NDW> o;
+  if constexpr (NDW == 4) {
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal));
+    o.w[0] = v.x; o.w[1] = v.y; o.w[2] = v.z; o.w[3] = v.w;
+  } else {
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal));
+    o.w[0] = v.x; o.w[1] = v.y;
+  }
+  return o;
+}
+
+// Wave-uniform description of one work item.
+struct Item {
+  int item, b, u, kvh, nc, t0, nt, np, h0, nsteps;
+};
+
+template <int PPS, int GT>
+__device__ __forceinline__ Item describe(const GqaParams& p, const int* s_prefix, int item,
+                                         int wave, int units, int G) {
+  const DecodeArgs& a = p.a;
+  Item it;
+  it.item = item;
+  int lo = 0, hi = a.batch - 1;
+  while (lo < hi) {  // largest b with s_prefix[b] <= item
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_prefix[mid] <= item) lo = mid; else hi = mid - 1;
+  }
+  it.b = lo;
+  const int rem = item - s_prefix[it.b];
+  const int chunk = rem / units;
+  it.u = rem - chunk * units;
+  it.kvh = it.u / p.n_hg;
+  const int hg = it.u - it.kvh * p.n_hg;
+  const int L = clamped_len(a, it.b);
+  it.nc = (L + p.item_tokens - 1) / p.item_tokens;
+  it.t0 = chunk * p.item_tokens;
+  it.nt = min(p.item_tokens, L - it.t0);
+  it.np = (it.nt + kPageSize - 1) / kPageSize;
+  it.h0 = it.kvh * G + hg * GT;
+  const int ngroups = (it.np + PPS - 1) / PPS;
+  const int steps = (ngroups > wave) ? (ngroups - wave + kWaves - 1) / kWaves : 0;
+  it.nsteps = (steps + 1) & ~1;  // even: the step loop is unrolled by two
+  return it;
 }
 
 template <int QT, int D, int GT>
@@ -158,6 +268,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
   using Gm = Geo<QT, D>;
   constexpr int EPL = Gm::EPL, LPT = Gm::LPT, TPL = Gm::TPL, LPP = Gm::LPP, NDW = Gm::NDW;
   constexpr int PPS = Gm::PPS, ROWS = Gm::ROWS, NB = Gm::NB, ESZ = Gm::ESZ;
+  constexpr int CODE = gqa_code_bytes(QT, D), SCL = gqa_scale_bytes(QT, D);
   // cross-wave partial sums [kWaves][GT][D] at the end of an item, or the
   // merge's chunk weights [chunks][GT]
   constexpr int kRed = (kWaves * GT * D > kMergeMaxWeights) ? kWaves * GT * D : kMergeMaxWeights;
@@ -167,6 +278,8 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
   __shared__ float s_hm[GT][2];
   __shared__ int s_wave[kWaves];
   __shared__ int s_last;
+  // per-wave staging of a step's K and V scales
+  __shared__ __attribute__((aligned(16))) uint8_t s_scl[kWaves][(QT == QT_BF16 ? 1 : 2 * PPS * SCL)];
 
   const DecodeArgs& a = p.a;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -187,58 +300,202 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
     if (a.lse)
       for (int h = tid; h < a.n_q_heads; h += kThreads) a.lse[(int64_t)b * a.n_q_heads + h] = -INFINITY;
   }
+  if ((int)blockIdx.x >= total) return;  // uniform over the block
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    // ---- which (sequence, chunk, kv head, head group) ----------------------------
-    int lo = 0, hi = a.batch - 1;
-    while (lo < hi) {  // largest b with s_prefix[b] <= item
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_prefix[mid] <= item) lo = mid; else hi = mid - 1;
-    }
-    const int b = lo;
-    const int rem = item - s_prefix[b];
-    const int chunk = rem / units;
-    const int u = rem - chunk * units;
-    const int kvh = u / p.n_hg;
-    const int hg = u - kvh * p.n_hg;
-    const int L = clamped_len(a, b);
-    const int nc = (L + p.item_tokens - 1) / p.item_tokens;
-    const int t0 = chunk * p.item_tokens;
-    const int nt = min(p.item_tokens, L - t0);
-    const int np = (nt + kPageSize - 1) / kPageSize;
-    const int h0 = kvh * G + hg * GT;
+  // per-lane offsets inside a (page, kv head) chunk, the same for every page
+  uint32_t code_off[LPP], scale_off[LPP];
+#pragma unroll
+  for (int i = 0; i < LPP; ++i) {
+    code_off[i] = (uint32_t)(((i * TPL + tsub) * D + d0) * ESZ);
+    scale_off[i] = (uint32_t)(((i * TPL + tsub) * NB + (d0 >> 5)) * 2);
+  }
+  const int64_t page_rows = (int64_t)a.n_kv_heads * kPageSize;
 
-    // ---- this wave's pages: steps s = 0..nsteps-1, each PPS pages ----------------
-    const int ngroups = (np + PPS - 1) / PPS;
-    const int nsteps = (ngroups > wave) ? (ngroups - wave + kWaves - 1) / kWaves : 0;
-    int pid_lane = -1;  // lane s*PPS+k holds the page id of step s, page k
-    if (lane < nsteps * PPS) {
-      const int s = lane / PPS, k = lane - s * PPS;
-      const int pi = (wave + s * kWaves) * PPS + k;
-      if (pi < np) {
-        const int pid = a.page_table[(int64_t)b * a.pt_stride + t0 / kPageSize + pi];
-        pid_lane = (pid >= 0 && (int64_t)pid < a.num_pages) ? pid : -1;
+  // page ids of the wave's pages of an item: lane s*PPS+k holds step s, page k
+  auto load_pids = [&](const Item& it) {
+    int pid = -1;
+    if (lane < it.nsteps * PPS) {
+      const int st = lane / PPS, k = lane - st * PPS;
+      const int pi = (wave + st * kWaves) * PPS + k;
+      if (pi < it.np) {
+        const int v = a.page_table[(int64_t)it.b * a.pt_stride + it.t0 / kPageSize + pi];
+        pid = (v >= 0 && (int64_t)v < a.num_pages) ? v : -1;
       }
     }
-
-    // query slice of this lane, log2 domain
-    float qf[GT][EPL];
+    return pid;
+  };
+  // the query slice of this lane as bf16 pairs (exact; the softmax scale is
+  // applied to each score in fp32)
+  auto load_q = [&](const Item& it, uint32_t (*qb)[EPL / 2]) {
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
-      const uint16_t* qrow = a.q + ((int64_t)b * a.n_q_heads + h0 + h) * D + d0;
+      const uint16_t* qrow = a.q + ((int64_t)it.b * a.n_q_heads + it.h0 + h) * D + d0;
 #pragma unroll
       for (int e = 0; e < EPL; e += 8) {
         const uint4 v = *reinterpret_cast<const uint4*>(qrow + e);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        qb[h][e / 2 + 0] = v.x;
+        qb[h][e / 2 + 1] = v.y;
+        qb[h][e / 2 + 2] = v.z;
+        qb[h][e / 2 + 3] = v.w;
+      }
+    }
+  };
+
+  // A step's loads.  The scales of a (page, kv head) chunk (SCL bytes) come
+  // in one 4-byte-per-lane load: lane L holds bytes [4L, 4L+4), lanes past
+  // the chunk read 0 through the descriptor's bound.  They are staged through
+  // a wave-private LDS area when the step is computed.
+  struct Buf {
+    Raw<NDW> k[ROWS], v[ROWS];
+    uint32_t ks[PPS], vs[PPS];
+  };
+  // Loads of one step: always issued (a masked page reads page 0, and rows
+  // it holds are never used), so no branch makes the compiler wait on them.
+  // The page base is wave-uniform; lanes add 32-bit offsets; the buffer
+  // descriptor bounds each access to its page chunk.
+  auto load_step = [&](const Item& it, int pid, int st, Buf& X) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          qf[h][e + 2 * k] = bf16_lo(w[k]) * p.scale_log2;
-          qf[h][e + 2 * k + 1] = bf16_hi(w[k]) * p.scale_log2;
+    for (int k = 0; k < PPS; ++k) {
+      const int P = max(__builtin_amdgcn_readlane(pid, st * PPS + k), 0);
+      const int64_t row0 = (int64_t)P * page_rows + (int64_t)it.kvh * kPageSize;
+      const auto rk = page_rsrc(a.k_pool + row0 * D * ESZ, CODE);
+      const auto rv = page_rsrc(a.v_pool + row0 * D * ESZ, CODE);
+#pragma unroll
+      for (int i = 0; i < LPP; ++i) {
+        X.k[k * LPP + i] = buf_load<NDW>(rk, code_off[i]);
+        X.v[k * LPP + i] = buf_load<NDW>(rv, code_off[i]);
+      }
+      if constexpr (QT != QT_BF16) {
+        const auto rks = page_rsrc(a.k_scales + row0 * NB, SCL);
+        const auto rvs = page_rsrc(a.v_scales + row0 * NB, SCL);
+        X.ks[k] = __builtin_amdgcn_raw_buffer_load_b32(rks, lane * 4, 0, 0);
+        X.vs[k] = __builtin_amdgcn_raw_buffer_load_b32(rvs, lane * 4, 0, 0);
+      }
+    }
+  };
+
+  float m[GT], lsum[GT], acc[GT][EPL];
+  uint32_t qb[GT][EPL / 2];
+
+  auto compute = [&](const Item& it, int pid, int st, const Buf& X) {
+    // scales of this step's pages -> this wave's LDS area -> one per row
+    float ksf[ROWS], vsf[ROWS];
+    if constexpr (QT != QT_BF16) {
+      uint8_t* sw = s_scl[wave];
+#pragma unroll
+      for (int k = 0; k < PPS; ++k) {
+        if (lane * 4 < SCL) {
+          *reinterpret_cast<uint32_t*>(sw + (2 * k) * SCL + lane * 4) = X.ks[k];
+          *reinterpret_cast<uint32_t*>(sw + (2 * k + 1) * SCL + lane * 4) = X.vs[k];
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int k = 0; k < PPS; ++k)
+#pragma unroll
+        for (int i = 0; i < LPP; ++i) {
+          ksf[k * LPP + i] = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sw + (2 * k) * SCL + scale_off[i]));
+          vsf[k * LPP + i] = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sw + (2 * k + 1) * SCL + scale_off[i]));
+        }
+      __builtin_amdgcn_wave_barrier();
+    } else {
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        ksf[r] = 1.0f;
+        vsf[r] = 1.0f;
+      }
+    }
+    // row validity: page present and token before the item end
+    bool ok[ROWS];
+#pragma unroll
+    for (int k = 0; k < PPS; ++k) {
+      const int P = __builtin_amdgcn_readlane(pid, st * PPS + k);
+      const int pi = (wave + st * kWaves) * PPS + k;
+#pragma unroll
+      for (int i = 0; i < LPP; ++i)
+        ok[k * LPP + i] = (P >= 0) && (pi * kPageSize + i * TPL + tsub < it.nt);
+    }
+    float sc[ROWS][GT];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      uint32_t kb2[EPL / 2];  // codes as bf16 pairs (exact)
+#pragma unroll
+      for (int i = 0; i < NDW; ++i)
+        decode_dword_bf16x2<QT>(X.k[r].w[i], kb2 + i * (QT == QT_BF16 ? 1 : 2));
+      const float f = ksf[r] * p.scale_log2;
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        float t = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL / 2; ++e) t = dot2_bf16(qb[h][e], kb2[e], t);
+        sc[r][h] = t * f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        const float t = group_sum<LPT>(sc[r][h]);
+        sc[r][h] = ok[r] ? t : -INFINITY;
+      }
+    // online softmax: step max per head (uniform across the wave)
+    bool grow = false;
+    float mn[GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      float t = sc[0][h];
+#pragma unroll
+      for (int r = 1; r < ROWS; ++r) t = fmaxf(t, sc[r][h]);
+      t = stride_max<LPT>(t);
+      mn[h] = fmaxf(m[h], t);
+      grow |= mn[h] > m[h];
+    }
+    if (grow) {
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        const float al = exp2_rel(m[h], mn[h]);
+        m[h] = mn[h];
+        lsum[h] *= al;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= al;
+      }
+    }
+    // weights and the weighted sum of V (rows never multiplied when masked)
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      if (ok[r]) {
+        float vv[EPL];
+        decode_raw<QT, NDW>(X.v[r], vv);
+        const float sv = vsf[r];
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          const float pr = exp2_rel(sc[r][h], m[h]);
+          lsum[h] += pr;
+          const float w = pr * sv;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(w, vv[e], acc[h][e]);
         }
       }
     }
+  };
 
-    float m[GT], lsum[GT], acc[GT][EPL];
+  Item cur = describe<PPS, GT>(p, s_prefix, blockIdx.x, wave, units, G);
+  int pid_cur = load_pids(cur);
+  load_q(cur, qb);
+  Buf A, B;
+  load_step(cur, pid_cur, 0, A);
+
+  while (true) {
+    const int nxt = cur.item + (int)gridDim.x;
+    const bool has_next = nxt < total;
+    Item nx = cur;
+    int pid_nx = -1;
+    uint32_t qn[GT][EPL / 2];
+    if (has_next) {
+      nx = describe<PPS, GT>(p, s_prefix, nxt, wave, units, G);
+      pid_nx = load_pids(nx);
+      load_q(nx, qn);
+    }
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
       m[h] = -INFINITY;
@@ -246,116 +503,18 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
     }
-
-    Raw<NDW> kr[ROWS], vr[ROWS], nkr[ROWS], nvr[ROWS];
-    float ks[ROWS], vs[ROWS], nks[ROWS], nvs[ROWS];
-    auto load_step = [&](int s, Raw<NDW>* K, Raw<NDW>* V, float* KS, float* VS) {
-#pragma unroll
-      for (int k = 0; k < PPS; ++k) {
-        const int P = __builtin_amdgcn_readlane(pid_lane, s * PPS + k);
-        if (P >= 0) {
-          const int64_t rbase = ((int64_t)P * a.n_kv_heads + kvh) * kPageSize;
-#pragma unroll
-          for (int i = 0; i < LPP; ++i) {
-            const int64_t r = rbase + i * TPL + tsub;
-            K[k * LPP + i] = load_raw<NDW>(a.k_pool + (r * D + d0) * ESZ);
-            V[k * LPP + i] = load_raw<NDW>(a.v_pool + (r * D + d0) * ESZ);
-            if constexpr (QT != QT_BF16) {
-              KS[k * LPP + i] = f16_bits_to_f32(a.k_scales[r * NB + (d0 >> 5)]);
-              VS[k * LPP + i] = f16_bits_to_f32(a.v_scales[r * NB + (d0 >> 5)]);
-            } else {
-              KS[k * LPP + i] = 1.0f;
-              VS[k * LPP + i] = 1.0f;
-            }
-          }
-        }
-      }
-    };
-
-    if (nsteps > 0) load_step(0, nkr, nvr, nks, nvs);
-    for (int s = 0; s < nsteps; ++s) {
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        kr[r] = nkr[r];
-        vr[r] = nvr[r];
-        ks[r] = nks[r];
-        vs[r] = nvs[r];
-      }
-      if (s + 1 < nsteps) load_step(s + 1, nkr, nvr, nks, nvs);
-
-      // row validity: page present and token before the sequence end
-      bool ok[ROWS];
-#pragma unroll
-      for (int k = 0; k < PPS; ++k) {
-        const int P = __builtin_amdgcn_readlane(pid_lane, s * PPS + k);
-        const int pi = (wave + s * kWaves) * PPS + k;
-#pragma unroll
-        for (int i = 0; i < LPP; ++i)
-          ok[k * LPP + i] = (P >= 0) && (pi * kPageSize + i * TPL + tsub < nt);
-      }
-
-      // scores
-      float sc[ROWS][GT];
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        float kv[EPL];
-        decode_raw<QT, NDW>(kr[r], kv);
-#pragma unroll
-        for (int h = 0; h < GT; ++h) {
-          float t = 0.0f;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) t = fmaf(qf[h][e], kv[e], t);
-          sc[r][h] = t * ks[r];
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r)
-#pragma unroll
-        for (int h = 0; h < GT; ++h) {
-          const float t = group_sum<LPT>(sc[r][h]);
-          sc[r][h] = ok[r] ? t : -INFINITY;
-        }
-
-      // online softmax: step max per head (uniform across the wave)
-      bool grow = false;
-      float mn[GT];
-#pragma unroll
-      for (int h = 0; h < GT; ++h) {
-        float t = sc[0][h];
-#pragma unroll
-        for (int r = 1; r < ROWS; ++r) t = fmaxf(t, sc[r][h]);
-        t = stride_max<LPT>(t);
-        mn[h] = fmaxf(m[h], t);
-        grow |= mn[h] > m[h];
-      }
-      if (grow) {
-#pragma unroll
-        for (int h = 0; h < GT; ++h) {
-          const float al = exp2_rel(m[h], mn[h]);
-          m[h] = mn[h];
-          lsum[h] *= al;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] *= al;
-        }
-      }
-
-      // weights and the weighted sum of V
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        if (ok[r]) {
-          float vv[EPL];
-          decode_raw<QT, NDW>(vr[r], vv);
-#pragma unroll
-          for (int h = 0; h < GT; ++h) {
-            const float pr = exp2_rel(sc[r][h], m[h]);
-            lsum[h] += pr;
-            const float w = pr * vs[r];
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(w, vv[e], acc[h][e]);
-          }
-        }
-      }
+    // stream this item's steps two at a time; the load two steps ahead is
+    // the next item's first step once this item runs out
+    for (int st = 0; st < cur.nsteps; st += 2) {
+      load_step(cur, pid_cur, st + 1, B);
+      compute(cur, pid_cur, st, A);
+      if (st + 2 < cur.nsteps)
+        load_step(cur, pid_cur, st + 2, A);
+      else if (has_next)
+        load_step(nx, pid_nx, 0, A);
+      compute(cur, pid_cur, st + 1, B);
     }
+    if (cur.nsteps == 0 && has_next) load_step(nx, pid_nx, 0, A);
 
     // ---- merge the rows held by other lanes, then the four waves ------------------
 #pragma unroll
@@ -388,6 +547,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
       s_hm[tid][1] = Ls;
     }
     __syncthreads();
+    const int item = cur.item, b = cur.b, u = cur.u, nc = cur.nc, h0 = cur.h0;
     for (int idx = tid; idx < GT * D; idx += kThreads) {
       const int h = idx / D, d = idx - h * D;
       const float M = s_hm[h][0];
@@ -400,68 +560,84 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
         a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
         if (d == 0 && a.lse) a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
       } else {
-        p.part_acc[((int64_t)item * GT + h) * D + d] = v;
+        store_agent(&p.part_acc[((int64_t)item * GT + h) * D + d], v);
         if (d == 0) {
-          p.part_ml[((int64_t)item * GT + h) * 2 + 0] = M;
-          p.part_ml[((int64_t)item * GT + h) * 2 + 1] = s_hm[h][1];
+          store_agent(&p.part_ml[((int64_t)item * GT + h) * 2 + 0], M);
+          store_agent(&p.part_ml[((int64_t)item * GT + h) * 2 + 1], s_hm[h][1]);
         }
       }
     }
-    if (nc == 1) continue;
 
-    // ---- the last item of this (sequence, kv head, head group) merges ---------------
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const int old = atomicAdd(&p.count[(int64_t)b * units + u], 1);
-      s_last = (old == nc - 1);
-    }
-    __syncthreads();
-    if (!s_last) continue;
-    __threadfence();
-    const int first = s_prefix[b] + u;  // item of chunk c: first + c * units
-    // chunk maxima -> per-head max and sum; weights kept in s_red [nc][GT]
-    for (int idx = tid; idx < nc * GT; idx += kThreads) {
-      const int c = idx / GT, h = idx - c * GT;
-      s_red[idx] = p.part_ml[((int64_t)(first + c * units) * GT + h) * 2];
-    }
-    __syncthreads();
-    for (int h = wave; h < GT; h += kWaves) {
-      float M = -INFINITY;
-      for (int c = lane; c < nc; c += 64) M = fmaxf(M, s_red[c * GT + h]);
-      M = stride_max<1>(M);
-      float Ls = 0.0f;
-      for (int c = lane; c < nc; c += 64) {
-        const float w = exp2_rel(s_red[c * GT + h], M);
-        Ls += w * p.part_ml[((int64_t)(first + c * units) * GT + h) * 2 + 1];
-        s_red[c * GT + h] = w;
+    if (nc > 1) {
+      // ---- the last item of this (sequence, kv head, head group) merges -------------
+      // every thread's partial stores are complete (agent-coherent) before
+      // the counter moves; the merging workgroup reads them with agent-scope
+      // loads
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(&p.count[(int64_t)b * units + u], 1,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old == nc - 1);
       }
-      Ls = stride_sum<1>(Ls);
-      if (lane == 0) {
-        s_hm[h][0] = M;
-        s_hm[h][1] = Ls;
+      __syncthreads();
+      if (s_last) {
+        const int first = s_prefix[b] + u;  // item of chunk c: first + c * units
+        for (int idx = tid; idx < nc * GT; idx += kThreads) {
+          const int c = idx / GT, h = idx - c * GT;
+          s_red[idx] = load_agent(&p.part_ml[((int64_t)(first + c * units) * GT + h) * 2]);
+        }
+        __syncthreads();
+        for (int h = wave; h < GT; h += kWaves) {
+          float M = -INFINITY;
+          for (int c = lane; c < nc; c += 64) M = fmaxf(M, s_red[c * GT + h]);
+          M = stride_max<1>(M);
+          float Ls = 0.0f;
+          for (int c = lane; c < nc; c += 64) {
+            const float w = exp2_rel(s_red[c * GT + h], M);
+            Ls += w * load_agent(&p.part_ml[((int64_t)(first + c * units) * GT + h) * 2 + 1]);
+            s_red[c * GT + h] = w;
+          }
+          Ls = stride_sum<1>(Ls);
+          if (lane == 0) {
+            s_hm[h][0] = M;
+            s_hm[h][1] = Ls;
+          }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < GT * D; idx += kThreads) {
+          const int h = idx / D, d = idx - h * D;
+          const float* src = p.part_acc + ((int64_t)first * GT + h) * D + d;
+          const int64_t cstride = (int64_t)units * GT * D;  // between chunks of this group
+          float v = 0.0f;
+          for (int c0 = 0; c0 < nc; c0 += 16) {  // 16 loads in flight per thread
+            float x[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              x[j] = (c0 + j < nc) ? load_agent(src + (c0 + j) * cstride) : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              if (c0 + j < nc) v += s_red[(c0 + j) * GT + h] * x[j];
+          }
+          const float M = s_hm[h][0], Ls = s_hm[h][1];
+          const int64_t orow = (int64_t)b * a.n_q_heads + h0 + h;
+          a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
+          if (d == 0 && a.lse)
+            a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
+        }
+        if (tid == 0)  // ready for the next call
+          __hip_atomic_store(&p.count[(int64_t)b * units + u], 0, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    __syncthreads();
-    for (int idx = tid; idx < GT * D; idx += kThreads) {
-      const int h = idx / D, d = idx - h * D;
-      float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
-      int c = 0;
-      for (; c + 4 <= nc; c += 4) {
-        v0 += s_red[(c + 0) * GT + h] * p.part_acc[((int64_t)(first + (c + 0) * units) * GT + h) * D + d];
-        v1 += s_red[(c + 1) * GT + h] * p.part_acc[((int64_t)(first + (c + 1) * units) * GT + h) * D + d];
-        v2 += s_red[(c + 2) * GT + h] * p.part_acc[((int64_t)(first + (c + 2) * units) * GT + h) * D + d];
-        v3 += s_red[(c + 3) * GT + h] * p.part_acc[((int64_t)(first + (c + 3) * units) * GT + h) * D + d];
-      }
-      for (; c < nc; ++c)
-        v0 += s_red[c * GT + h] * p.part_acc[((int64_t)(first + c * units) * GT + h) * D + d];
-      const float v = (v0 + v1) + (v2 + v3);
-      const float M = s_hm[h][0], Ls = s_hm[h][1];
-      const int64_t orow = (int64_t)b * a.n_q_heads + h0 + h;
-      a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
-      if (d == 0 && a.lse) a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
-    }
-    if (tid == 0) p.count[(int64_t)b * units + u] = 0;  // ready for the next call
+    if (!has_next) break;
+    cur = nx;
+    pid_cur = pid_nx;
+#pragma unroll
+    for (int h = 0; h < GT; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL / 2; ++e) qb[h][e] = qn[h][e];
   }
 }
 

@@ -48,6 +48,40 @@ __device__ __forceinline__ void q8x4_to_f32(uint32_t w, float* o) {
   o[3] = (float)(int32_t)(int8_t)(w >> 24);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Four 8-bit codes (or two bf16) -> bf16 pairs, exactly: e4m3 and int8 values
+// all fit bf16's 8-bit significand.  e4m3 uses the gfx950 scaled packed
+// conversion with scale 1.0; int8 goes through fp32.
+template <int QT>
+__device__ __forceinline__ void decode_dword_bf16x2(uint32_t w, uint32_t* o) {
+  if constexpr (QT == 1) {
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  } else if constexpr (QT == 2) {
+    float f[4];
+    q8x4_to_f32(w, f);
+    // |int8| <= 127 is exact in bf16: truncating the low 16 bits is exact
+    o[0] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+    o[1] = (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xffff0000u);
+  } else {
+    o[0] = w;
+  }
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> one bf16 pair (round to nearest even), .x in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 template <int QT>
 __device__ __forceinline__ void decode_dword(uint32_t w, float* o) {
   if constexpr (QT == 1) {

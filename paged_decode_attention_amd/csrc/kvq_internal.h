@@ -13,10 +13,12 @@ enum { QT_BF16 = 0, QT_FP8 = 1, QT_Q8 = 2 };
 constexpr int kPageSize = 16;
 // Largest batch the decode kernels index through their on-chip work list.
 constexpr int kMaxBatch = 4096;
+// Waves per workgroup of the GQA decode kernel.
+constexpr int kDecodeWaves = 4;
 // Compute units the split planner assumes (MI355X); the plan must not depend
 // on the device so that the workspace query and the call agree.
 constexpr int kPlanCUs = 256;
-// A work item spans at most this many pages (64 per wave of a 4-wave group).
+// A work item spans at most 64 pages per wave (256 for 4 waves).
 constexpr int kMaxItemPages = 256;
 // The last workgroup of a (sequence, kv head, head group) merges the chunk
 // partials itself when there are at most this many; otherwise a separate
