@@ -103,6 +103,97 @@ def cpu_baseline(wl, qtype, k_rows, v_rows, q_bits):
     }
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def decode_only(args, wl, qtype, dev) -> int:
+    """Time kvq_paged_decode alone on `wl`, sweeping pool replicas so that
+    each call reads its KV from HBM, and print one JSON line."""
+    import torch
+    from paged_decode_attention_amd import kvq
+    from paged_decode_attention_amd import workloads as W
+
+    H, D, Dv = wl.n_kv_heads, wl.head_dim_qk, wl.head_dim_v
+    one = kvq.pool_bytes(qtype, wl.num_pages, W.PAGE, H, D)[0] * (1 if wl.shared else 2)
+    R = args.replicas or max(1, min(16, -(-(1 << 30) // one)))
+    log("workload", wl.name, "qtype", qtype, "replicas", R, "pool bytes", one)
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+
+    slots = torch.arange(wl.n_slots, dtype=torch.int32, device=dev)
+    d_k = dev_bf16(wl.kv_rows(0, 0, wl.n_slots))
+    d_v = None if wl.shared else dev_bf16(wl.kv_rows(1, 0, wl.n_slots))
+    pools = []
+    for _ in range(R):
+        kp, ks = kvq.alloc_pool(qtype, wl.num_pages, H, D, device=dev)
+        if wl.shared:
+            kvq.store(qtype, d_k, None, slots, kp, ks)
+            pools.append((kp, ks, kp, ks))
+        else:
+            vp, vs = kvq.alloc_pool(qtype, wl.num_pages, H, D, device=dev)
+            kvq.store(qtype, d_k, d_v, slots, kp, ks, vp, vs)
+            pools.append((kp, ks, vp, vs))
+    torch.cuda.synchronize()
+    del d_k, d_v, slots
+    q = dev_bf16(wl.query())
+    pt = torch.from_numpy(wl.page_table).to(dev)
+    sl = torch.from_numpy(wl.seq_lens).to(dev)
+    ws = None
+    calls = []
+    for kp, ks, vp, vs in pools:
+        d = kvq.PreparedDecode(qtype, q, kp, ks, vp, vs, pt, sl, wl.sm_scale, head_dim_v=Dv,
+                               workspace=ws)
+        ws = d.workspace
+        calls.append(d)
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    if args.only == "decode":
+        for _ in range(args.steps):
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
+        log("ran %d decode calls" % (args.steps * R))
+        return 0
+    K = args.steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(K):
+        for c in calls:
+            c()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / (K * R)
+    nbytes = wl.algorithmic_bytes(qtype)
+    n_tok = int(np.minimum(wl.seq_lens, wl.max_pages * W.PAGE).sum())
+    res = {
+        "metric": "paged-decode effective HBM GB/s, 1 GPU (decode only)",
+        "value": round(nbytes / (us * 1e-6) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "higher_is_better": True,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "kv_storage": qtype, "replicas": R},
+        "decode_call_us": round(us, 3),
+        "pct_of_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_GBPS, 2),
+        "algorithmic_bytes_per_call": nbytes,
+    }
+    if wl.shared:
+        flops = 2.0 * wl.n_q_heads * n_tok * (D + Dv)
+        tf = flops / (us * 1e-6) / 1e12
+        res["tflops"] = round(tf, 1)
+        res["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+        res["t_roof_us"] = round(max(nbytes / PEAK_GBPS / 1e3, flops / MFMA_BF16_PEAK_TFLOPS / 1e6), 3)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +202,12 @@ def main() -> int:
     ap.add_argument("--qtype", default="fp8_e4m3", choices=["fp8_e4m3", "q8_0", "bf16"])
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="qwen3",
+                    choices=["qwen3", "ragged256", "single256", "mla"],
+                    help="qwen3 (default) is the decode step this benchmark reports; the others "
+                         "time kvq_paged_decode alone on that workload and print their own line")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="pool copies swept by the decode-only workloads (0: enough for 1 GB)")
     ap.add_argument("--only", choices=["decode", "copy"], default=None,
                     help="counter passes: run just the timed decode calls, or a plain "
                          "1 GiB device copy (the reference for scaling FETCH_SIZE/WRITE_SIZE)")
@@ -137,6 +234,8 @@ def main() -> int:
         torch.cuda.synchronize()
         log("copied %d x %d bytes" % (args.steps, src.numel()))
         return 0
+    if args.workload != "qwen3":
+        return decode_only(args, W.BY_NAME[args.workload](), qtype, dev)
     wl = W.qwen3(replicas=args.layers)
     L, B, H, D = wl.layer_replicas, wl.batch, wl.n_kv_heads, wl.head_dim_qk
     log("workload", wl.name, "layers", L, "qtype", qtype)

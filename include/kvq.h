@@ -172,9 +172,11 @@ size_t kvq_paged_decode_workspace_bytes(kvq_dtype dtype, int batch, int n_q_head
  *                at zero again, so a workspace is zeroed once, not per call.
  *                Calls that share a workspace must not overlap.
  * Supported: page_size 16; separate K/V with head_dim_qk == head_dim_v in
- * {32, 64, 128, 256} and any n_q_heads a multiple of n_kv_heads; the shared
- * slab with head_dim_qk 576, head_dim_v 512, n_kv_heads 1 and n_q_heads a
- * multiple of 16 up to 128; batch 1..4096; max_pages >= 1; num_pages >= 1.
+ * {32, 64, 128, 256} and any n_q_heads a multiple of n_kv_heads, batch
+ * 1..4096; the shared slab with head_dim_qk 576, head_dim_v 512, n_kv_heads
+ * 1, n_q_heads a multiple of 16 up to 128, batch 1..1024 and max_pages up to
+ * 32768; max_pages >= 1; num_pages >= 1.  For the slab, K enters the dot
+ * products as bf16(code * scale), as in the pages' dequantize-to-bf16 path.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP. */
 int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
                      const uint16_t* k_scales, const void* v_pool, const uint16_t* v_scales,

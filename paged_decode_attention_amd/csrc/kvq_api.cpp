@@ -114,8 +114,28 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
   if (head_dim_v > head_dim_qk) return no("head_dim_v %d > head_dim_qk %d", head_dim_v, head_dim_qk);
   DecodePlan p{};
   const int G = n_q_heads / n_kv_heads;
-  if (head_dim_qk == 576 && head_dim_v == 512 && n_kv_heads == 1) {
-    return no("the shared 576/512 latent slab is not supported by this build");
+  if (head_dim_qk == kMlaDqk && head_dim_v == kMlaDv && n_kv_heads == 1) {
+    if (n_q_heads % 16 != 0 || n_q_heads > 128)
+      return no("the 576/512 slab needs n_q_heads a multiple of 16 up to 128 (got %d)", n_q_heads);
+    if (batch > kMlaMaxBatch)
+      return no("batch %d exceeds %d for the 576/512 slab", batch, kMlaMaxBatch);
+    p.kind = DK_MLA;
+    p.gt = n_q_heads;
+    p.n_hg = 1;
+    // Item length in 32-token tiles: about one item per CU over the
+    // upper-bound context, at most kMlaMaxItemPages pages.
+    const int64_t tiles_per_seq = ((int64_t)max_pages * kPageSize + kMlaTile - 1) / kMlaTile;
+    int64_t item_tiles = ((int64_t)batch * tiles_per_seq + kPlanCUs - 1) / kPlanCUs;
+    const int64_t max_tiles = kMlaMaxItemPages * kPageSize / kMlaTile;
+    if (item_tiles < 1) item_tiles = 1;
+    if (item_tiles > max_tiles) item_tiles = max_tiles;
+    p.item_pages = (int)(item_tiles * kMlaTile / kPageSize);
+    const int64_t chunks = (max_pages + p.item_pages - 1) / p.item_pages;
+    if (chunks > kMlaMaxChunks)
+      return no("max_pages %d is too large for the 576/512 slab (at most %d)", max_pages,
+                kMlaMaxChunks * kMlaMaxItemPages);
+    p.fused_merge = false;
+    p.max_items = (int64_t)batch * chunks;
   } else if (head_dim_qk == head_dim_v &&
              (head_dim_qk == 32 || head_dim_qk == 64 || head_dim_qk == 128 || head_dim_qk == 256)) {
     p.kind = DK_GQA;

@@ -28,6 +28,7 @@
 // item writes its output directly; otherwise each item writes (m, l, acc)
 // to the workspace and the last workgroup to finish a (sequence, kv head,
 // head group) -- found with a counter that it resets -- merges them.
+#include "kvq_attn.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -36,8 +37,6 @@ namespace {
 
 constexpr int kWaves = kDecodeWaves;
 constexpr int kThreads = 64 * kWaves;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
 template <int QT, int D>
 struct Geo {
@@ -87,133 +86,6 @@ __device__ __forceinline__ void decode_raw(const Raw<NDW>& r, float* o) {
   constexpr int PER = (QT == QT_BF16) ? 2 : 4;
 #pragma unroll
   for (int i = 0; i < NDW; ++i) decode_dword<QT>(r.w[i], o + PER * i);
-}
-
-// DPP lane moves inside a row of 16 lanes (VALU, no LDS traffic).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
-constexpr int kHalfMirror = 0x141; // lane i <-> 7-i within 8
-constexpr int kRowMirror = 0x140;  // lane i <-> 15-i within 16
-template <int R>
-constexpr int kRowRor = 0x120 + R;  // rotate right by R within 16
-
-// Lane exchange across rows of 16 / halves of 32 (gfx950 permlane swaps,
-// VALU only): with both operands equal, the pair returned holds the value of
-// lane l and of lane l^16 (resp. l^32), so their sum is the 2-lane sum.
-__device__ __forceinline__ float sum_xor16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_xor32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float max_xor16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// Sum over aligned groups of W consecutive lanes (W a power of two <= 64):
-// each step adds the partner that holds the sum of the neighbouring half.
-template <int W>
-__device__ __forceinline__ float group_sum(float v) {
-  if constexpr (W >= 2) v += dpp<kQuadXor1>(v);
-  if constexpr (W >= 4) v += dpp<kQuadXor2>(v);
-  if constexpr (W >= 8) v += dpp<kHalfMirror>(v);
-  if constexpr (W >= 16) v += dpp<kRowMirror>(v);
-  if constexpr (W >= 32) v = sum_xor16(v);
-  if constexpr (W >= 64) v = sum_xor32(v);
-  return v;
-}
-// Sum / max over the lanes with equal (lane mod S): rotations by S, 2S, ...
-// inside each row of 16 visit every such lane once, then across rows.
-template <int S>
-__device__ __forceinline__ float stride_sum(float v) {
-  if constexpr (S <= 1) v += dpp<kRowRor<1>>(v);
-  if constexpr (S <= 2) v += dpp<kRowRor<2>>(v);
-  if constexpr (S <= 4) v += dpp<kRowRor<4>>(v);
-  if constexpr (S <= 8) v += dpp<kRowRor<8>>(v);
-  if constexpr (S <= 16) v = sum_xor16(v);
-  if constexpr (S <= 32) v = sum_xor32(v);
-  return v;
-}
-template <int S>
-__device__ __forceinline__ float stride_max(float v) {
-  if constexpr (S <= 1) v = fmaxf(v, dpp<kRowRor<1>>(v));
-  if constexpr (S <= 2) v = fmaxf(v, dpp<kRowRor<2>>(v));
-  if constexpr (S <= 4) v = fmaxf(v, dpp<kRowRor<4>>(v));
-  if constexpr (S <= 8) v = fmaxf(v, dpp<kRowRor<8>>(v));
-  if constexpr (S <= 16) v = max_xor16(v);
-  if constexpr (S <= 32) v = max_xor32(v);
-  return v;
-}
-
-// Split-K partials cross workgroups on different XCDs: agent-scope relaxed
-// accesses keep them coherent without flushing the L2.
-__device__ __forceinline__ void store_agent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ int clamped_len(const DecodeArgs& a, int b) {
-  int L = a.seq_lens[b];
-  const int64_t cap = (int64_t)a.max_pages * kPageSize;
-  if (L < 0) L = 0;
-  if ((int64_t)L > cap) L = (int)cap;
-  return L;
-}
-
-// Exclusive scan of per-sequence item counts into s_prefix[0..B], by all 256
-// threads: each sums a contiguous range of sequences, the ranges are scanned
-// with wave shuffles and one LDS exchange, then written out.
-__device__ void build_prefix(const DecodeArgs& a, int item_tokens, int units, int* s_prefix,
-                             int* s_wave) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int B = a.batch;
-  const int per = (B + kThreads - 1) / kThreads;
-  const int b0 = tid * per, b1 = min(b0 + per, B);
-  int local = 0;
-  for (int b = b0; b < b1; ++b) local += (clamped_len(a, b) + item_tokens - 1) / item_tokens * units;
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
-  }
-  if (lane == 63) s_wave[wave] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += s_wave[w];
-  int run = base + incl - local;
-  for (int b = b0; b < b1; ++b) {
-    s_prefix[b] = run;
-    run += (clamped_len(a, b) + item_tokens - 1) / item_tokens * units;
-  }
-  if (tid == kThreads - 1) s_prefix[B] = base + incl;
-  __syncthreads();
-}
-
-// exp2(x - m) that is 0 (not NaN) when both are -inf.  The raw hardware
-// exp2 is enough here: arguments are <= 0 and tiny results may flush to 0.
-__device__ __forceinline__ float exp2_rel(float x, float m) {
-  return (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - m);
-}
-
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
-constexpr int kNonTemporal = 2;         // cache policy: streaming (read once)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
 }
 
 template <int NDW>
@@ -288,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
   const int units = a.n_kv_heads * p.n_hg;
   const int G = a.n_q_heads / a.n_kv_heads;
 
-  build_prefix(a, p.item_tokens, units, s_prefix, s_wave);
+  build_prefix<kThreads>(a, p.item_tokens, units, s_prefix, s_wave);
   const int total = s_prefix[a.batch];
   if (blockIdx.x == 0)
     for (int b = tid; b <= a.batch; b += kThreads) p.prefix[b] = s_prefix[b];

@@ -27,6 +27,16 @@ constexpr int kFusedMergeMaxChunks = 64;
 // Chunk weights the merge keeps in LDS: chunks * heads per item.
 constexpr int kMergeMaxWeights = 4096;
 
+// Shared MLA latent slab: row width (K), V width (leading part of the row),
+// tokens per LDS tile, and the planner's limits (batch held in LDS beside
+// the tiles, pages per work item, chunks the merge weighs per sequence).
+constexpr int kMlaDqk = 576;
+constexpr int kMlaDv = 512;
+constexpr int kMlaTile = 32;
+constexpr int kMlaMaxBatch = 1024;
+constexpr int kMlaMaxItemPages = 64;
+constexpr int kMlaMaxChunks = 512;
+
 // GQA decode geometry shared by the planner and the kernels: bytes of one
 // (page, kv head) of codes and of scales, and how many pages a wave streams
 // through its LDS buffer per step (about 8.5 KB of K and V per step).
