@@ -167,7 +167,9 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
   p.off_count = align256((size_t)(batch + 1) * sizeof(int));
   p.off_ml = p.off_count + align256((size_t)batch * n_kv_heads * p.n_hg * sizeof(int));
   p.off_acc = p.off_ml + align256((size_t)p.max_items * p.gt * 2 * sizeof(float));
-  p.bytes = p.off_acc + align256((size_t)p.max_items * p.gt * head_dim_v * sizeof(float));
+  // split-K partial outputs: fp32 accumulators (GQA) or bf16 normalized rows (MLA)
+  const size_t acc_elem = (p.kind == DK_MLA) ? sizeof(uint16_t) : sizeof(float);
+  p.bytes = p.off_acc + align256((size_t)p.max_items * p.gt * head_dim_v * acc_elem);
   *plan = p;
   return true;
 }

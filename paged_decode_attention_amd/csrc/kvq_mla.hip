@@ -31,7 +31,10 @@
 // Work item = (sequence, chunk of item_tokens tokens); items are enumerated
 // on the device from seq_lens and a persistent grid strides over them.  A
 // sequence that fits one item is written directly; otherwise each item
-// stores (m, l, acc) for every head and mla_merge_kernel combines them.
+// stores its normalized output (bf16) and (m, l) for every head, and
+// mla_merge_kernel combines them.
+#include <type_traits>
+
 #include "kvq_attn.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -50,9 +53,11 @@ constexpr int kVR = kTile + 8;        // bf16 per V^T row in LDS (80 B)
 // V^T rows are padded by 8 more elements every 16 rows so that the 16-row
 // stride of the writers falls on distinct banks.
 constexpr int kVtElems = kDv * kVR + (kDv / 16) * 8;
+// Output staging row (bf16): 512 + 8 keeps the 16-byte rows aligned.
+constexpr int kStageRow = kDv + 8;
 constexpr int kSlack = 64;            // log2-domain headroom above the softmax reference
 
-__device__ __forceinline__ int vt_index(int d, int pos) { return d * kVR + (d >> 4) * 8 + pos; }
+__host__ __device__ constexpr int vt_index(int d, int pos) { return d * kVR + (d >> 4) * 8 + pos; }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -64,13 +69,90 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// The same product for the score tiles, written so that its accumulator stays
+// in ordinary VGPRs: the 512x32 fp32 P V accumulator of a wave fills all 256
+// AGPRs, and the compiler would otherwise place these tiles there as well.
+// The compiler treats the statement as opaque, so it does not pad the
+// result's first VALU read; mfma16_v_settle() does that (more than the 18
+// wait states an 8-pass XDL result needs before a VALU read).
+__device__ __forceinline__ void mfma16_v_first(f32x4& d, u32x4 a, u32x4 b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16_v(f32x4& d, u32x4 a, u32x4 b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16_v_settle(f32x4& a, f32x4& b, f32x4& c, f32x4& d) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
+// ---- explicitly pipelined LDS operand reads ------------------------------------------
+// The multiply phases read one 16-byte operand per lane per two MFMAs; to keep
+// the matrix core busy, several reads must be in flight.  The reads are issued
+// as ordered asm with immediate offsets, and each consumer waits with an
+// explicit lgkmcnt: LDS operations complete in order, so "at most N
+// outstanding" with N of this sequence's reads issued after the one needed
+// guarantees it has landed (any other LDS or scalar operation in between only
+// makes the wait stricter).
+template <int OFF>
+__device__ __forceinline__ void ds_read16(u32x4& d, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "i"(OFF));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4& d) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(d) : "i"(N));
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;  // the low half of a flat LDS address is the LDS offset
+}
+template <int I, int N>
+struct StaticFor {
+  template <class F>
+  __device__ __forceinline__ static void run(F&& f) {
+    f(std::integral_constant<int, I>{});
+    StaticFor<I + 1, N>::run(f);
+  }
+};
+template <int N>
+struct StaticFor<N, N> {
+  template <class F>
+  __device__ __forceinline__ static void run(F&&) {}
+};
+// The compiler does not count the asm LDS writes above, so it cannot be
+// relied on to wait for them before a barrier: every barrier that publishes
+// them is preceded by this.
+__device__ __forceinline__ void lds_writes_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int OFF>
+__device__ __forceinline__ void ds_write16(uint32_t addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_write8(uint32_t addr, u32x2 v) {
+  asm volatile("ds_write_b64 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF));
+}
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int kAhead = 4;  // operand reads in flight
+constexpr int kRing = kAhead + 1;
+// Dequantization micro-steps of the next tile (one LDS write each), run from
+// P V step kStoreAt on.
+constexpr int kStoreSteps = 25;
+constexpr int kStoreAt = 32 - kStoreSteps;
+// LDS operations issued after P V read dt when step dt waits for it: the
+// reads still ahead (at most kAhead - 1) and the writes of steps dt-4 .. dt-1.
+constexpr int pv_wait(int dt) {
+  int w = 0;
+  for (int s = cmax(0, dt - kAhead); s < dt; ++s) w += (s >= kStoreAt) ? 1 : 0;
+  return cmin(kAhead - 1, 31 - dt) + w;
+}
+
 struct MlaParams {
   DecodeArgs a;
   int item_tokens;   // a multiple of kTile
   float scale_log2;  // sm_scale * log2(e)
   int* prefix;       // [batch + 1] items before each sequence (written by block 0)
-  float* part_ml;    // [items][n_q_heads][2]  (log2-domain max, sum)
-  float* part_acc;   // [items][n_q_heads][512]
+  float* part_ml;       // [items][n_q_heads][2]  (log2-domain reference, sum)
+  uint16_t* part_out;   // [items][n_q_heads][512] bf16: the item's normalized output
 };
 
 template <int QT>
@@ -125,6 +207,13 @@ __device__ __forceinline__ void dequant_dword(uint32_t w, float s, uint32_t* o) 
   }
 }
 
+// A copy of x the compiler cannot see through (it recomputes what derives
+// from it instead of holding that in registers).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ float scale_half(uint32_t w, int shift) {
   return f16_bits_to_f32((uint16_t)(w >> shift));
 }
@@ -135,8 +224,11 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
   constexpr int ESZ = Gm::ESZ, ROWB = Gm::ROWB, PAGEB = Gm::PAGEB, SCLB = Gm::SCLB;
   constexpr int VW = Gm::VW, RW = Gm::RW;
   constexpr int EPD = (QT == QT_BF16) ? 1 : 2;  // bf16 pairs per code dword
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kTile * kKS];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kVtElems];
+  // two tile buffers (K rows, V^T); at the end of an item the same memory
+  // stages each wave's output rows
+  __shared__ __attribute__((aligned(16))) uint16_t s_tiles[2 * kTile * kKS + 2 * kVtElems];
+  auto kbuf = [&](int buf) { return s_tiles + buf * (kTile * kKS); };
+  auto vbuf = [&](int buf) { return s_tiles + 2 * kTile * kKS + buf * kVtElems; };
   __shared__ int s_wave[kW];
   __shared__ int s_flag[3];  // per-tile restart votes, rotating
   extern __shared__ int s_prefix[];  // [batch + 1]
@@ -159,23 +251,23 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
       for (int h = tid; h < Hq; h += kT) a.lse[(int64_t)b * Hq + h] = -INFINITY;
   }
 
-  // ---- loader geometry (fixed per thread) ---------------------------------------
-  const int q4 = tid >> 5, u = tid & 31;  // V part: token quad, 16-element unit
-  const int rt = tid >> 3, p8 = tid & 7;  // rope: token, 8-element unit
-  const int wpage = wave >> 1;            // page of the tile this wave's loads touch
-  uint32_t voff[4], soff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tip = (4 * q4 + i) & (kPageSize - 1);
-    voff[i] = (uint32_t)(tip * ROWB + u * 16 * ESZ);
-    soff[i] = (uint32_t)(tip * kNB * 2 + (u >> 2) * 4);
-  }
-  const uint32_t roff = (uint32_t)((rt & (kPageSize - 1)) * ROWB + (kDv + 8 * p8) * ESZ);
-  const uint32_t rsoff = (uint32_t)((rt & (kPageSize - 1)) * kNB * 2 + (kDv / 32) * 2);
-  const int vshift = ((u >> 1) & 1) * 16, rshift = (p8 >> 2) * 16;
-  // position of the quad's first token in a V^T row: S^T hands lane group g
-  // the tokens 4g..4g+3 of each 16-token half; they become k slots 8g..8g+7
-  const int vpos = (q4 < 4) ? 8 * q4 : 8 * (q4 - 4) + 4;
+  // ---- tile geometry ----------------------------------------------------------------
+  // Tile token t (0..31, natural order; t < 16 on the tile's first page) is
+  // K row rho(t) = 16*((t>>2)&1) + 4*(t>>3) + (t&3) in LDS, so that MFMA row
+  // tile tt, row n of the S^T product is token 8*(n>>2) + 4*tt + (n&3).  A
+  // lane in group g then holds tokens 8g .. 8g+7 of the tile after the
+  // softmax, which is exactly its k-slot range of the P^T operand, and V^T
+  // keeps tokens in natural order.
+  //
+  // Loaders: lane l of wave w owns token quad q = 2w + ((l>>3)&1) (tokens
+  // 4q .. 4q+3, all on page w>>1) and the 16-element unit u = (l&7) |
+  // ((l>>4)<<3) of the latent part; and rope token rt = 8w + (l>>3), 8-element
+  // unit p8 = l&7.  With this assignment each group of 8 (16-byte writes) or
+  // 16 lanes (8-byte writes) covers all LDS banks once: K rows are written
+  // in 16-byte halves, lanes with (u>>2)&1 set writing their second half
+  // first.  The offsets are recomputed from an opaque copy of tid where they
+  // are used, so they do not stay live across the multiply phase.
+  const int wpage = wave >> 1;
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     // ---- describe the item (uniform over the block) ------------------------------
@@ -199,6 +291,11 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
       const int v = a.page_table[(int64_t)b * a.pt_stride + t0 / kPageSize + lane];
       pid = (v >= 0 && (int64_t)v < a.num_pages) ? v : -1;
     }
+    // page id of tile j's page k (k = 0, 1); -1 past the item
+    auto page_of = [&](int j, int k) {
+      const int c = 2 * j + k;
+      return c < 64 ? __builtin_amdgcn_readlane(pid, c) : -1;
+    };
 
     // this wave's 32 query heads as MFMA B operands: qr[ht][ks] holds, for
     // head 32w + 16ht + (l%16), elements 32ks + 8(l/16) .. +7
@@ -216,66 +313,95 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
     }
 
     auto load_tile = [&](int j, MlaRaw<QT>& R) {
-      const int P = max(__builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(pid, 2 * j + wpage)), 0);
+      const int t = opaque(tid);
+      const int l = t & 63, q = 2 * (t >> 6) + ((l >> 3) & 1), u = (l & 7) | ((l >> 4) << 3);
+      const int rt = t >> 3, p8 = t & 7;
+      const uint32_t vbase = (uint32_t)((4 * (q & 3)) * ROWB + u * 16 * ESZ);
+      const uint32_t sbase = (uint32_t)((4 * (q & 3)) * kNB * 2 + (u >> 2) * 4);
+      const uint32_t roff = (uint32_t)((rt & (kPageSize - 1)) * ROWB + (kDv + 8 * p8) * ESZ);
+      const uint32_t rsoff = (uint32_t)((rt & (kPageSize - 1)) * kNB * 2 + (kDv / 32) * 2);
+      const int P = max(__builtin_amdgcn_readfirstlane(page_of(j, wpage)), 0);
       const auto rc = page_rsrc(a.k_pool + (int64_t)P * PAGEB, PAGEB);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) buf_load_dw<VW>(rc, voff[i], R.v[i]);
+      for (int i = 0; i < 4; ++i) buf_load_dw<VW>(rc, vbase + i * ROWB, R.v[i]);
       buf_load_dw<RW>(rc, roff, R.r);
       if constexpr (QT != QT_BF16) {
         const auto rs = page_rsrc(a.k_scales + (int64_t)P * (SCLB / 2), SCLB);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R.vs[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff[i], 0, 0);
+        for (int i = 0; i < 4; ++i)
+          R.vs[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, sbase + i * kNB * 2, 0, 0);
         R.rs = __builtin_amdgcn_raw_buffer_load_b32(rs, rsoff, 0, 0);
       }
     };
 
-    // dequantize a loaded tile into LDS buffer `buf`, four elements at a
-    // time for the thread's four tokens; rows of masked pages or past the
-    // item end are written as zeros
-    auto store_tile = [&](int j, const MlaRaw<QT>& R, int buf) {
-      uint16_t* K = s_k[buf];
-      uint16_t* Vt = s_vt[buf];
-      const bool page_ok = __builtin_amdgcn_readlane(pid, 2 * j + wpage) >= 0;
+    // Dequantizing tile j from registers into LDS buffer `buf`, as 25
+    // micro-steps of one LDS write each (so they can be spread between the
+    // multiplies of the tile being computed):
+    //   0..3   first half of the unit, token i: dequantize, write its K row part
+    //   4..11  first half, element e: write V^T row 16u + 8h + e (4 tokens)
+    //   12..23 the same for the second half
+    //   24     rope part of token rt
+    // Rows of masked pages or past the item end are written as zeros.
+    struct StoreState {
+      uint32_t kb, vb, rb;  // LDS byte addresses: K row part, V^T element 0, rope
+      int h0;               // the half written first
       float sv[4];
-      bool ok[4];
+      bool ok[4], okr;
+      uint32_t hv[4][4];    // the current half: 4 tokens x 4 bf16 pairs
+    } st;
+    auto store_begin = [&](int j, const MlaRaw<QT>& R, int buf) {
+      const int t = opaque(tid);
+      const int l = t & 63, q = 2 * (t >> 6) + ((l >> 3) & 1), u = (l & 7) | ((l >> 4) << 3);
+      const int rt = t >> 3, p8 = t & 7;
+      const int row_q = 16 * (q & 1) + 4 * (q >> 1);
+      const int row_r = 16 * ((rt >> 2) & 1) + 4 * (rt >> 3) + (rt & 3);
+      st.kb = lds_addr(kbuf(buf)) + (uint32_t)(row_q * kKS * 2 + 32 * u);
+      st.vb = lds_addr(vbuf(buf)) + (uint32_t)(vt_index(16 * u, 4 * q) * 2);
+      st.rb = lds_addr(kbuf(buf)) + (uint32_t)(row_r * kKS * 2 + (kDv + 8 * p8) * 2);
+      st.h0 = (u >> 2) & 1;
+      const bool page_ok = page_of(j, wpage) >= 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ok[i] = page_ok && (kTile * j + 4 * q4 + i < nt);
-        sv[i] = (QT == QT_BF16) ? 1.0f : scale_half(R.vs[i], vshift);
+        st.ok[i] = page_ok && (kTile * j + 4 * q + i < nt);
+        st.sv[i] = (QT == QT_BF16) ? 1.0f : scale_half(R.vs[i], ((u >> 1) & 1) * 16);
       }
+      st.okr = page_ok && (kTile * j + rt < nt);
+    };
+    auto store_step = [&](auto sc, const MlaRaw<QT>& R) {
+      constexpr int S = decltype(sc)::value;
+      if constexpr (S < 24 && S % 12 < 4) {  // token i of half hh: dequantize
+        constexpr int hh = S / 12, i = S % 12;
+        const int h = st.h0 ^ hh;  // lane-dependent half
+        uint32_t c[VW / 2];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {  // elements 16u + 4k .. +3
-        uint32_t pr[4][2];
+        for (int k = 0; k < VW / 2; ++k) c[k] = h ? R.v[i][VW / 2 + k] : R.v[i][k];
+        uint32_t* o = st.hv[i];
+        if constexpr (QT == QT_BF16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (QT == QT_BF16) {
-            pr[i][0] = R.v[i][2 * k];
-            pr[i][1] = R.v[i][2 * k + 1];
-          } else {
-            dequant_dword<QT>(R.v[i][k], sv[i], pr[i]);
-          }
-          pr[i][0] = ok[i] ? pr[i][0] : 0u;
-          pr[i][1] = ok[i] ? pr[i][1] : 0u;
-          *reinterpret_cast<u32x2*>(K + (4 * q4 + i) * kKS + 16 * u + 4 * k) = u32x2{pr[i][0], pr[i][1]};
+          for (int k = 0; k < 4; ++k) o[k] = c[k];
+        } else {
+          dequant_dword<QT>(c[0], st.sv[i], o);
+          dequant_dword<QT>(c[1], st.sv[i], o + 2);
         }
-        // V^T: element d of the four tokens as two bf16 pairs
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          const uint32_t w01 = __builtin_amdgcn_perm(pr[1][e >> 1], pr[0][e >> 1], sel);
-          const uint32_t w23 = __builtin_amdgcn_perm(pr[3][e >> 1], pr[2][e >> 1], sel);
-          *reinterpret_cast<u32x2*>(Vt + vt_index(16 * u + 4 * k + e, vpos)) = u32x2{w01, w23};
-        }
-      }
-      {
-        const bool okr = page_ok && (kTile * j + rt < nt);
-        const float s = (QT == QT_BF16) ? 1.0f : scale_half(R.rs, rshift);
+        for (int k = 0; k < 4; ++k) o[k] = st.ok[i] ? o[k] : 0u;
+        ds_write16<i * kKS * 2>(st.kb + 16 * h, u32x4{o[0], o[1], o[2], o[3]});
+      } else if constexpr (S < 24) {  // element e of half hh: V^T row, 4 tokens
+        constexpr int hh = S / 12, e = S % 12 - 4;
+        const int h = st.h0 ^ hh;
+        constexpr uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t w01 = __builtin_amdgcn_perm(st.hv[1][e >> 1], st.hv[0][e >> 1], sel);
+        const uint32_t w23 = __builtin_amdgcn_perm(st.hv[3][e >> 1], st.hv[2][e >> 1], sel);
+        ds_write8<e * kVR * 2>(st.vb + (uint32_t)(h * 8 * kVR * 2), u32x2{w01, w23});
+      } else {  // rope
+        const int t = opaque(tid);
+        const float s = (QT == QT_BF16) ? 1.0f : scale_half(R.rs, ((t & 7) >> 2) * 16);
         uint32_t rw[4];
 #pragma unroll
         for (int k = 0; k < RW; ++k) dequant_dword<QT>(R.r[k], s, &rw[k * EPD]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) rw[k] = okr ? rw[k] : 0u;
-        *reinterpret_cast<u32x4*>(K + rt * kKS + kDv + 8 * p8) = u32x4{rw[0], rw[1], rw[2], rw[3]};
+        for (int k = 0; k < 4; ++k) rw[k] = st.okr ? rw[k] : 0u;
+        ds_write16<0>(st.rb, u32x4{rw[0], rw[1], rw[2], rw[3]});
       }
     };
 
@@ -289,23 +415,40 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
     float lsum[2];
     f32x4 acc[kDv / 16][2];
 
-    auto compute = [&](int j, int buf, int fslot) {
-      const uint16_t* K = s_k[buf];
-      const uint16_t* Vt = s_vt[buf];
-      // S^T = K Q^T: lane l holds, for head 16ht + l%16, tokens 16tt + 4g .. +3
+    // Tile j from LDS buffer `buf`; meanwhile tile j+1 (in R) is dequantized
+    // into the other buffer, and then tile j+2 is loaded into R.
+    auto compute = [&](int j, int buf, int fslot, MlaRaw<QT>& R) {
+      // S^T = K Q^T.  Read r = 2ks + tt is K rows 16tt + l%16 (see rho),
+      // elements 32ks + 8g .. +7.
       f32x4 S[2][2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) S[tt][0] = S[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < kNB; ++ks)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const u32x4 A = *reinterpret_cast<const u32x4*>(K + (16 * tt + n16) * kKS + 32 * ks + 8 * g);
-          S[tt][0] = mfma16(A, qr[0][ks], S[tt][0]);
-          S[tt][1] = mfma16(A, qr[1][ks], S[tt][1]);
-        }
-      const bool ok0 = __builtin_amdgcn_readlane(pid, 2 * j) >= 0;
-      const bool ok1 = __builtin_amdgcn_readlane(pid, 2 * j + 1) >= 0;
+      {
+        constexpr int NR = 2 * kNB;
+        const uint32_t ka = lds_addr(kbuf(buf) + n16 * kKS + 8 * g);
+        u32x4 ring[kRing];
+        StaticFor<0, kAhead>::run([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          ds_read16<(r % 2) * 16 * kKS * 2 + (r / 2) * 64>(ring[r], ka);
+        });
+        StaticFor<0, NR>::run([&](auto rc) {
+          constexpr int r = decltype(rc)::value, ks = r / 2, tt = r % 2;
+          lgkm_wait<cmin(kAhead - 1, NR - 1 - r)>(ring[r % kRing]);
+          if constexpr (ks == 0) {
+            mfma16_v_first(S[tt][0], ring[r % kRing], qr[0][ks]);
+            mfma16_v_first(S[tt][1], ring[r % kRing], qr[1][ks]);
+          } else {
+            mfma16_v(S[tt][0], ring[r % kRing], qr[0][ks]);
+            mfma16_v(S[tt][1], ring[r % kRing], qr[1][ks]);
+          }
+          if constexpr (r + kAhead < NR) {
+            constexpr int n = r + kAhead;
+            ds_read16<(n % 2) * 16 * kKS * 2 + (n / 2) * 64>(ring[n % kRing], ka);
+          }
+        });
+      }
+      mfma16_v_settle(S[0][0], S[0][1], S[1][0], S[1][1]);
+      // lane group g holds tokens 8g + 4tt + r: page 0 for g < 2
+      const bool ok0 = page_of(j, 0) >= 0, ok1 = page_of(j, 1) >= 0;
+      const bool pok = (g < 2) ? ok0 : ok1;
       u32x4 pk[2];
       bool over = false;
 #pragma unroll
@@ -315,8 +458,8 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int tok = kTile * j + 16 * tt + 4 * g + r;
-            const bool ok = (tt ? ok1 : ok0) && tok < nt;
+            const int tok = kTile * j + 8 * g + 4 * tt + r;
+            const bool ok = pok && tok < nt;
             const float v = ok ? S[tt][ht][r] * p.scale_log2 : -INFINITY;
             sc[4 * tt + r] = v;
             t = fmaxf(t, v);
@@ -336,13 +479,30 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
                        pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
       }
       if (over) s_flag[fslot] = 1;
-      // O^T += V^T P^T
-#pragma unroll
-      for (int dt = 0; dt < kDv / 16; ++dt) {
-        const u32x4 A = *reinterpret_cast<const u32x4*>(Vt + vt_index(16 * dt + n16, 8 * g));
-        acc[dt][0] = mfma16(A, pk[0], acc[dt][0]);
-        acc[dt][1] = mfma16(A, pk[1], acc[dt][1]);
+      // O^T += V^T P^T; read dt is V^T rows 16dt + l%16, tokens 8g .. 8g+7.
+      // From step kStoreAt on, each step also runs one micro-step of tile
+      // j+1's dequantization (one LDS write more per step, counted in the
+      // waits).
+      store_begin(j + 1, R, buf ^ 1);
+      {
+        constexpr int NR = kDv / 16;
+        constexpr int STEP = vt_index(16, 0) * 2;  // bytes between 16-row groups
+        const uint32_t va = lds_addr(vbuf(buf) + vt_index(n16, 8 * g));
+        u32x4 ring[kRing];
+        StaticFor<0, kAhead>::run([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          ds_read16<r * STEP>(ring[r], va);
+        });
+        StaticFor<0, NR>::run([&](auto rc) {
+          constexpr int dt = decltype(rc)::value;
+          lgkm_wait<pv_wait(dt)>(ring[dt % kRing]);
+          acc[dt][0] = mfma16(ring[dt % kRing], pk[0], acc[dt][0]);
+          acc[dt][1] = mfma16(ring[dt % kRing], pk[1], acc[dt][1]);
+          if constexpr (dt + kAhead < NR) ds_read16<(dt + kAhead) * STEP>(ring[(dt + kAhead) % kRing], va);
+          if constexpr (dt >= kStoreAt) store_step(std::integral_constant<int, dt - kStoreAt>{}, R);
+        });
       }
+      if (j + 2 < ntiles) load_tile(j + 2, R);
     };
 
     MlaRaw<QT> R;
@@ -356,21 +516,22 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
       load_tile(0, R);
       __syncthreads();  // earlier reads of both buffers and of the votes are done
       if (tid < 3) s_flag[tid] = 0;
-      store_tile(0, R, 0);
+      store_begin(0, R, 0);
+      StaticFor<0, kStoreSteps>::run([&](auto sc) { store_step(sc, R); });
       if (ntiles > 1) load_tile(1, R);
+      lds_writes_done();
       __syncthreads();
       // Tile j votes into slot j % 3 and is decided after its barrier.  The
       // slot of tile j+1 is cleared before that barrier: its last readers
       // (tile j-2's decision) are past barrier j-1, its writers after j.
+      // (The last tile also writes its spare buffer, with zeros: harmless,
+      // that buffer is not read before the next barrier.)
       bool restart = false;
       for (int j = 0, slot = 0; j < ntiles; ++j) {
         const int next = (slot == 2) ? 0 : slot + 1;
-        compute(j, j & 1, slot);
-        if (j + 1 < ntiles) {
-          store_tile(j + 1, R, (j + 1) & 1);
-          if (j + 2 < ntiles) load_tile(j + 2, R);
-        }
+        compute(j, j & 1, slot, R);
         if (tid == 0) s_flag[next] = 0;
+        lds_writes_done();
         __syncthreads();
         restart = s_flag[slot] != 0;  // the same for every thread
         if (restart) break;
@@ -382,54 +543,73 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
     }
 
     // ---- item result --------------------------------------------------------------
+    // Each head's row, normalized and rounded to bf16, goes to the output (a
+    // sequence that fits one item) or to the item's partial slot.  The rows
+    // are staged in LDS (the tile buffers are free after the loop's last
+    // barrier) so that every global store writes 1 KB contiguous per wave.
+    {
+      uint16_t* stage = s_tiles + wave * (32 * kStageRow);
+      float Lh[2];
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const float Ls = sum_xor32(sum_xor16(lsum[ht]));
-      const int h = 32 * wave + 16 * ht + n16;
-      if (h >= Hq) continue;
-      if (nc == 1) {
+      for (int ht = 0; ht < 2; ++ht) {
+        const float Ls = sum_xor32(sum_xor16(lsum[ht]));
+        Lh[ht] = Ls;
         const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-        uint16_t* orow = a.out + ((int64_t)b * Hq + h) * kDv + 4 * g;
+        uint16_t* srow = stage + (16 * ht + n16) * kStageRow + 4 * g;
 #pragma unroll
         for (int dt = 0; dt < kDv / 16; ++dt) {
           const f32x4 v = acc[dt][ht];
-          *reinterpret_cast<u32x2*>(orow + 16 * dt) =
+          *reinterpret_cast<u32x2*>(srow + 16 * dt) =
               u32x2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
         }
-        if (g == 0 && a.lse)
-          a.lse[(int64_t)b * Hq + h] = (mref[ht] == -INFINITY) ? -INFINITY : (mref[ht] + log2f(Ls)) * kLn2;
-      } else {
-        float* prow = p.part_acc + ((int64_t)item * Hq + h) * kDv + 4 * g;
+      }
 #pragma unroll
-        for (int dt = 0; dt < kDv / 16; ++dt) *reinterpret_cast<f32x4*>(prow + 16 * dt) = acc[dt][ht];
-        if (g == 0) {
-          p.part_ml[((int64_t)item * Hq + h) * 2 + 0] = mref[ht];
-          p.part_ml[((int64_t)item * Hq + h) * 2 + 1] = Ls;
+      for (int ht = 0; ht < 2; ++ht) {
+        const int h = 32 * wave + 16 * ht + n16;
+        if (g == 0 && h < Hq) {
+          if (nc == 1) {
+            if (a.lse)
+              a.lse[(int64_t)b * Hq + h] =
+                  (mref[ht] == -INFINITY) ? -INFINITY : (mref[ht] + log2f(Lh[ht])) * kLn2;
+          } else {
+            p.part_ml[((int64_t)item * Hq + h) * 2 + 0] = mref[ht];
+            p.part_ml[((int64_t)item * Hq + h) * 2 + 1] = Lh[ht];
+          }
         }
+      }
+      __builtin_amdgcn_wave_barrier();  // the stage is private to the wave
+      uint16_t* dst = (nc == 1) ? a.out + (int64_t)b * Hq * kDv
+                                : p.part_out + (int64_t)item * Hq * kDv;
+      for (int r = 0; r < 32; ++r) {
+        const int h = 32 * wave + r;
+        if (h >= Hq) break;
+        *reinterpret_cast<u32x4*>(dst + (int64_t)h * kDv + 8 * lane) =
+            *reinterpret_cast<const u32x4*>(stage + r * kStageRow + 8 * lane);
       }
     }
   }
 }
 
 // ---- split-K merge -------------------------------------------------------------------
-// Block = (sequence b, head h, 32-column slice); 8 groups of 32 threads take
-// every 8th chunk.  O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c.
-constexpr int kMergeCols = 32;
-constexpr int kMergeGroups = 8;
+// Block = (sequence b, head h, half of the columns); 16 groups of 32 threads
+// take every 16th chunk, a thread 8 columns, four chunk rows in flight.
+// With w_c = 2^(m_c - M) l_c: O = sum_c w_c O_c / sum_c w_c (O_c the chunk's
+// normalized output) and lse = M + log2(sum_c w_c) in log2 units.
+constexpr int kMergeGroups = 16;
+constexpr int kMergeCols = kDv / 2;
+constexpr int kMergeThreads = kMergeGroups * (kMergeCols / 8);
 
-__global__ __launch_bounds__(kMergeCols * kMergeGroups) void mla_merge_kernel(MlaParams p) {
+__global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaParams p) {
   const DecodeArgs& a = p.a;
   const int Hq = a.n_q_heads;
-  constexpr int kSlices = kDv / kMergeCols;
-  const int slice = blockIdx.x % kSlices;
-  const int bh = blockIdx.x / kSlices;
+  const int half = blockIdx.x & 1, bh = blockIdx.x >> 1;
   const int h = bh % Hq, b = bh / Hq;
   const int first = p.prefix[b];
   const int nc = p.prefix[b + 1] - first;
   if (nc <= 1) return;  // written by the decode kernel itself
   __shared__ float s_w[kMlaMaxChunks];
-  __shared__ float s_red[kMergeGroups][kMergeCols];
-  __shared__ float s_ML[2];
+  __shared__ __attribute__((aligned(16))) float s_red[kMergeGroups][kMergeCols];
+  __shared__ float s_L;
   const int tid = threadIdx.x, lane = tid & 63;
   if (tid < 64) {
     float M = -INFINITY;
@@ -438,42 +618,50 @@ __global__ __launch_bounds__(kMergeCols * kMergeGroups) void mla_merge_kernel(Ml
     float Ls = 0.0f;
     for (int c = lane; c < nc; c += 64) {
       const float* ml = p.part_ml + ((int64_t)(first + c) * Hq + h) * 2;
-      const float w = exp2_rel(ml[0], M);
+      const float w = exp2_rel(ml[0], M) * ml[1];
       s_w[c] = w;
-      Ls += w * ml[1];
+      Ls += w;
     }
     Ls = stride_sum<1>(Ls);
     if (lane == 0) {
-      s_ML[0] = M;
-      s_ML[1] = Ls;
+      s_L = Ls;
+      if (a.lse && half == 0)
+        a.lse[(int64_t)b * Hq + h] = (Ls > 0.0f) ? (M + log2f(Ls)) * kLn2 : -INFINITY;
     }
   }
   __syncthreads();
-  const int grp = tid / kMergeCols, j = tid % kMergeCols;
-  const int d = slice * kMergeCols + j;
-  const float* src = p.part_acc + ((int64_t)first * Hq + h) * kDv + d;
+  const int grp = tid >> 5, j = tid & 31;
+  const int d0 = half * kMergeCols + 8 * j;
+  const uint16_t* src = p.part_out + ((int64_t)first * Hq + h) * kDv + d0;
   const int64_t cstride = (int64_t)Hq * kDv;
-  float v = 0.0f;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](const u32x4& x, float w) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] += w * bf16_lo(x[k]);
+      v[2 * k + 1] += w * bf16_hi(x[k]);
+    }
+  };
   int c = grp;
   for (; c + 3 * kMergeGroups < nc; c += 4 * kMergeGroups) {
-    const float x0 = src[(int64_t)c * cstride];
-    const float x1 = src[(int64_t)(c + kMergeGroups) * cstride];
-    const float x2 = src[(int64_t)(c + 2 * kMergeGroups) * cstride];
-    const float x3 = src[(int64_t)(c + 3 * kMergeGroups) * cstride];
-    v += s_w[c] * x0 + s_w[c + kMergeGroups] * x1 + s_w[c + 2 * kMergeGroups] * x2 +
-         s_w[c + 3 * kMergeGroups] * x3;
+    u32x4 x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      x[k] = *reinterpret_cast<const u32x4*>(src + (int64_t)(c + k * kMergeGroups) * cstride);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) add(x[k], s_w[c + k * kMergeGroups]);
   }
-  for (; c < nc; c += kMergeGroups) v += s_w[c] * src[(int64_t)c * cstride];
-  s_red[grp][j] = v;
+  for (; c < nc; c += kMergeGroups) add(*reinterpret_cast<const u32x4*>(src + (int64_t)c * cstride), s_w[c]);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s_red[grp][8 * j + k] = v[k];
   __syncthreads();
   if (tid < kMergeCols) {
     float t = 0.0f;
 #pragma unroll
     for (int k = 0; k < kMergeGroups; ++k) t += s_red[k][tid];
-    const float M = s_ML[0], Ls = s_ML[1];
-    const int64_t orow = (int64_t)b * Hq + h;
-    a.out[orow * kDv + d] = (uint16_t)bf16_rne(Ls > 0.0f ? t / Ls : 0.0f);
-    if (d == 0 && a.lse) a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
+    const float Ls = s_L;
+    a.out[((int64_t)b * Hq + h) * kDv + half * kMergeCols + tid] =
+        (uint16_t)bf16_rne(Ls > 0.0f ? t / Ls : 0.0f);
   }
 }
 
@@ -483,7 +671,7 @@ hipError_t launch_q(const MlaParams& mp, int grid, int merge_grid, hipStream_t s
   mla_decode_kernel<QT><<<grid, kT, dyn, s>>>(mp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || merge_grid == 0) return e;
-  mla_merge_kernel<<<merge_grid, kMergeCols * kMergeGroups, 0, s>>>(mp);
+  mla_merge_kernel<<<merge_grid, kMergeThreads, 0, s>>>(mp);
   return hipGetLastError();
 }
 
@@ -498,12 +686,12 @@ hipError_t launch_mla_decode(const DecodeArgs& a, const DecodePlan& plan, int nu
   mp.scale_log2 = a.sm_scale * kLog2e;
   mp.prefix = reinterpret_cast<int*>(ws + plan.off_prefix);
   mp.part_ml = reinterpret_cast<float*>(ws + plan.off_ml);
-  mp.part_acc = reinterpret_cast<float*>(ws + plan.off_acc);
+  mp.part_out = reinterpret_cast<uint16_t*>(ws + plan.off_acc);
   int64_t grid = num_cus;  // one workgroup per CU fits the tiles' LDS
   if (grid > plan.max_items) grid = plan.max_items;
   if (grid < 1) grid = 1;
   const int64_t max_chunks = (a.max_pages + plan.item_pages - 1) / plan.item_pages;
-  const int merge_grid = (max_chunks > 1) ? a.batch * a.n_q_heads * (kDv / kMergeCols) : 0;
+  const int merge_grid = (max_chunks > 1) ? a.batch * a.n_q_heads * 2 : 0;
   switch (a.qtype) {
     case QT_BF16: return launch_q<QT_BF16>(mp, (int)grid, merge_grid, s);
     case QT_FP8: return launch_q<QT_FP8>(mp, (int)grid, merge_grid, s);
