@@ -20,7 +20,8 @@ Workloads (all with page size 16):
            latent + 64 rope), 128 q heads, V = first 512; the latent part is
            already on the e4m3 grid under power-of-two block-64 scales, the
            rope tail is plain bf16 N(0,1).
-  mixed    a 2^20-token pool (65536 pages) of N(0,1) background, batch 64
+  mixed    a 2^20-token pool (65536 pages) of N(0,1) background (page-seeded,
+           see Workload.page_rows), batch 64
            with contexts log-uniform in [1024, 131072], 8192 new tokens (the
            last 128 of each sequence) to store, with 1% all-zero 32-blocks,
            1% constant blocks and 0.1% +-1e4 outliers; 1% of the older page-
@@ -103,6 +104,19 @@ class Workload:
         if not out:
             return np.zeros((0, self.n_kv_heads, self.head_dim_qk), np.uint16)
         return to_bf16_bits(np.concatenate(out))
+
+    def page_rows(self, tensor: int, pages) -> np.ndarray:
+        """bf16 bits uint16 [len(pages) * 16, n_kv_heads, head_dim] for the slots
+        of `pages`, each page drawn from its own sub-stream (N(0,1)).  The mixed
+        workload's pool background is defined this way, so that any subset of
+        its 65536 pages can be generated on its own."""
+        H, D = self.n_kv_heads, self.head_dim_qk
+        pages = np.asarray(pages, dtype=np.int64)
+        out = np.empty((len(pages), PAGE, H, D), np.float32)
+        for i, pg in enumerate(pages):
+            rng = np.random.Generator(np.random.PCG64([self.seed, tensor, 1 << 24, int(pg)]))
+            out[i] = rng.standard_normal((PAGE, H, D), dtype=np.float32)
+        return to_bf16_bits(out.reshape(-1, H, D))
 
     def query(self) -> np.ndarray:
         rng = np.random.Generator(np.random.PCG64([self.seed, 7, 0]))
