@@ -139,13 +139,19 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
   } else if (head_dim_qk == head_dim_v &&
              (head_dim_qk == 32 || head_dim_qk == 64 || head_dim_qk == 128 || head_dim_qk == 256)) {
     p.kind = DK_GQA;
-    p.gt = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+    // 8 or more query heads per kv head (up to 16, or a multiple of 16) run
+    // on the matrix-core kernel, the G heads as one padded 16-wide tile
+    p.mfma = G >= 8 && head_dim_qk >= 64 && (G <= 16 || G % 16 == 0);
+    if (p.mfma)
+      p.gt = (G <= 16) ? G : 16;
+    else
+      p.gt = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     p.n_hg = G / p.gt;
     const int64_t units = (int64_t)batch * n_kv_heads * p.n_hg;
     // Item length: about 2 work items per CU over the upper-bound context,
     // a whole step of pages per wave, at most kMaxItemPages, and few enough
     // chunks per sequence for the merge's weights to fit in LDS.
-    const int step = kDecodeWaves * gqa_pages_per_step(qtype, head_dim_qk);
+    const int step = kDecodeWaves * (p.mfma ? 1 : gqa_pages_per_step(qtype, head_dim_qk));
     const int64_t target = 2 * (int64_t)kPlanCUs;
     int64_t want = ((int64_t)max_pages * units + target - 1) / target;
     const int64_t for_merge = ((int64_t)max_pages * p.gt + kMergeMaxWeights - 1) / kMergeMaxWeights;
@@ -352,7 +358,8 @@ int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
   a.workspace = workspace;
   const int cus = num_cus_current();
   hipError_t e = (plan.kind == kvq::DK_MLA) ? kvq::launch_mla_decode(a, plan, cus, stream)
-                                            : kvq::launch_gqa_decode(a, plan, cus, stream);
+                 : plan.mfma                 ? kvq::launch_gqa_mfma_decode(a, plan, cus, stream)
+                                             : kvq::launch_gqa_decode(a, plan, cus, stream);
   if (e != hipSuccess) return hip_fail(e, "kvq_paged_decode");
   return ok();
 }

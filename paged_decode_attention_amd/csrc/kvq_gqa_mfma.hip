@@ -1,0 +1,490 @@
+// kvq_gqa_mfma.hip -- paged decode attention over separate K/V pools for
+// wide query groups (8 to 16 query heads per kv head) on the matrix cores
+// (gfx950, bf16 MFMA, no LDS in the streaming loop).
+//
+// Sources: [PR103] "feat(kvcache): 8-bit KV cache (q8_0 / fp8_e4m3) behind
+// --kv-cache-dtype" §What (dequantize before the dot, because the block scale
+// runs along head_dim); [PR113] "feat(kvcache): 8-bit DSV4 window/compressed
+// KV behind --kv-cache-dtype" §Testing (split-k decode, masked (-1) columns).
+//
+// With G query heads sharing a kv head, every K and V element feeds G dot
+// products; at G >= 8 the VALU formulation runs out of issue slots before
+// HBM is busy, so the products move to the matrix cores.  The G heads of a
+// kv head (padded to 16) form the N dimension of every MFMA; tokens and
+// head_dim elements come straight from registers:
+//   - S^T = K Q^T per page (16 tokens) with v_mfma_f32_16x16x32_bf16: lane
+//     (row n, group g) holds 8 codes of token n, elements 32ks + 8g .. +7, so
+//     each k-step is exactly one 32-element scale block.  8-bit codes are
+//     exact in bf16; every block has its own product tile, and the block
+//     scales (per token, per block) weight the tiles in fp32:
+//     s_t = sum_ks scale[t][ks] * (code_t . q)_ks.
+//   - O^T += V^T P^T per page with v_mfma_f32_16x16x16_bf16: the S^T tile
+//     hands lane (head n, group g) the probabilities of tokens 4g .. 4g+3,
+//     which is its P^T operand as is.  V^T needs lane (row n, group g) to
+//     hold V[4g .. 4g+3][dv]: the lane loads D/16 consecutive codes of each
+//     of those 4 tokens (dv = (D/16)n .. +D/16) and transposes them in
+//     registers (byte permutes), so tile i's row n is dv = (D/16)n + i.  The
+//     V scale of (token, block) is the same for all of a lane's dv, so V is
+//     dequantized on the way (one multiply per element).
+// Each of the four waves streams its own pages with the next page's loads in
+// flight; the waves are merged through LDS at the end of a work item, and
+// split-K items are merged by the last workgroup of their (sequence, kv
+// head, head group), as in the VALU kernel.
+#include "kvq_attn.h"
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kW = kDecodeWaves;
+constexpr int kT = 64 * kW;
+constexpr int kN = 16;  // heads per MFMA column tile
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
+                                                   __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
+}
+
+struct MfParams {
+  DecodeArgs a;
+  int gt, n_hg, item_tokens;
+  float scale_log2;  // sm_scale * log2(e)
+  int* prefix;       // [batch + 1]
+  int* count;        // [batch * units] arrival counters, zero between calls
+  float* part_ml;    // [items][gt][2]
+  float* part_acc;   // [items][gt][D]
+};
+
+template <int QT, int D>
+struct MfGeo {
+  static constexpr int ESZ = (QT == QT_BF16) ? 2 : 1;
+  static constexpr int NKS = D / 32;              // QK k-steps = scale blocks per row
+  static constexpr int NT = D / 16;               // PV row tiles
+  static constexpr int KDW = 2 * ESZ;             // dwords of a lane's 8 K elements
+  static constexpr int VDW = (D / 16) * ESZ / 4;  // dwords of a lane's V slice per token
+  static constexpr int CODE = kPageSize * D * ESZ;
+  static constexpr int SCL = (QT == QT_BF16) ? 4 : kPageSize * NKS * 2;
+  static constexpr int SDW = (NKS + 1) / 2;       // dwords of one token's K scales
+};
+
+template <int QT, int D>
+struct PageRaw {
+  using G = MfGeo<QT, D>;
+  uint32_t k[G::NKS][G::KDW];
+  uint32_t v[4][G::VDW];
+  uint32_t ks[4][G::SDW];
+  uint32_t vs[4];
+};
+
+template <int N, int AUX>
+__device__ __forceinline__ void bload(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* o) {
+  if constexpr (N == 4) {
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  } else if constexpr (N == 2) {
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
+    o[0] = v.x; o[1] = v.y;
+  } else if constexpr (N == 1) {
+    o[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
+  } else {
+    static_assert(N == 8, "load width");
+    bload<4, AUX>(r, off, o);
+    bload<4, AUX>(r, off + 16, o + 4);
+  }
+}
+
+// 4x4 byte transpose: out[c] byte r = in[r] byte c.
+__device__ __forceinline__ void transpose4x4(const uint32_t* in, uint32_t* out) {
+  const uint32_t t0 = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
+  const uint32_t t1 = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);
+  const uint32_t t2 = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+template <int QT, int D>
+__global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
+  using Gm = MfGeo<QT, D>;
+  constexpr int ESZ = Gm::ESZ, NKS = Gm::NKS, NT = Gm::NT, KDW = Gm::KDW, VDW = Gm::VDW;
+  constexpr int CODE = Gm::CODE, SCL = Gm::SCL, SDW = Gm::SDW;
+  using Raw = PageRaw<QT, D>;
+  extern __shared__ int s_prefix[];  // [batch + 1]
+  // per-wave (m, l) and O^T accumulators at the end of an item, or the merge's
+  // chunk weights
+  constexpr int kRed = (kW * kN * D > kMergeMaxWeights) ? kW * kN * D : kMergeMaxWeights;
+  __shared__ float s_red[kRed];
+  __shared__ float s_ml[kW][kN][2];
+  __shared__ float s_hm[kN][2];
+  __shared__ int s_wave[kW];
+  __shared__ int s_last;
+
+  const DecodeArgs& a = p.a;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, g = lane >> 4;
+  const int GT = p.gt;
+  const int units = a.n_kv_heads * p.n_hg;
+  const int G = a.n_q_heads / a.n_kv_heads;
+
+  build_prefix<kT>(a, p.item_tokens, units, s_prefix, s_wave);
+  const int total = s_prefix[a.batch];
+  if (blockIdx.x == 0)
+    for (int b = tid; b <= a.batch; b += kT) p.prefix[b] = s_prefix[b];
+  for (int b = blockIdx.x; b < a.batch; b += gridDim.x) {
+    if (s_prefix[b] != s_prefix[b + 1]) continue;
+    for (int i = tid; i < a.n_q_heads * D; i += kT) a.out[(int64_t)b * a.n_q_heads * D + i] = 0;
+    if (a.lse)
+      for (int h = tid; h < a.n_q_heads; h += kT) a.lse[(int64_t)b * a.n_q_heads + h] = -INFINITY;
+  }
+
+  // per-lane offsets inside a (page, kv head) chunk
+  const uint32_t koff = (uint32_t)((n16 * D + 8 * g) * ESZ);                  // + 32 ks ESZ
+  const uint32_t voff = (uint32_t)((4 * g * D + (D / 16) * n16) * ESZ);       // + r D ESZ
+  const uint32_t ksoff = (uint32_t)(4 * g * NKS * 2);                         // + r NKS 2
+  const int vblk = n16 * D / 512;                                             // V scale block
+  const uint32_t vsoff = (uint32_t)(4 * g * NKS * 2 + (vblk * 2 & ~3));       // + r NKS 2
+  const int vshift = (vblk & 1) * 16;
+  const int64_t page_rows = (int64_t)a.n_kv_heads * kPageSize;
+
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    // ---- describe the item -------------------------------------------------------
+    int lo = 0, hi = a.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_prefix[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int rem = item - s_prefix[b];
+    const int chunk = rem / units, u = rem - chunk * units;
+    const int kvh = u / p.n_hg, hg = u - kvh * p.n_hg;
+    const int L = clamped_len(a, b);
+    const int nc = (L + p.item_tokens - 1) / p.item_tokens;
+    const int t0 = chunk * p.item_tokens;
+    const int nt = min(p.item_tokens, L - t0);
+    const int np = (nt + kPageSize - 1) / kPageSize;
+    const int h0 = kvh * G + hg * GT;
+    const int nsteps = (np > wave) ? (np - wave + kW - 1) / kW : 0;  // pages of this wave
+
+    // page ids of this wave's steps: lane k holds the id of step k (page
+    // wave + 4k of the item; at most 64 steps), -1 when masked or absent
+    int pids = -1;
+    if (lane < nsteps) {
+      const int pi = wave + lane * kW;
+      const int v = a.page_table[(int64_t)b * a.pt_stride + t0 / kPageSize + pi];
+      pids = (v >= 0 && (int64_t)v < a.num_pages) ? v : -1;
+    }
+    auto pid_of = [&](int st) { return __builtin_amdgcn_readlane(pids, st); };
+
+    // Q^T operands: qb[ks] = q[h0 + n16][32ks + 8g .. +7] (0 for padding heads)
+    u32x4 qb[NKS];
+    {
+      const bool real = n16 < GT;
+      const uint16_t* qrow = a.q + ((int64_t)b * a.n_q_heads + h0 + (real ? n16 : 0)) * D + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
+        if (!real) v = u32x4{0, 0, 0, 0};
+        qb[ks] = v;
+      }
+    }
+
+    auto load_page = [&](int pid, Raw& R) {
+      const int P = max(pid, 0);  // a masked page reads page 0; its rows are never used
+      const int64_t row0 = (int64_t)P * page_rows + (int64_t)kvh * kPageSize;
+      const auto rk = page_rsrc(a.k_pool + row0 * D * ESZ, CODE);
+      const auto rv = page_rsrc(a.v_pool + row0 * D * ESZ, CODE);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) bload<KDW, kNonTemporal>(rk, koff + 32 * ks * ESZ, R.k[ks]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bload<VDW, kNonTemporal>(rv, voff + r * D * ESZ, R.v[r]);
+      if constexpr (QT != QT_BF16) {
+        const auto rks = page_rsrc(a.k_scales + row0 * NKS, SCL);
+        const auto rvs = page_rsrc(a.v_scales + row0 * NKS, SCL);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bload<SDW, 0>(rks, ksoff + r * NKS * 2, R.ks[r]);
+          R.vs[r] = __builtin_amdgcn_raw_buffer_load_b32(rvs, vsoff + r * NKS * 2, 0, 0);
+        }
+      }
+    };
+
+    float m = -INFINITY, lsum = 0.0f;  // for head n16 (the same in every lane group)
+    f32x4 acc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int st, int pid, const Raw& R) {
+      // ---- S^T = K Q^T, one product tile per scale block ---------------------
+      float s[4];
+      if constexpr (QT == QT_BF16) {
+        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          S = mfma_k32(u32x4{R.k[ks][0], R.k[ks][1], R.k[ks][2], R.k[ks][3]}, qb[ks], S);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[r] = S[r];
+      } else {
+        f32x4 Sk[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          uint32_t kb[4];
+          decode_dword_bf16x2<QT>(R.k[ks][0], kb);
+          decode_dword_bf16x2<QT>(R.k[ks][1], kb + 2);
+          Sk[ks] = mfma_k32(u32x4{kb[0], kb[1], kb[2], kb[3]}, qb[ks], f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float t = 0.0f;
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+            t = fmaf(f16_bits_to_f32((uint16_t)(R.ks[r][ks >> 1] >> ((ks & 1) * 16))), Sk[ks][r], t);
+          s[r] = t;
+        }
+      }
+      // ---- online softmax over the page's 16 tokens (lane: head n16) ----------
+      const int tok0 = (wave + st * kW) * kPageSize + 4 * g;  // token of r = 0 in the item
+      bool ok[4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ok[r] = (pid >= 0) && (tok0 + r < nt);
+        s[r] = ok[r] ? s[r] * p.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, s[r]);
+      }
+      tmax = max_xor32(max_xor16(tmax));
+      const float mn = fmaxf(m, tmax);
+      if (__builtin_amdgcn_ballot_w64(mn > m)) {
+        const float al = exp2_rel(m, mn);
+        lsum *= al;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) acc[i] *= al;
+      }
+      m = mn;
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[r] = exp2_rel(s[r], m);
+        lsum += pr[r];
+      }
+      const u32x2 pt = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+      // ---- O^T += V^T P^T -----------------------------------------------------
+      // tokens past the item end or on a masked page: codes and scale zeroed
+      // (their probability is 0, but the slot may hold NaN codes)
+      if constexpr (QT == QT_BF16) {
+        uint32_t w[4][VDW];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int k = 0; k < VDW; ++k) w[r][k] = ok[r] ? R.v[r][k] : 0u;
+#pragma unroll
+        for (int k = 0; k < VDW; ++k) {  // dword k holds dv 2k, 2k+1
+          const u32x2 e0 = u32x2{__builtin_amdgcn_perm(w[1][k], w[0][k], 0x05040100u),
+                                 __builtin_amdgcn_perm(w[3][k], w[2][k], 0x05040100u)};
+          const u32x2 e1 = u32x2{__builtin_amdgcn_perm(w[1][k], w[0][k], 0x07060302u),
+                                 __builtin_amdgcn_perm(w[3][k], w[2][k], 0x07060302u)};
+          acc[2 * k] = mfma_k16(e0, pt, acc[2 * k]);
+          acc[2 * k + 1] = mfma_k16(e1, pt, acc[2 * k + 1]);
+        }
+      } else {
+        float sv[4];
+        uint32_t w[4][VDW];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sv[r] = ok[r] ? f16_bits_to_f32((uint16_t)(R.vs[r] >> vshift)) : 0.0f;
+#pragma unroll
+          for (int k = 0; k < VDW; ++k) w[r][k] = ok[r] ? R.v[r][k] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < VDW; ++k) {  // dword k holds dv 4k .. 4k+3 of each token
+          uint32_t col[4];
+          const uint32_t in[4] = {w[0][k], w[1][k], w[2][k], w[3][k]};
+          transpose4x4(in, col);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            float f[4];
+            decode_dword<QT>(col[c], f);
+            const u32x2 e = u32x2{pack_bf16x2(f[0] * sv[0], f[1] * sv[1]),
+                                  pack_bf16x2(f[2] * sv[2], f[3] * sv[3])};
+            acc[4 * k + c] = mfma_k16(e, pt, acc[4 * k + c]);
+          }
+        }
+      }
+    };
+
+    // ---- stream this wave's pages, the next page's loads in flight ---------------
+    Raw A, B;
+    int pa = (nsteps > 0) ? pid_of(0) : -1;
+    if (nsteps > 0) load_page(pa, A);
+    for (int st = 0; st < nsteps; st += 2) {
+      const int pb = (st + 1 < nsteps) ? pid_of(st + 1) : -1;
+      if (st + 1 < nsteps) load_page(pb, B);
+      compute(st, pa, A);
+      if (st + 1 < nsteps) {
+        const int pn = (st + 2 < nsteps) ? pid_of(st + 2) : -1;
+        if (st + 2 < nsteps) load_page(pn, A);
+        compute(st + 1, pb, B);
+        pa = pn;
+      }
+    }
+
+    // ---- merge the four waves ---------------------------------------------------------
+    lsum = sum_xor32(sum_xor16(lsum));
+    __syncthreads();  // s_red / s_ml of the previous item are free
+    // O^T tile i, lane (head n16, group g), row 4g + r is dv (D/16)(4g + r) + i
+    {
+      float* dst = s_red + (wave * kN + n16) * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) dst[(D / 16) * (4 * g + r) + i] = acc[i][r];
+      if (g == 0) {
+        s_ml[wave][n16][0] = m;
+        s_ml[wave][n16][1] = lsum;
+      }
+    }
+    __syncthreads();
+    if (tid < kN) {
+      float M = s_ml[0][tid][0];
+#pragma unroll
+      for (int w = 1; w < kW; ++w) M = fmaxf(M, s_ml[w][tid][0]);
+      float Ls = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kW; ++w) Ls += exp2_rel(s_ml[w][tid][0], M) * s_ml[w][tid][1];
+      s_hm[tid][0] = M;
+      s_hm[tid][1] = Ls;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < GT * D; idx += kT) {
+      const int h = idx / D, d = idx - h * D;
+      const float M = s_hm[h][0];
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kW; ++w) v += exp2_rel(s_ml[w][h][0], M) * s_red[(w * kN + h) * D + d];
+      if (nc == 1) {
+        const float Ls = s_hm[h][1];
+        const int64_t orow = (int64_t)b * a.n_q_heads + h0 + h;
+        a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
+        if (d == 0 && a.lse) a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
+      } else {
+        store_agent(&p.part_acc[((int64_t)item * GT + h) * D + d], v);
+        if (d == 0) {
+          store_agent(&p.part_ml[((int64_t)item * GT + h) * 2 + 0], M);
+          store_agent(&p.part_ml[((int64_t)item * GT + h) * 2 + 1], s_hm[h][1]);
+        }
+      }
+    }
+
+    if (nc > 1) {
+      // ---- the last item of this (sequence, kv head, head group) merges ---------
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(&p.count[(int64_t)b * units + u], 1,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old == nc - 1);
+      }
+      __syncthreads();
+      if (s_last) {
+        const int first = s_prefix[b] + u;  // item of chunk c: first + c * units
+        for (int idx = tid; idx < nc * GT; idx += kT) {
+          const int c = idx / GT, h = idx - c * GT;
+          s_red[idx] = load_agent(&p.part_ml[((int64_t)(first + c * units) * GT + h) * 2]);
+        }
+        __syncthreads();
+        for (int h = wave; h < GT; h += kW) {
+          float M = -INFINITY;
+          for (int c = lane; c < nc; c += 64) M = fmaxf(M, s_red[c * GT + h]);
+          M = stride_max<1>(M);
+          float Ls = 0.0f;
+          for (int c = lane; c < nc; c += 64) {
+            const float w = exp2_rel(s_red[c * GT + h], M);
+            Ls += w * load_agent(&p.part_ml[((int64_t)(first + c * units) * GT + h) * 2 + 1]);
+            s_red[c * GT + h] = w;
+          }
+          Ls = stride_sum<1>(Ls);
+          if (lane == 0) {
+            s_hm[h][0] = M;
+            s_hm[h][1] = Ls;
+          }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < GT * D; idx += kT) {
+          const int h = idx / D, d = idx - h * D;
+          const float* src = p.part_acc + ((int64_t)first * GT + h) * D + d;
+          const int64_t cstride = (int64_t)units * GT * D;
+          float v = 0.0f;
+          for (int c0 = 0; c0 < nc; c0 += 16) {
+            float x[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) x[j] = (c0 + j < nc) ? load_agent(src + (c0 + j) * cstride) : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              if (c0 + j < nc) v += s_red[(c0 + j) * GT + h] * x[j];
+          }
+          const float M = s_hm[h][0], Ls = s_hm[h][1];
+          const int64_t orow = (int64_t)b * a.n_q_heads + h0 + h;
+          a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
+          if (d == 0 && a.lse) a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
+        }
+        if (tid == 0)
+          __hip_atomic_store(&p.count[(int64_t)b * units + u], 0, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+template <int QT, int D>
+hipError_t launch_d(const MfParams& mp, int grid, hipStream_t s) {
+  const size_t dyn = (size_t)(mp.a.batch + 1) * sizeof(int);
+  gqa_mfma_kernel<QT, D><<<grid, kT, dyn, s>>>(mp);
+  return hipGetLastError();
+}
+
+template <int QT>
+hipError_t launch_q(const MfParams& mp, int grid, hipStream_t s) {
+  switch (mp.a.head_dim_qk) {
+    case 64: return launch_d<QT, 64>(mp, grid, s);
+    case 128: return launch_d<QT, 128>(mp, grid, s);
+    default: return launch_d<QT, 256>(mp, grid, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gqa_mfma_decode(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
+                                  hipStream_t s) {
+  char* ws = static_cast<char*>(a.workspace);
+  MfParams mp;
+  mp.a = a;
+  mp.gt = plan.gt;
+  mp.n_hg = plan.n_hg;
+  mp.item_tokens = plan.item_pages * kPageSize;
+  mp.scale_log2 = a.sm_scale * kLog2e;
+  mp.prefix = reinterpret_cast<int*>(ws + plan.off_prefix);
+  mp.count = reinterpret_cast<int*>(ws + plan.off_count);
+  mp.part_ml = reinterpret_cast<float*>(ws + plan.off_ml);
+  mp.part_acc = reinterpret_cast<float*>(ws + plan.off_acc);
+  int64_t grid = (int64_t)num_cus * 2;
+  if (grid > plan.max_items) grid = plan.max_items;
+  if (grid < 1) grid = 1;
+  switch (a.qtype) {
+    case QT_BF16: return launch_q<QT_BF16>(mp, (int)grid, s);
+    case QT_FP8: return launch_q<QT_FP8>(mp, (int)grid, s);
+    default: return launch_q<QT_Q8>(mp, (int)grid, s);
+  }
+}
+
+}  // namespace kvq

@@ -89,6 +89,7 @@ struct DecodePlan {
   int n_hg;           // head groups per kv head (G / gt)
   int item_pages;     // pages per split-K work item
   bool fused_merge;   // merge inside the split kernel (else a merge kernel)
+  bool mfma;          // GQA: wide query groups on the matrix-core kernel
   int64_t max_items;  // upper bound on work items (sizes the workspace)
   size_t off_prefix, off_count, off_ml, off_acc, bytes;  // workspace layout
 };
@@ -118,6 +119,8 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
 
 hipError_t launch_gqa_decode(const DecodeArgs& a, const DecodePlan& p, int num_cus,
                              hipStream_t s);
+hipError_t launch_gqa_mfma_decode(const DecodeArgs& a, const DecodePlan& p, int num_cus,
+                                  hipStream_t s);
 hipError_t launch_mla_decode(const DecodeArgs& a, const DecodePlan& p, int num_cus,
                              hipStream_t s);
 

@@ -58,7 +58,9 @@ def check(wl, qtype, rows=None, tol=TOL):
 
 @pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0", "bf16"])
 @pytest.mark.parametrize("D,Hq,Hkv", [(32, 4, 4), (64, 8, 2), (128, 16, 8), (128, 8, 1),
-                                      (256, 16, 2), (128, 12, 2), (64, 6, 2)])
+                                      (256, 16, 2), (128, 12, 2), (64, 6, 2),
+                                      # 8+ query heads per kv head: the matrix-core kernel
+                                      (64, 16, 1), (128, 32, 2), (128, 32, 1), (256, 40, 4)])
 def test_decode_small_matches_oracle(qtype, D, Hq, Hkv):
     lens = [0, 1, 15, 16, 17, 300, 1111]
     wl = small_workload(D, Hq, Hkv, lens, 80, seed=D * 7 + Hq, mask_frac=0.1)
@@ -68,11 +70,12 @@ def test_decode_small_matches_oracle(qtype, D, Hq, Hkv):
 
 
 @pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0"])
-def test_poisoned_unused_slots_never_reach_the_output(qtype):
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 16, 8), (256, 16, 2), (64, 16, 1)])
+def test_poisoned_unused_slots_never_reach_the_output(qtype, D, Hq, Hkv):
     """NaN codes and NaN scales in unwritten slots, masked pages and pages the
     table never names must not leak: the output stays finite and equal to
     the oracle's (which reads only valid tokens)."""
-    wl = small_workload(128, 16, 8, [33, 250, 17], 40, seed=5, mask_frac=0.2, extra_pages=7)
+    wl = small_workload(D, Hq, Hkv, [33, 250, 17], 40, seed=5, mask_frac=0.2, extra_pages=7)
     k = kvq()
     H, D = wl.n_kv_heads, wl.head_dim_qk
     kp, ks = k.alloc_pool(qtype, wl.num_pages, H, D)
