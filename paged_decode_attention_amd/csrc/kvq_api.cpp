@@ -151,7 +151,7 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
     // Item length: about 2 work items per CU over the upper-bound context,
     // a whole step of pages per wave, at most kMaxItemPages, and few enough
     // chunks per sequence for the merge's weights to fit in LDS.
-    const int step = kDecodeWaves * (p.mfma ? 1 : gqa_pages_per_step(qtype, head_dim_qk));
+    const int step = kDecodeWaves * (p.mfma ? 1 : gqa_pages_per_step(qtype, head_dim_qk) * kGqaDepth);
     const int64_t target = 2 * (int64_t)kPlanCUs;
     int64_t want = ((int64_t)max_pages * units + target - 1) / target;
     const int64_t for_merge = ((int64_t)max_pages * p.gt + kMergeMaxWeights - 1) / kMergeMaxWeights;

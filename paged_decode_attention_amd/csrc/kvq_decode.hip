@@ -36,6 +36,9 @@ namespace kvq {
 namespace {
 
 constexpr int kWaves = kDecodeWaves;
+// Register buffers per wave: the loads of a step are issued kDepth - 1 steps
+// before it is computed.
+constexpr int kDepth = kGqaDepth;
 constexpr int kThreads = 64 * kWaves;
 
 template <int QT, int D>
@@ -131,7 +134,7 @@ __device__ __forceinline__ Item describe(const GqaParams& p, const int* s_prefix
   it.h0 = it.kvh * G + hg * GT;
   const int ngroups = (it.np + PPS - 1) / PPS;
   const int steps = (ngroups > wave) ? (ngroups - wave + kWaves - 1) / kWaves : 0;
-  it.nsteps = (steps + 1) & ~1;  // even: the step loop is unrolled by two
+  it.nsteps = (steps + kDepth - 1) / kDepth * kDepth;  // the step loop is unrolled by kDepth
   return it;
 }
 
@@ -354,8 +357,18 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
   Item cur = describe<PPS, GT>(p, s_prefix, blockIdx.x, wave, units, G);
   int pid_cur = load_pids(cur);
   load_q(cur, qb);
-  Buf A, B;
-  load_step(cur, pid_cur, 0, A);
+  Buf R[kDepth];
+  // the loads of "pipeline step" s: step s of the current item, or of the
+  // next one once the current item runs out
+  auto issue = [&](const Item& c, int pc, bool hn, const Item& n, int pn, int s, Buf& X) {
+    if (s < c.nsteps)
+      load_step(c, pc, s, X);
+    else if (hn && s - c.nsteps < n.nsteps)
+      load_step(n, pn, s - c.nsteps, X);
+  };
+#pragma unroll
+  for (int k = 0; k < kDepth - 1; ++k)
+    if (k < cur.nsteps) load_step(cur, pid_cur, k, R[k]);
 
   while (true) {
     const int nxt = cur.item + (int)gridDim.x;
@@ -375,18 +388,20 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
     }
-    // stream this item's steps two at a time; the load two steps ahead is
-    // the next item's first step once this item runs out
-    for (int st = 0; st < cur.nsteps; st += 2) {
-      load_step(cur, pid_cur, st + 1, B);
-      compute(cur, pid_cur, st, A);
-      if (st + 2 < cur.nsteps)
-        load_step(cur, pid_cur, st + 2, A);
-      else if (has_next)
-        load_step(nx, pid_nx, 0, A);
-      compute(cur, pid_cur, st + 1, B);
+    // stream this item's steps kDepth at a time, each step's loads issued
+    // kDepth - 1 steps ahead (into the next item's first steps at the end)
+    for (int st = 0; st < cur.nsteps; st += kDepth) {
+#pragma unroll
+      for (int k = 0; k < kDepth; ++k) {
+        issue(cur, pid_cur, has_next, nx, pid_nx, st + k + kDepth - 1, R[(k + kDepth - 1) % kDepth]);
+        compute(cur, pid_cur, st + k, R[k]);
+      }
     }
-    if (cur.nsteps == 0 && has_next) load_step(nx, pid_nx, 0, A);
+    if (cur.nsteps == 0 && has_next) {
+#pragma unroll
+      for (int k = 0; k < kDepth - 1; ++k)
+        if (k < nx.nsteps) load_step(nx, pid_nx, k, R[k]);
+    }
 
     // ---- merge the rows held by other lanes, then the four waves ------------------
 #pragma unroll

@@ -47,10 +47,12 @@ __host__ __device__ constexpr int gqa_code_bytes(int qtype, int d) {
 __host__ __device__ constexpr int gqa_scale_bytes(int qtype, int d) {
   return qtype == QT_BF16 ? 0 : kPageSize * (d / 32) * 2;
 }
+constexpr int kGqaStepBytes = 8704;  // K and V bytes a wave loads per step (at least a page)
+constexpr int kGqaDepth = 2;         // steps in flight per wave, including the one computed
 __host__ __device__ constexpr int gqa_pages_per_step(int qtype, int d) {
-  return (8704 / (2 * (gqa_code_bytes(qtype, d) + gqa_scale_bytes(qtype, d)))) < 1
+  return (kGqaStepBytes / (2 * (gqa_code_bytes(qtype, d) + gqa_scale_bytes(qtype, d)))) < 1
              ? 1
-             : 8704 / (2 * (gqa_code_bytes(qtype, d) + gqa_scale_bytes(qtype, d)));
+             : kGqaStepBytes / (2 * (gqa_code_bytes(qtype, d) + gqa_scale_bytes(qtype, d)));
 }
 
 struct StoreArgs {
