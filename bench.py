@@ -40,6 +40,7 @@ def log(*a):
 
 # Sources whose change invalidates a recorded counter measurement.
 KERNEL_SOURCES = ["paged_decode_attention_amd/csrc/kvq_decode.hip",
+                  "paged_decode_attention_amd/csrc/kvq_attn.h",
                   "paged_decode_attention_amd/csrc/kvq_internal.h",
                   "paged_decode_attention_amd/csrc/kvq_device.h",
                   "paged_decode_attention_amd/csrc/kvq_api.cpp"]

@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
       mn[h] = fmaxf(m[h], t);
       grow |= mn[h] > m[h];
     }
-    if (grow) {
+    if (__builtin_amdgcn_ballot_w64(grow)) {  // uniform: every lane agrees on the max
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
         const float al = exp2_rel(m[h], mn[h]);
