@@ -161,8 +161,12 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
     const int cap = kMaxItemPages * kDecodeWaves / 4 / step * step;
     if (for_merge > cap) return no("max_pages %d is too large for the split-K merge", max_pages);
     p.item_pages = (int)(want < cap ? want : cap);
-    p.fused_merge = true;
-    p.max_items = units * ((max_pages + p.item_pages - 1) / p.item_pages);
+    const int64_t chunks = (max_pages + p.item_pages - 1) / p.item_pages;
+    // the last workgroup merges a sequence's partials itself while they are
+    // small; beyond that a merge kernel spreads the reads over the GPU
+    p.fused_merge = head_dim_v < 64 ||
+                    chunks * p.gt * head_dim_v * (int64_t)sizeof(float) <= kFusedMergeMaxBytes;
+    p.max_items = units * chunks;
   } else {
     return no("head_dim %d/%d is not supported (separate K/V: 32, 64, 128 or 256 with equal "
               "K and V widths; shared slab: 576/512 with one kv head)",

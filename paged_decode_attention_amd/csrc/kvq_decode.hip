@@ -59,6 +59,7 @@ struct Geo {
 struct GqaParams {
   DecodeArgs a;
   int gt, n_hg, item_tokens;
+  int fused;         // merge split-K partials in the last workgroup (else a merge kernel)
   float scale_log2;  // sm_scale * log2(e)
   int* prefix;       // [batch + 1] items before each sequence (written by block 0)
   int* count;        // [batch * units] arrival counters, zero between calls
@@ -455,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
       }
     }
 
-    if (nc > 1) {
+    if (nc > 1 && p.fused) {
       // ---- the last item of this (sequence, kv head, head group) merges -------------
       // every thread's partial stores are complete (agent-coherent) before
       // the counter moves; the merging workgroup reads them with agent-scope
@@ -565,6 +566,7 @@ hipError_t launch_gqa_decode(const DecodeArgs& a, const DecodePlan& plan, int nu
   gp.gt = plan.gt;
   gp.n_hg = plan.n_hg;
   gp.item_tokens = plan.item_pages * kPageSize;
+  gp.fused = plan.fused_merge ? 1 : 0;
   gp.scale_log2 = a.sm_scale * kLog2e;
   gp.prefix = reinterpret_cast<int*>(ws + plan.off_prefix);
   gp.count = reinterpret_cast<int*>(ws + plan.off_count);
@@ -573,11 +575,14 @@ hipError_t launch_gqa_decode(const DecodeArgs& a, const DecodePlan& plan, int nu
   int64_t grid = (int64_t)num_cus * 4;
   if (grid > plan.max_items) grid = plan.max_items;
   if (grid < 1) grid = 1;
+  hipError_t e;
   switch (a.qtype) {
-    case QT_BF16: return launch_d<QT_BF16>(gp, (int)grid, s);
-    case QT_FP8: return launch_d<QT_FP8>(gp, (int)grid, s);
-    default: return launch_d<QT_Q8>(gp, (int)grid, s);
+    case QT_BF16: e = launch_d<QT_BF16>(gp, (int)grid, s); break;
+    case QT_FP8: e = launch_d<QT_FP8>(gp, (int)grid, s); break;
+    default: e = launch_d<QT_Q8>(gp, (int)grid, s); break;
   }
+  if (e != hipSuccess || plan.fused_merge) return e;
+  return launch_gqa_merge(a, plan, s);
 }
 
 }  // namespace kvq

@@ -56,6 +56,7 @@ __device__ __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
 struct MfParams {
   DecodeArgs a;
   int gt, n_hg, item_tokens;
+  int fused;         // merge split-K partials in the last workgroup (else a merge kernel)
   float scale_log2;  // sm_scale * log2(e)
   int* prefix;       // [batch + 1]
   int* count;        // [batch * units] arrival counters, zero between calls
@@ -119,6 +120,9 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   constexpr int ESZ = Gm::ESZ, NKS = Gm::NKS, NT = Gm::NT, KDW = Gm::KDW, VDW = Gm::VDW;
   constexpr int CODE = Gm::CODE, SCL = Gm::SCL, SDW = Gm::SDW;
   using Raw = PageRaw<QT, D>;
+  // page buffers per wave (one page's loads in flight while one is computed;
+  // deeper register pipelines measured slower)
+  constexpr int NBUF = 2;
   extern __shared__ int s_prefix[];  // [batch + 1]
   // per-wave (m, l) and O^T accumulators at the end of an item, or the merge's
   // chunk weights
@@ -235,21 +239,27 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[r] = S[r];
       } else {
-        f32x4 Sk[NKS];
+        // blocks in groups of four: four product tiles live at a time
+        constexpr int GS = NKS < 4 ? NKS : 4;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          uint32_t kb[4];
-          decode_dword_bf16x2<QT>(R.k[ks][0], kb);
-          decode_dword_bf16x2<QT>(R.k[ks][1], kb + 2);
-          Sk[ks] = mfma_k32(u32x4{kb[0], kb[1], kb[2], kb[3]}, qb[ks], f32x4{0.f, 0.f, 0.f, 0.f});
-        }
+        for (int r = 0; r < 4; ++r) s[r] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float t = 0.0f;
+        for (int k0 = 0; k0 < NKS; k0 += GS) {
+          f32x4 Sk[GS];
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks)
-            t = fmaf(f16_bits_to_f32((uint16_t)(R.ks[r][ks >> 1] >> ((ks & 1) * 16))), Sk[ks][r], t);
-          s[r] = t;
+          for (int k = 0; k < GS; ++k) {
+            uint32_t kb[4];
+            decode_dword_bf16x2<QT>(R.k[k0 + k][0], kb);
+            decode_dword_bf16x2<QT>(R.k[k0 + k][1], kb + 2);
+            Sk[k] = mfma_k32(u32x4{kb[0], kb[1], kb[2], kb[3]}, qb[k0 + k], f32x4{0.f, 0.f, 0.f, 0.f});
+          }
+#pragma unroll
+          for (int k = 0; k < GS; ++k) {
+            const int ks = k0 + k;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              s[r] = fmaf(f16_bits_to_f32((uint16_t)(R.ks[r][ks >> 1] >> ((ks & 1) * 16))), Sk[k][r], s[r]);
+          }
         }
       }
       // ---- online softmax over the page's 16 tokens (lane: head n16) ----------
@@ -322,19 +332,17 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
       }
     };
 
-    // ---- stream this wave's pages, the next page's loads in flight ---------------
-    Raw A, B;
-    int pa = (nsteps > 0) ? pid_of(0) : -1;
-    if (nsteps > 0) load_page(pa, A);
-    for (int st = 0; st < nsteps; st += 2) {
-      const int pb = (st + 1 < nsteps) ? pid_of(st + 1) : -1;
-      if (st + 1 < nsteps) load_page(pb, B);
-      compute(st, pa, A);
-      if (st + 1 < nsteps) {
-        const int pn = (st + 2 < nsteps) ? pid_of(st + 2) : -1;
-        if (st + 2 < nsteps) load_page(pn, A);
-        compute(st + 1, pb, B);
-        pa = pn;
+    // ---- stream this wave's pages, NBUF - 1 pages' loads in flight ---------------
+    Raw R[NBUF];
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k)
+      if (k < nsteps) load_page(pid_of(k), R[k]);
+    for (int st = 0; st < nsteps; st += NBUF) {
+#pragma unroll
+      for (int k = 0; k < NBUF; ++k) {
+        const int sn = st + k + NBUF - 1;
+        if (sn < nsteps) load_page(pid_of(sn), R[(k + NBUF - 1) % NBUF]);
+        if (st + k < nsteps) compute(st + k, pid_of(st + k), R[k]);
       }
     }
 
@@ -385,7 +393,7 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
       }
     }
 
-    if (nc > 1) {
+    if (nc > 1 && p.fused) {
       // ---- the last item of this (sequence, kv head, head group) merges ---------
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_waitcnt(0);
@@ -472,6 +480,7 @@ hipError_t launch_gqa_mfma_decode(const DecodeArgs& a, const DecodePlan& plan, i
   mp.gt = plan.gt;
   mp.n_hg = plan.n_hg;
   mp.item_tokens = plan.item_pages * kPageSize;
+  mp.fused = plan.fused_merge ? 1 : 0;
   mp.scale_log2 = a.sm_scale * kLog2e;
   mp.prefix = reinterpret_cast<int*>(ws + plan.off_prefix);
   mp.count = reinterpret_cast<int*>(ws + plan.off_count);
@@ -480,11 +489,14 @@ hipError_t launch_gqa_mfma_decode(const DecodeArgs& a, const DecodePlan& plan, i
   int64_t grid = (int64_t)num_cus * 2;
   if (grid > plan.max_items) grid = plan.max_items;
   if (grid < 1) grid = 1;
+  hipError_t e;
   switch (a.qtype) {
-    case QT_BF16: return launch_q<QT_BF16>(mp, (int)grid, s);
-    case QT_FP8: return launch_q<QT_FP8>(mp, (int)grid, s);
-    default: return launch_q<QT_Q8>(mp, (int)grid, s);
+    case QT_BF16: e = launch_q<QT_BF16>(mp, (int)grid, s); break;
+    case QT_FP8: e = launch_q<QT_FP8>(mp, (int)grid, s); break;
+    default: e = launch_q<QT_Q8>(mp, (int)grid, s); break;
   }
+  if (e != hipSuccess || plan.fused_merge) return e;
+  return launch_gqa_merge(a, plan, s);
 }
 
 }  // namespace kvq

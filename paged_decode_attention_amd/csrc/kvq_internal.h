@@ -21,9 +21,9 @@ constexpr int kPlanCUs = 256;
 // A work item spans at most 64 pages per wave (256 for 4 waves).
 constexpr int kMaxItemPages = 256;
 // The last workgroup of a (sequence, kv head, head group) merges the chunk
-// partials itself when there are at most this many; otherwise a separate
-// merge kernel runs.
-constexpr int kFusedMergeMaxChunks = 64;
+// partials itself when they hold at most this many bytes; otherwise a
+// separate merge kernel runs.
+constexpr int kFusedMergeMaxBytes = 64 * 1024;
 // Chunk weights the merge keeps in LDS: chunks * heads per item.
 constexpr int kMergeMaxWeights = 4096;
 
@@ -121,6 +121,8 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
 
 hipError_t launch_gqa_decode(const DecodeArgs& a, const DecodePlan& p, int num_cus,
                              hipStream_t s);
+// The separate split-K merge of the GQA kernels (plan.fused_merge == false).
+hipError_t launch_gqa_merge(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 hipError_t launch_gqa_mfma_decode(const DecodeArgs& a, const DecodePlan& p, int num_cus,
                                   hipStream_t s);
 hipError_t launch_mla_decode(const DecodeArgs& a, const DecodePlan& p, int num_cus,

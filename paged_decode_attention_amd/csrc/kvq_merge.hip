@@ -1,0 +1,119 @@
+// kvq_merge.hip -- split-K merge for the separate-K/V decode kernels when a
+// sequence is split into many work items (long contexts, small batches).
+//
+// Source: [PR113] "feat(kvcache): 8-bit DSV4 window/compressed KV behind
+// --kv-cache-dtype" §Testing (split-k decode): partial results over chunks of
+// the sequence are combined with their log-sum-exp weights.
+//
+// Each item of (sequence b, kv head / head group u) left (m_c, l_c) per head
+// (log2-domain running max and sum) and acc_c[h][d] (fp32, unnormalized).
+// With M = max_c m_c and w_c = 2^(m_c - M):
+//   out[h][d] = sum_c w_c acc_c[h][d] / sum_c w_c l_c,  lse = (M + log2 sum_c w_c l_c) ln 2.
+// Block = (b, u, head, 64 columns); 16 groups of 16 threads take every 16th
+// chunk, a thread 4 columns, four chunk rows in flight.  The decode kernels
+// merge in their last workgroup instead when the partials of a sequence are
+// few (see plan_decode).
+#include "kvq_attn.h"
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kGroups = 16;
+constexpr int kCols = 64;
+constexpr int kThreads = kGroups * (kCols / 4);
+
+struct MergeParams {
+  DecodeArgs a;
+  int gt, n_hg, units, D;
+  const int* prefix;
+  const float* part_ml;
+  const float* part_acc;
+};
+
+__global__ __launch_bounds__(kThreads) void gqa_merge_kernel(MergeParams p) {
+  const DecodeArgs& a = p.a;
+  const int nd = p.D / kCols;
+  int x = blockIdx.x;
+  const int dchunk = x % nd;
+  x /= nd;
+  const int h = x % p.gt;
+  x /= p.gt;
+  const int u = x % p.units, b = x / p.units;
+  const int nc = (p.prefix[b + 1] - p.prefix[b]) / p.units;
+  if (nc <= 1) return;  // written by the decode kernel itself
+  const int first = p.prefix[b] + u;  // item of chunk c: first + c * units
+  __shared__ float s_w[kMergeMaxWeights];
+  __shared__ __attribute__((aligned(16))) f32x4 s_red[kGroups][kCols / 4];
+  __shared__ float s_L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int kvh = u / p.n_hg, hg = u - kvh * p.n_hg;
+  const int64_t orow = (int64_t)b * a.n_q_heads + kvh * G + hg * p.gt + h;
+  if (tid < 64) {
+    float M = -INFINITY;
+    for (int c = lane; c < nc; c += 64)
+      M = fmaxf(M, p.part_ml[((int64_t)(first + c * p.units) * p.gt + h) * 2]);
+    M = stride_max<1>(M);
+    float Ls = 0.0f;
+    for (int c = lane; c < nc; c += 64) {
+      const float* ml = p.part_ml + ((int64_t)(first + c * p.units) * p.gt + h) * 2;
+      const float w = exp2_rel(ml[0], M);
+      s_w[c] = w;
+      Ls += w * ml[1];
+    }
+    Ls = stride_sum<1>(Ls);
+    if (lane == 0) {
+      s_L = Ls;
+      if (a.lse && dchunk == 0)
+        a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
+    }
+  }
+  __syncthreads();
+  const int grp = tid / (kCols / 4), j = tid % (kCols / 4);
+  const int d = dchunk * kCols + 4 * j;
+  const float* src = p.part_acc + ((int64_t)first * p.gt + h) * p.D + d;
+  const int64_t cstride = (int64_t)p.units * p.gt * p.D;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  int c = grp;
+  for (; c + 3 * kGroups < nc; c += 4 * kGroups) {
+    f32x4 xs[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xs[k] = *reinterpret_cast<const f32x4*>(src + (int64_t)(c + k * kGroups) * cstride);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v += s_w[c + k * kGroups] * xs[k];
+  }
+  for (; c < nc; c += kGroups) v += s_w[c] * *reinterpret_cast<const f32x4*>(src + (int64_t)c * cstride);
+  s_red[grp][j] = v;
+  __syncthreads();
+  if (tid < kCols / 4) {
+    f32x4 t = s_red[0][tid];
+#pragma unroll
+    for (int k = 1; k < kGroups; ++k) t += s_red[k][tid];
+    const float Ls = s_L;
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    uint16_t* o = a.out + orow * p.D + dchunk * kCols + 4 * tid;
+    *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(t[0] * inv, t[1] * inv), pack_bf16x2(t[2] * inv, t[3] * inv)};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gqa_merge(const DecodeArgs& a, const DecodePlan& plan, hipStream_t s) {
+  const char* ws = static_cast<const char*>(a.workspace);
+  MergeParams mp;
+  mp.a = a;
+  mp.gt = plan.gt;
+  mp.n_hg = plan.n_hg;
+  mp.units = a.n_kv_heads * plan.n_hg;
+  mp.D = a.head_dim_qk;
+  mp.prefix = reinterpret_cast<const int*>(ws + plan.off_prefix);
+  mp.part_ml = reinterpret_cast<const float*>(ws + plan.off_ml);
+  mp.part_acc = reinterpret_cast<const float*>(ws + plan.off_acc);
+  const int64_t grid = (int64_t)a.batch * mp.units * plan.gt * (mp.D / kCols);
+  gqa_merge_kernel<<<(int)grid, kThreads, 0, s>>>(mp);
+  return hipGetLastError();
+}
+
+}  // namespace kvq
