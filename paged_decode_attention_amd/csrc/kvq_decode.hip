@@ -13,15 +13,17 @@
 // exclusive scan in LDS); a persistent grid strides over them.
 //
 // Inside an item each of the 4 waves streams its own pages (page groups of
-// PPS pages dealt round-robin), with the next group's K and V codes and
-// scales loaded into registers while the current group is computed, so a
-// wave keeps about 8.5 KB in flight and no block barrier sits in the loop:
+// PPS pages dealt round-robin), with the next groups' K and V codes and
+// scales loaded into registers while the current group is computed, and no
+// block barrier in the loop:
 //   - a lane owns EPL consecutive elements of a token row (one 16-byte load);
 //     its partial q.k over that slice is multiplied by the K block scale in
 //     fp32 (the code sum itself is exact) and summed over the LPT lanes of
 //     the row, giving log2-domain scores in registers;
-//   - an online softmax per head (running max, rescaled only when it grows);
-//   - p * s_v per (row, head) weights the V codes into fp32 accumulators.
+//   - softmax weights against a reference fixed per item and head (the
+//     largest score of the wave's first step; see the stream loop);
+//   - p * s_v per (row, head) weights the V codes into fp32 accumulators
+//     (for e4m3 codes two rows at a time, as bf16 pairs in dot2 products).
 // Rows past the sequence end and masked pages are never multiplied, so NaN
 // codes or scales in unused slots cannot reach the output.  The four waves
 // are merged through LDS at the end of the item.  A sequence that fits one
@@ -36,7 +38,7 @@ namespace kvq {
 namespace {
 
 constexpr int kWaves = kDecodeWaves;
-// Register buffers per wave: the loads of a step are issued kDepth - 1 steps
+// Register buffers per wave: the loads of a step are issued kDepth steps
 // before it is computed.
 constexpr int kDepth = kGqaDepth;
 constexpr int kThreads = 64 * kWaves;
@@ -135,7 +137,10 @@ __device__ __forceinline__ Item describe(const GqaParams& p, const int* s_prefix
   it.h0 = it.kvh * G + hg * GT;
   const int ngroups = (it.np + PPS - 1) / PPS;
   const int steps = (ngroups > wave) ? (ngroups - wave + kWaves - 1) / kWaves : 0;
-  it.nsteps = (steps + kDepth - 1) / kDepth * kDepth;  // the step loop is unrolled by kDepth
+  // the step loop is unrolled by kDepth and runs at least kDepth steps (a
+  // wave with no pages streams masked steps), so every path through it
+  // issues the same loads
+  it.nsteps = max((steps + kDepth - 1) / kDepth * kDepth, kDepth);
   return it;
 }
 
@@ -158,7 +163,9 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_scl[kWaves][(QT == QT_BF16 ? 1 : 2 * PPS * SCL)];
 
   const DecodeArgs& a = p.a;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform (an SGPR): page descriptors built from it stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seg = lane % LPT, tsub = lane / LPT;
   const int d0 = seg * EPL;
   const int units = a.n_kv_heads * p.n_hg;
@@ -225,37 +232,45 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
     Raw<NDW> k[ROWS], v[ROWS];
     uint32_t ks[PPS], vs[PPS];
   };
-  // Loads of one step: always issued (a masked page reads page 0, and rows
-  // it holds are never used), so no branch makes the compiler wait on them.
-  // The page base is wave-uniform; lanes add 32-bit offsets; the buffer
-  // descriptor bounds each access to its page chunk.
-  auto load_step = [&](const Item& it, int pid, int st, Buf& X) {
+  // Loads of one step.  They are issued on every path, never under a
+  // branch: the hardware counts outstanding loads in issue order, and a load
+  // skipped on one path would make the compiler wait for every load in
+  // flight (the prefetch included) before the next compute.  A masked page
+  // or a step past the end (valid == false) gets zero-length descriptors,
+  // whose loads return 0 without touching memory; such rows are never
+  // used.  The page base is wave-uniform; lanes add 32-bit
+  // offsets; the descriptor bounds each access to its page chunk.
+  auto load_step = [&](const Item& it, int pid, int st, bool valid, Buf& X) {
 #pragma unroll
     for (int k = 0; k < PPS; ++k) {
-      const int P = max(__builtin_amdgcn_readlane(pid, st * PPS + k), 0);
-      const int64_t row0 = (int64_t)P * page_rows + (int64_t)it.kvh * kPageSize;
-      const auto rk = page_rsrc(a.k_pool + row0 * D * ESZ, CODE);
-      const auto rv = page_rsrc(a.v_pool + row0 * D * ESZ, CODE);
+      const int Pr = __builtin_amdgcn_readlane(pid, min(st * PPS + k, 63));
+      const bool live = valid && Pr >= 0;
+      const int64_t row0 = (int64_t)max(Pr, 0) * page_rows + (int64_t)it.kvh * kPageSize;
+      const auto rk = page_rsrc(a.k_pool + row0 * D * ESZ, live ? CODE : 0);
+      const auto rv = page_rsrc(a.v_pool + row0 * D * ESZ, live ? CODE : 0);
 #pragma unroll
       for (int i = 0; i < LPP; ++i) {
         X.k[k * LPP + i] = buf_load<NDW>(rk, code_off[i]);
         X.v[k * LPP + i] = buf_load<NDW>(rv, code_off[i]);
       }
       if constexpr (QT != QT_BF16) {
-        const auto rks = page_rsrc(a.k_scales + row0 * NB, SCL);
-        const auto rvs = page_rsrc(a.v_scales + row0 * NB, SCL);
+        const auto rks = page_rsrc(a.k_scales + row0 * NB, live ? SCL : 0);
+        const auto rvs = page_rsrc(a.v_scales + row0 * NB, live ? SCL : 0);
         X.ks[k] = __builtin_amdgcn_raw_buffer_load_b32(rks, lane * 4, 0, 0);
         X.vs[k] = __builtin_amdgcn_raw_buffer_load_b32(rvs, lane * 4, 0, 0);
       }
     }
   };
 
-  float m[GT], lsum[GT], acc[GT][EPL];
+  float mref[GT], smax[GT], lsum[GT], acc[GT][EPL];
   uint32_t qb[GT][EPL / 2];
 
-  auto compute = [&](const Item& it, int pid, int st, const Buf& X) {
+  // Log2-domain scores of a step's rows (-inf for rows on a masked page or
+  // past the item end), their validity and the V scale of each row.
+  auto scores = [&](const Item& it, int pid, int st, const Buf& X, float (*sc)[GT], bool* ok,
+                    float* vsf) {
     // scales of this step's pages -> this wave's LDS area -> one per row
-    float ksf[ROWS], vsf[ROWS];
+    float ksf[ROWS];
     if constexpr (QT != QT_BF16) {
       uint8_t* sw = s_scl[wave];
 #pragma unroll
@@ -281,17 +296,16 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
         vsf[r] = 1.0f;
       }
     }
-    // row validity: page present and token before the item end
-    bool ok[ROWS];
+    // row validity: page present and token before the item end (a select,
+    // not a branch, so the step's work stays one scheduling region)
 #pragma unroll
     for (int k = 0; k < PPS; ++k) {
-      const int P = __builtin_amdgcn_readlane(pid, st * PPS + k);
+      const int P = __builtin_amdgcn_readlane(pid, min(st * PPS + k, 63));
       const int pi = (wave + st * kWaves) * PPS + k;
+      const int lim = P >= 0 ? it.nt : 0;
 #pragma unroll
-      for (int i = 0; i < LPP; ++i)
-        ok[k * LPP + i] = (P >= 0) && (pi * kPageSize + i * TPL + tsub < it.nt);
+      for (int i = 0; i < LPP; ++i) ok[k * LPP + i] = pi * kPageSize + i * TPL + tsub < lim;
     }
-    float sc[ROWS][GT];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       uint32_t kb2[EPL / 2];  // codes as bf16 pairs (exact)
@@ -314,95 +328,123 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
         const float t = group_sum<LPT>(sc[r][h]);
         sc[r][h] = ok[r] ? t : -INFINITY;
       }
-    // online softmax: step max per head (uniform across the wave)
-    bool grow = false;
-    float mn[GT];
+  };
+
+  // Weights against the fixed reference and the weighted sum of V.  Codes
+  // of invalid rows are zeroed (their weight is 0, but the slot may hold NaN
+  // codes or scales).
+  auto accumulate = [&](const Buf& X, float (*sc)[GT], const bool* ok, const float* vsf) {
+    float w[ROWS][GT];
 #pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      float t = sc[0][h];
-#pragma unroll
-      for (int r = 1; r < ROWS; ++r) t = fmaxf(t, sc[r][h]);
-      t = stride_max<LPT>(t);
-      mn[h] = fmaxf(m[h], t);
-      grow |= mn[h] > m[h];
-    }
-    if (__builtin_amdgcn_ballot_w64(grow)) {  // uniform: every lane agrees on the max
+    for (int r = 0; r < ROWS; ++r)
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        const float al = exp2_rel(m[h], mn[h]);
-        m[h] = mn[h];
-        lsum[h] *= al;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] *= al;
+        smax[h] = fmaxf(smax[h], sc[r][h]);
+        const float pr = __builtin_amdgcn_exp2f(sc[r][h] - mref[h]);  // 0 for -inf
+        lsum[h] += pr;
+        w[r][h] = ok[r] ? pr * vsf[r] : 0.0f;
       }
-    }
-    // weights and the weighted sum of V (rows never multiplied when masked)
+    if constexpr (QT == QT_FP8 && ROWS % 2 == 0) {
+      // two rows at a time: each element's two codes form one bf16 pair
+      // (exact) and meet the two rows' weights (rounded to bf16) in a dot2
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      if (ok[r]) {
-        float vv[EPL];
-        decode_raw<QT, NDW>(X.v[r], vv);
-        const float sv = vsf[r];
+      for (int r = 0; r < ROWS; r += 2) {
+        const uint32_t k0 = ok[r] ? 0xffffffffu : 0u, k1 = ok[r + 1] ? 0xffffffffu : 0u;
+        uint32_t wp[GT];
 #pragma unroll
-        for (int h = 0; h < GT; ++h) {
-          const float pr = exp2_rel(sc[r][h], m[h]);
-          lsum[h] += pr;
-          const float w = pr * sv;
+        for (int h = 0; h < GT; ++h) wp[h] = pack_bf16x2(w[r][h], w[r + 1][h]);
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(w, vv[e], acc[h][e]);
+        for (int i = 0; i < NDW; ++i) {
+          const uint32_t a = X.v[r].w[i] & k0, b = X.v[r + 1].w[i] & k1;
+          const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+          const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+          uint32_t vp[4];
+          decode_dword_bf16x2<QT_FP8>(lo, vp);
+          decode_dword_bf16x2<QT_FP8>(hi, vp + 2);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int h = 0; h < GT; ++h) acc[h][4 * i + j] = dot2_bf16(vp[j], wp[h], acc[h][4 * i + j]);
         }
       }
-    }
-  };
-
-  Item cur = describe<PPS, GT>(p, s_prefix, blockIdx.x, wave, units, G);
-  int pid_cur = load_pids(cur);
-  load_q(cur, qb);
-  Buf R[kDepth];
-  // the loads of "pipeline step" s: step s of the current item, or of the
-  // next one once the current item runs out
-  auto issue = [&](const Item& c, int pc, bool hn, const Item& n, int pn, int s, Buf& X) {
-    if (s < c.nsteps)
-      load_step(c, pc, s, X);
-    else if (hn && s - c.nsteps < n.nsteps)
-      load_step(n, pn, s - c.nsteps, X);
-  };
+    } else {
 #pragma unroll
-  for (int k = 0; k < kDepth - 1; ++k)
-    if (k < cur.nsteps) load_step(cur, pid_cur, k, R[k]);
-
-  while (true) {
-    const int nxt = cur.item + (int)gridDim.x;
-    const bool has_next = nxt < total;
-    Item nx = cur;
-    int pid_nx = -1;
-    uint32_t qn[GT][EPL / 2];
-    if (has_next) {
-      nx = describe<PPS, GT>(p, s_prefix, nxt, wave, units, G);
-      pid_nx = load_pids(nx);
-      load_q(nx, qn);
-    }
+      for (int r = 0; r < ROWS; ++r) {
+        const uint32_t keep = ok[r] ? 0xffffffffu : 0u;
+        Raw<NDW> vr;
 #pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      m[h] = -INFINITY;
-      lsum[h] = 0.0f;
+        for (int i = 0; i < NDW; ++i) vr.w[i] = X.v[r].w[i] & keep;
+        float vv[EPL];
+        decode_raw<QT, NDW>(vr, vv);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
-    }
-    // stream this item's steps kDepth at a time, each step's loads issued
-    // kDepth - 1 steps ahead (into the next item's first steps at the end)
-    for (int st = 0; st < cur.nsteps; st += kDepth) {
+        for (int h = 0; h < GT; ++h)
 #pragma unroll
-      for (int k = 0; k < kDepth; ++k) {
-        issue(cur, pid_cur, has_next, nx, pid_nx, st + k + kDepth - 1, R[(k + kDepth - 1) % kDepth]);
-        compute(cur, pid_cur, st + k, R[k]);
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(w[r][h], vv[e], acc[h][e]);
       }
     }
-    if (cur.nsteps == 0 && has_next) {
+  };
+
+  Buf R[kDepth];
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const Item cur = describe<PPS, GT>(p, s_prefix, item, wave, units, G);
+    const int pid_cur = load_pids(cur);
+    load_q(cur, qb);
+    // Stream the item's steps, kDepth steps' loads in flight (cur.nsteps is
+    // a multiple of kDepth).  The softmax reference of each head stays fixed
+    // over a pass: the largest score of the wave's first step (0 when it has
+    // none), so the weights 2^(s - mref) need no running-max update, no
+    // cross-lane reduction and no rescaling.  A pass whose largest score ends
+    // more than 2^64 away from the reference (weights could overflow, or all
+    // underflow) is streamed again with that score as the reference.
+    float M[GT];  // largest score per head over the wave's rows of the item
+    for (int pass = 0;; ++pass) {
 #pragma unroll
-      for (int k = 0; k < kDepth - 1; ++k)
-        if (k < nx.nsteps) load_step(nx, pid_nx, k, R[k]);
+      for (int k = 0; k < kDepth; ++k) load_step(cur, pid_cur, k, k < cur.nsteps, R[k]);
+      if (pass == 0) {
+        float sc0[ROWS][GT], vs0[ROWS];
+        bool ok0[ROWS];
+        scores(cur, pid_cur, 0, R[0], sc0, ok0, vs0);
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          float t = sc0[0][h];
+#pragma unroll
+          for (int r = 1; r < ROWS; ++r) t = fmaxf(t, sc0[r][h]);
+          t = stride_max<LPT>(t);
+          mref[h] = (t == -INFINITY) ? 0.0f : t;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        smax[h] = -INFINITY;
+        lsum[h] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
+      }
+      for (int st = 0; st < cur.nsteps; st += kDepth) {
+#pragma unroll
+        for (int k = 0; k < kDepth; ++k) {
+          float sc[ROWS][GT], vsf[ROWS];
+          bool ok[ROWS];
+          scores(cur, pid_cur, st + k, R[k], sc, ok, vsf);
+          accumulate(R[k], sc, ok, vsf);
+          const int sn = st + k + kDepth;
+          load_step(cur, pid_cur, sn, sn < cur.nsteps, R[k]);
+        }
+      }
+      bool redo = false;
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        M[h] = stride_max<LPT>(smax[h]);
+        redo |= M[h] != -INFINITY && (M[h] > mref[h] + 64.0f || M[h] < mref[h] - 64.0f);
+      }
+      if (!__builtin_amdgcn_ballot_w64(redo)) break;
+#pragma unroll
+      for (int h = 0; h < GT; ++h) mref[h] = (M[h] == -INFINITY) ? 0.0f : M[h];
     }
+    // a head with no valid row here contributes nothing to the merges
+    float m[GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) m[h] = (M[h] == -INFINITY) ? -INFINITY : mref[h];
 
     // ---- merge the rows held by other lanes, then the four waves ------------------
 #pragma unroll
@@ -435,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
       s_hm[tid][1] = Ls;
     }
     __syncthreads();
-    const int item = cur.item, b = cur.b, u = cur.u, nc = cur.nc, h0 = cur.h0;
+    const int b = cur.b, u = cur.u, nc = cur.nc, h0 = cur.h0;
     for (int idx = tid; idx < GT * D; idx += kThreads) {
       const int h = idx / D, d = idx - h * D;
       const float M = s_hm[h][0];
@@ -519,13 +561,6 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
                              __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    if (!has_next) break;
-    cur = nx;
-    pid_cur = pid_nx;
-#pragma unroll
-    for (int h = 0; h < GT; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL / 2; ++e) qb[h][e] = qn[h][e];
   }
 }
 

@@ -41,6 +41,19 @@ constexpr int kW = kDecodeWaves;
 constexpr int kT = 64 * kW;
 constexpr int kN = 16;  // heads per MFMA column tile
 
+// Lane j of each row of 16 lanes, to every lane of the row (DPP row_newbcast).
+// j is a constant once the callers' loops are unrolled; the switch folds.
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v, int j) {
+#define KVQ_RB(n) \
+  case n: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + n, 0xF, 0xF, false);
+  switch (j) {
+    KVQ_RB(0) KVQ_RB(1) KVQ_RB(2) KVQ_RB(3) KVQ_RB(4) KVQ_RB(5) KVQ_RB(6) KVQ_RB(7)
+    KVQ_RB(8) KVQ_RB(9) KVQ_RB(10) KVQ_RB(11) KVQ_RB(12) KVQ_RB(13) KVQ_RB(14)
+    default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + 15, 0xF, 0xF, false);
+  }
+#undef KVQ_RB
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -73,7 +86,6 @@ struct MfGeo {
   static constexpr int VDW = (D / 16) * ESZ / 4;  // dwords of a lane's V slice per token
   static constexpr int CODE = kPageSize * D * ESZ;
   static constexpr int SCL = (QT == QT_BF16) ? 4 : kPageSize * NKS * 2;
-  static constexpr int SDW = (NKS + 1) / 2;       // dwords of one token's K scales
 };
 
 template <int QT, int D>
@@ -81,7 +93,9 @@ struct PageRaw {
   using G = MfGeo<QT, D>;
   uint32_t k[G::NKS][G::KDW];
   uint32_t v[4][G::VDW];
-  uint32_t ks[4][G::SDW];
+  // K scales of tokens 4g .. 4g+3 (8 NKS bytes): dword j of them in lane
+  // (j, g), fetched by the lanes of the row with a DPP row broadcast
+  uint32_t ks;
   uint32_t vs[4];
 };
 
@@ -118,11 +132,11 @@ template <int QT, int D>
 __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   using Gm = MfGeo<QT, D>;
   constexpr int ESZ = Gm::ESZ, NKS = Gm::NKS, NT = Gm::NT, KDW = Gm::KDW, VDW = Gm::VDW;
-  constexpr int CODE = Gm::CODE, SCL = Gm::SCL, SDW = Gm::SDW;
+  constexpr int CODE = Gm::CODE, SCL = Gm::SCL;
   using Raw = PageRaw<QT, D>;
-  // page buffers per wave (one page's loads in flight while one is computed;
-  // deeper register pipelines measured slower)
-  constexpr int NBUF = 2;
+  // page buffers per wave: NBUF pages' loads in flight while one is computed
+  // (at head_dim 256 one wave per SIMD fits, so it keeps more)
+  constexpr int NBUF = (D >= 256) ? 4 : 2;
   extern __shared__ int s_prefix[];  // [batch + 1]
   // per-wave (m, l) and O^T accumulators at the end of an item, or the merge's
   // chunk weights
@@ -155,7 +169,7 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   // per-lane offsets inside a (page, kv head) chunk
   const uint32_t koff = (uint32_t)((n16 * D + 8 * g) * ESZ);                  // + 32 ks ESZ
   const uint32_t voff = (uint32_t)((4 * g * D + (D / 16) * n16) * ESZ);       // + r D ESZ
-  const uint32_t ksoff = (uint32_t)(4 * g * NKS * 2);                         // + r NKS 2
+  const uint32_t ksoff = (uint32_t)(8 * NKS * g + 4 * min(n16, 2 * NKS - 1));
   const int vblk = n16 * D / 512;                                             // V scale block
   const uint32_t vsoff = (uint32_t)(4 * g * NKS * 2 + (vblk * 2 & ~3));       // + r NKS 2
   const int vshift = (vblk & 1) * 16;
@@ -188,7 +202,14 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
       const int v = a.page_table[(int64_t)b * a.pt_stride + t0 / kPageSize + pi];
       pids = (v >= 0 && (int64_t)v < a.num_pages) ? v : -1;
     }
-    auto pid_of = [&](int st) { return __builtin_amdgcn_readlane(pids, st); };
+    // padded steps past the wave's pages are masked (id -1)
+    auto pid_of = [&](int st) {
+      const int v = __builtin_amdgcn_readlane(pids, min(st, 63));
+      return st < nsteps ? v : -1;
+    };
+    // the stream runs a whole number of NBUF-step rounds (at least one), so
+    // every path through it issues the same loads
+    const int nst = max((nsteps + NBUF - 1) / NBUF * NBUF, NBUF);
 
     // Q^T operands: qb[ks] = q[h0 + n16][32ks + 8g .. +7] (0 for padding heads)
     u32x4 qb[NKS];
@@ -203,34 +224,35 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
       }
     }
 
+    // The loads of a page are issued on every path, never under a branch:
+    // the hardware counts outstanding loads in issue order, and a load
+    // skipped on one path would make the compiler wait for every load in
+    // flight (the prefetch included) before the next compute.  A masked or
+    // absent page (id -1) gets zero-length descriptors, whose loads return 0
+    // without touching memory; its rows are never used.
     auto load_page = [&](int pid, Raw& R) {
-      const int P = max(pid, 0);  // a masked page reads page 0; its rows are never used
+      const int P = max(pid, 0);
       const int64_t row0 = (int64_t)P * page_rows + (int64_t)kvh * kPageSize;
-      const auto rk = page_rsrc(a.k_pool + row0 * D * ESZ, CODE);
-      const auto rv = page_rsrc(a.v_pool + row0 * D * ESZ, CODE);
+      const int code_bytes = pid >= 0 ? CODE : 0;
+      const auto rk = page_rsrc(a.k_pool + row0 * D * ESZ, code_bytes);
+      const auto rv = page_rsrc(a.v_pool + row0 * D * ESZ, code_bytes);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) bload<KDW, kNonTemporal>(rk, koff + 32 * ks * ESZ, R.k[ks]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) bload<VDW, kNonTemporal>(rv, voff + r * D * ESZ, R.v[r]);
       if constexpr (QT != QT_BF16) {
-        const auto rks = page_rsrc(a.k_scales + row0 * NKS, SCL);
-        const auto rvs = page_rsrc(a.v_scales + row0 * NKS, SCL);
+        const auto rks = page_rsrc(a.k_scales + row0 * NKS, pid >= 0 ? SCL : 0);
+        const auto rvs = page_rsrc(a.v_scales + row0 * NKS, pid >= 0 ? SCL : 0);
+        R.ks = __builtin_amdgcn_raw_buffer_load_b32(rks, ksoff, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          bload<SDW, 0>(rks, ksoff + r * NKS * 2, R.ks[r]);
+        for (int r = 0; r < 4; ++r)
           R.vs[r] = __builtin_amdgcn_raw_buffer_load_b32(rvs, vsoff + r * NKS * 2, 0, 0);
-        }
       }
     };
 
-    float m = -INFINITY, lsum = 0.0f;  // for head n16 (the same in every lane group)
-    f32x4 acc[NT];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto compute = [&](int st, int pid, const Raw& R) {
-      // ---- S^T = K Q^T, one product tile per scale block ---------------------
-      float s[4];
+    // ---- S^T = K Q^T of one page: log2-domain scores of tokens 4g .. 4g+3 of
+    // the page for head n16, -inf past the item end or on a masked page ----------
+    auto scores = [&](int st, int pid, const Raw& R, float* s, bool* ok) {
       if constexpr (QT == QT_BF16) {
         f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -239,7 +261,7 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[r] = S[r];
       } else {
-        // blocks in groups of four: four product tiles live at a time
+        // one product tile per scale block, in groups of four live tiles
         constexpr int GS = NKS < 4 ? NKS : 4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[r] = 0.0f;
@@ -257,46 +279,48 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
           for (int k = 0; k < GS; ++k) {
             const int ks = k0 + k;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              s[r] = fmaf(f16_bits_to_f32((uint16_t)(R.ks[r][ks >> 1] >> ((ks & 1) * 16))), Sk[k][r], s[r]);
+            for (int r = 0; r < 4; ++r) {
+              // scale (r, ks) is fp16 number r NKS + ks of the row's run
+              const int idx = r * NKS + ks;
+              const uint32_t w = row_bcast(R.ks, idx >> 1);
+              s[r] = fmaf(f16_bits_to_f32((uint16_t)(w >> ((idx & 1) * 16))), Sk[k][r], s[r]);
+            }
           }
         }
       }
-      // ---- online softmax over the page's 16 tokens (lane: head n16) ----------
       const int tok0 = (wave + st * kW) * kPageSize + 4 * g;  // token of r = 0 in the item
-      bool ok[4];
-      float tmax = -INFINITY;
+      const int lim = pid >= 0 ? nt : 0;  // a select, not a branch around the page's work
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        ok[r] = (pid >= 0) && (tok0 + r < nt);
+        ok[r] = tok0 + r < lim;
         s[r] = ok[r] ? s[r] * p.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, s[r]);
       }
-      tmax = max_xor32(max_xor16(tmax));
-      const float mn = fmaxf(m, tmax);
-      if (__builtin_amdgcn_ballot_w64(mn > m)) {
-        const float al = exp2_rel(m, mn);
-        lsum *= al;
-#pragma unroll
-        for (int i = 0; i < NT; ++i) acc[i] *= al;
-      }
-      m = mn;
+    };
+
+    // ---- weights against the fixed reference, O^T += V^T P^T -------------------
+    float mref, lsum, smax;  // for head n16 (the same in every lane group)
+    f32x4 acc[NT];
+    auto accumulate = [&](const Raw& R, const float* s, const bool* ok) {
       float pr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pr[r] = exp2_rel(s[r], m);
+        smax = fmaxf(smax, s[r]);
+        pr[r] = __builtin_amdgcn_exp2f(s[r] - mref);  // 0 for a -inf score
         lsum += pr[r];
       }
       const u32x2 pt = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
-      // ---- O^T += V^T P^T -----------------------------------------------------
       // tokens past the item end or on a masked page: codes and scale zeroed
       // (their probability is 0, but the slot may hold NaN codes)
+      // (masks, not branches, so the page's work stays one scheduling region)
+      uint32_t keep[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) keep[r] = ok[r] ? 0xffffffffu : 0u;
       if constexpr (QT == QT_BF16) {
         uint32_t w[4][VDW];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int k = 0; k < VDW; ++k) w[r][k] = ok[r] ? R.v[r][k] : 0u;
+          for (int k = 0; k < VDW; ++k) w[r][k] = R.v[r][k] & keep[r];
 #pragma unroll
         for (int k = 0; k < VDW; ++k) {  // dword k holds dv 2k, 2k+1
           const u32x2 e0 = u32x2{__builtin_amdgcn_perm(w[1][k], w[0][k], 0x05040100u),
@@ -311,9 +335,9 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
         uint32_t w[4][VDW];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          sv[r] = ok[r] ? f16_bits_to_f32((uint16_t)(R.vs[r] >> vshift)) : 0.0f;
+          sv[r] = f16_bits_to_f32((uint16_t)((R.vs[r] >> vshift) & keep[r]));
 #pragma unroll
-          for (int k = 0; k < VDW; ++k) w[r][k] = ok[r] ? R.v[r][k] : 0u;
+          for (int k = 0; k < VDW; ++k) w[r][k] = R.v[r][k] & keep[r];
         }
 #pragma unroll
         for (int k = 0; k < VDW; ++k) {  // dword k holds dv 4k .. 4k+3 of each token
@@ -332,19 +356,47 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
       }
     };
 
-    // ---- stream this wave's pages, NBUF - 1 pages' loads in flight ---------------
+    // ---- stream this wave's pages, NBUF pages' loads in flight ---------------------
+    // The softmax reference of head n16 stays fixed over the pass: the largest
+    // score of the wave's first page (0 when it has none).  Weights 2^(s -
+    // mref) then need no running-max update, no cross-lane reduction and no
+    // rescaling of the accumulators.  A pass whose largest score ends up more
+    // than 2^64 away from the reference (the weights could overflow, or every
+    // weight underflow) is streamed again with that score as the reference.
     Raw R[NBUF];
+    float M;  // largest score of head n16 over the wave's pages
+    for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int k = 0; k < NBUF - 1; ++k)
-      if (k < nsteps) load_page(pid_of(k), R[k]);
-    for (int st = 0; st < nsteps; st += NBUF) {
-#pragma unroll
-      for (int k = 0; k < NBUF; ++k) {
-        const int sn = st + k + NBUF - 1;
-        if (sn < nsteps) load_page(pid_of(sn), R[(k + NBUF - 1) % NBUF]);
-        if (st + k < nsteps) compute(st + k, pid_of(st + k), R[k]);
+      for (int k = 0; k < NBUF; ++k) load_page(pid_of(k), R[k]);
+      if (pass == 0) {
+        float s0[4];
+        bool ok0[4];
+        scores(0, pid_of(0), R[0], s0, ok0);
+        float t = fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3]));
+        t = max_xor32(max_xor16(t));
+        mref = (t == -INFINITY) ? 0.0f : t;
       }
+      lsum = 0.0f;
+      smax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int st = 0; st < nst; st += NBUF) {
+#pragma unroll
+        for (int k = 0; k < NBUF; ++k) {
+          float s[4];
+          bool ok[4];
+          scores(st + k, pid_of(st + k), R[k], s, ok);
+          accumulate(R[k], s, ok);
+          load_page(pid_of(st + k + NBUF), R[k]);
+        }
+      }
+      M = max_xor32(max_xor16(smax));
+      const bool redo = M != -INFINITY && (M > mref + 64.0f || M < mref - 64.0f);
+      if (!__builtin_amdgcn_ballot_w64(redo)) break;
+      mref = (M == -INFINITY) ? 0.0f : M;
     }
+    // a head with no valid token here contributes nothing to the merges
+    const float m = (M == -INFINITY) ? -INFINITY : mref;
 
     // ---- merge the four waves ---------------------------------------------------------
     lsum = sum_xor32(sum_xor16(lsum));
