@@ -28,6 +28,15 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  The separate-K/V matrix-core kernel keeps its MFMA
+# accumulators in ordinary VGPRs: it then needs no AGPR copies and fits two
+# (head_dim 256) or three (head_dim 128) waves per SIMD.  The MLA kernel, whose
+# output accumulator fills the AGPR file, keeps the default.
+EXTRA_FLAGS = {
+    "kvq_gqa_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -37,7 +46,8 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -83,6 +83,10 @@ struct MfGeo {
   static constexpr int NKS = D / 32;              // QK k-steps = scale blocks per row
   static constexpr int NT = D / 16;               // PV row tiles
   static constexpr int KDW = 2 * ESZ;             // dwords of a lane's 8 K elements
+  // 8-bit codes: a lane loads 16 contiguous codes of its token per 64 elements
+  // (one 16-byte load), and a cross-half lane swap hands every lane group
+  // its 8 codes of each 32-element block; bf16: one 16-byte load per block
+  static constexpr int KLD = (ESZ == 1) ? D / 64 : NKS;  // K loads per lane per page
   static constexpr int VDW = (D / 16) * ESZ / 4;  // dwords of a lane's V slice per token
   static constexpr int CODE = kPageSize * D * ESZ;
   static constexpr int SCL = (QT == QT_BF16) ? 4 : kPageSize * NKS * 2;
@@ -91,7 +95,7 @@ struct MfGeo {
 template <int QT, int D>
 struct PageRaw {
   using G = MfGeo<QT, D>;
-  uint32_t k[G::NKS][G::KDW];
+  uint32_t k[G::KLD][4];
   uint32_t v[4][G::VDW];
   // K scales of tokens 4g .. 4g+3 (8 NKS bytes): dword j of them in lane
   // (j, g), fetched by the lanes of the row with a DPP row broadcast
@@ -131,12 +135,12 @@ __device__ __forceinline__ void transpose4x4(const uint32_t* in, uint32_t* out) 
 template <int QT, int D>
 __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   using Gm = MfGeo<QT, D>;
-  constexpr int ESZ = Gm::ESZ, NKS = Gm::NKS, NT = Gm::NT, KDW = Gm::KDW, VDW = Gm::VDW;
+  constexpr int ESZ = Gm::ESZ, NKS = Gm::NKS, NT = Gm::NT, VDW = Gm::VDW, KLD = Gm::KLD;
   constexpr int CODE = Gm::CODE, SCL = Gm::SCL;
   using Raw = PageRaw<QT, D>;
   // page buffers per wave: NBUF pages' loads in flight while one is computed
-  // (at head_dim 256 one wave per SIMD fits, so it keeps more)
-  constexpr int NBUF = (D >= 256) ? 4 : 2;
+  // (two, so that two waves fit each SIMD at head_dim 256)
+  constexpr int NBUF = 2;
   extern __shared__ int s_prefix[];  // [batch + 1]
   // per-wave (m, l) and O^T accumulators at the end of an item, or the merge's
   // chunk weights
@@ -167,7 +171,9 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   }
 
   // per-lane offsets inside a (page, kv head) chunk
-  const uint32_t koff = (uint32_t)((n16 * D + 8 * g) * ESZ);                  // + 32 ks ESZ
+  // K: token n16, elements 64 m + 16 g .. +15 (8-bit, + 64 m) or 32 ks + 8 g
+  // .. +7 (bf16, + 64 ks bytes)
+  const uint32_t koff = (uint32_t)(ESZ == 1 ? n16 * D + 16 * g : (n16 * D + 8 * g) * 2);
   const uint32_t voff = (uint32_t)((4 * g * D + (D / 16) * n16) * ESZ);       // + r D ESZ
   const uint32_t ksoff = (uint32_t)(8 * NKS * g + 4 * min(n16, 2 * NKS - 1));
   const int vblk = n16 * D / 512;                                             // V scale block
@@ -215,7 +221,10 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     u32x4 qb[NKS];
     {
       const bool real = n16 < GT;
-      const uint16_t* qrow = a.q + ((int64_t)b * a.n_q_heads + h0 + (real ? n16 : 0)) * D + 8 * g;
+      // the elements of block ks that lane group g holds in the K operand:
+      // 32 ks + 8 g (bf16), or after the 8-bit lane swap 32 ks + (0, 16, 8, 24)[g]
+      const int goff = (ESZ == 1) ? 16 * (g & 1) + 8 * (g >> 1) : 8 * g;
+      const uint16_t* qrow = a.q + ((int64_t)b * a.n_q_heads + h0 + (real ? n16 : 0)) * D + goff;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
@@ -237,7 +246,7 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
       const auto rk = page_rsrc(a.k_pool + row0 * D * ESZ, code_bytes);
       const auto rv = page_rsrc(a.v_pool + row0 * D * ESZ, code_bytes);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) bload<KDW, kNonTemporal>(rk, koff + 32 * ks * ESZ, R.k[ks]);
+      for (int m = 0; m < KLD; ++m) bload<4, kNonTemporal>(rk, koff + 64 * m, R.k[m]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) bload<VDW, kNonTemporal>(rv, voff + r * D * ESZ, R.v[r]);
       if constexpr (QT != QT_BF16) {
@@ -270,9 +279,17 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
           f32x4 Sk[GS];
 #pragma unroll
           for (int k = 0; k < GS; ++k) {
+            // block ks = 2m + j: lanes 0-31 hold 16 codes of block 2m, lanes
+            // 32-63 of block 2m + 1; a swap of the upper half of one dword
+            // pair with the lower half of the other gives every lane group 8
+            // codes of each block (elements 32 ks + (0, 16, 8, 24)[g] ..)
+            const int ks = k0 + k, m = ks >> 1;
+            const auto x0 = __builtin_amdgcn_permlane32_swap(R.k[m][0], R.k[m][2], false, false);
+            const auto x1 = __builtin_amdgcn_permlane32_swap(R.k[m][1], R.k[m][3], false, false);
+            const uint32_t c0 = (ks & 1) ? x0[1] : x0[0], c1 = (ks & 1) ? x1[1] : x1[0];
             uint32_t kb[4];
-            decode_dword_bf16x2<QT>(R.k[k0 + k][0], kb);
-            decode_dword_bf16x2<QT>(R.k[k0 + k][1], kb + 2);
+            decode_dword_bf16x2<QT>(c0, kb);
+            decode_dword_bf16x2<QT>(c1, kb + 2);
             Sk[k] = mfma_k32(u32x4{kb[0], kb[1], kb[2], kb[3]}, qb[k0 + k], f32x4{0.f, 0.f, 0.f, 0.f});
           }
 #pragma unroll
