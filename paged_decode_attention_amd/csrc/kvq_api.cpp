@@ -147,26 +147,39 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
     else
       p.gt = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     p.n_hg = G / p.gt;
-    const int64_t units = (int64_t)batch * n_kv_heads * p.n_hg;
-    // Item length: about 2 work items per CU over the upper-bound context,
-    // a whole step of pages per wave, at most kMaxItemPages, and few enough
-    // chunks per sequence for the merge's weights to fit in LDS.
+    const int64_t seq_units = (int64_t)n_kv_heads * p.n_hg;  // (kv head, head group) pairs
+    const int64_t units = (int64_t)batch * seq_units;
+    // Work items are sized on the device from the actual lengths (about
+    // `target` of them over the batch, one per resident workgroup); here only
+    // the bounds: whole steps of pages per wave, at most kMaxItemPages, and
+    // few enough chunks per sequence for the merge's weights to fit in LDS.
     const int step = kDecodeWaves * (p.mfma ? 1 : gqa_pages_per_step(qtype, head_dim_qk) * kGqaDepth);
     const int64_t target = 2 * (int64_t)kPlanCUs;
-    int64_t want = ((int64_t)max_pages * units + target - 1) / target;
+    const int cap = kMaxItemPages / step * step;
     const int64_t for_merge = ((int64_t)max_pages * p.gt + kMergeMaxWeights - 1) / kMergeMaxWeights;
-    if (want < for_merge) want = for_merge;
-    if (want < step) want = step;
-    want = (want + step - 1) / step * step;
-    const int cap = kMaxItemPages * kDecodeWaves / 4 / step * step;
-    if (for_merge > cap) return no("max_pages %d is too large for the split-K merge", max_pages);
-    p.item_pages = (int)(want < cap ? want : cap);
-    const int64_t chunks = (max_pages + p.item_pages - 1) / p.item_pages;
+    const int64_t min_pages = ((for_merge > step ? for_merge : step) + step - 1) / step * step;
+    if (min_pages > cap) return no("max_pages %d is too large for the split-K merge", max_pages);
+    p.step = step;
+    p.min_pages = (int)min_pages;
+    p.cap_pages = cap;
+    p.target = (int)target;
+    p.item_pages = (int)min_pages;
+    // items: at most work / item_pages + one partial item per (sequence, unit);
+    // item_pages >= work / target unless capped, and >= min_pages always
+    const int64_t by_min = units * ((max_pages + min_pages - 1) / min_pages);
+    int64_t by_target = ((int64_t)batch * max_pages * seq_units + cap - 1) / cap;
+    if (by_target < target) by_target = target;
+    by_target += units;
+    p.max_items = by_min < by_target ? by_min : by_target;
+    // chunks of one sequence: at most max_pages / min_pages, and at most
+    // about target / seq_units unless the item size is capped
+    int64_t chunks = (max_pages + cap - 1) / cap;
+    if (chunks < target / seq_units + 1) chunks = target / seq_units + 1;
+    if (chunks > (max_pages + min_pages - 1) / min_pages) chunks = (max_pages + min_pages - 1) / min_pages;
     // the last workgroup merges a sequence's partials itself while they are
     // small; beyond that a merge kernel spreads the reads over the GPU
     p.fused_merge = head_dim_v < 64 ||
                     chunks * p.gt * head_dim_v * (int64_t)sizeof(float) <= kFusedMergeMaxBytes;
-    p.max_items = units * chunks;
   } else {
     return no("head_dim %d/%d is not supported (separate K/V: 32, 64, 128 or 256 with equal "
               "K and V widths; shared slab: 576/512 with one kv head)",

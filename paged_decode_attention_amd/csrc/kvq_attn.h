@@ -129,6 +129,41 @@ __device__ void build_prefix(const DecodeArgs& a, int item_tokens, int units, in
   __syncthreads();
 }
 
+// How the GQA kernels size their work items (see DecodePlan).
+struct ItemRule {
+  int step, min_pages, cap_pages, target;
+};
+
+// Pages per work item from the batch's actual lengths, the same in every
+// workgroup: about r.target items over all (sequence, unit) pairs, a
+// multiple of r.step, within [r.min_pages, r.cap_pages]; then the exclusive
+// scan of per-sequence item counts into s_prefix.  Returns tokens per item.
+template <int kThreads>
+__device__ int plan_items(const DecodeArgs& a, const ItemRule& r, int units, int* s_prefix,
+                          int* s_wave) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = a.batch;
+  const int per = (B + kThreads - 1) / kThreads;
+  const int b0 = tid * per, b1 = min(b0 + per, B);
+  int pages = 0;
+  for (int b = b0; b < b1; ++b) pages += (clamped_len(a, b) + kPageSize - 1) / kPageSize;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) pages += __shfl_xor(pages, off, 64);
+  if (lane == 0) s_wave[wave] = pages;
+  __syncthreads();
+  int64_t total = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) total += s_wave[w];
+  __syncthreads();  // s_wave is reused by the scan
+  const int64_t work = total * units;
+  int64_t ip = (work + r.target - 1) / r.target;
+  ip = (ip + r.step - 1) / r.step * r.step;
+  ip = ip < r.min_pages ? r.min_pages : (ip > r.cap_pages ? r.cap_pages : ip);
+  const int item_tokens = (int)ip * kPageSize;
+  build_prefix<kThreads>(a, item_tokens, units, s_prefix, s_wave);
+  return item_tokens;
+}
+
 // exp2(x - m) that is 0 (not NaN) when both are -inf.  The raw hardware
 // exp2 is enough here: arguments are <= 0 and tiny results may flush to 0.
 __device__ __forceinline__ float exp2_rel(float x, float m) {

@@ -60,7 +60,8 @@ struct Geo {
 
 struct GqaParams {
   DecodeArgs a;
-  int gt, n_hg, item_tokens;
+  int gt, n_hg;
+  ItemRule rule;     // work item size (see plan_items)
   int fused;         // merge split-K partials in the last workgroup (else a merge kernel)
   float scale_log2;  // sm_scale * log2(e)
   int* prefix;       // [batch + 1] items before each sequence (written by block 0)
@@ -113,8 +114,8 @@ struct Item {
 };
 
 template <int PPS, int GT>
-__device__ __forceinline__ Item describe(const GqaParams& p, const int* s_prefix, int item,
-                                         int wave, int units, int G) {
+__device__ __forceinline__ Item describe(const GqaParams& p, int item_tokens, const int* s_prefix,
+                                         int item, int wave, int units, int G) {
   const DecodeArgs& a = p.a;
   Item it;
   it.item = item;
@@ -130,9 +131,9 @@ __device__ __forceinline__ Item describe(const GqaParams& p, const int* s_prefix
   it.kvh = it.u / p.n_hg;
   const int hg = it.u - it.kvh * p.n_hg;
   const int L = clamped_len(a, it.b);
-  it.nc = (L + p.item_tokens - 1) / p.item_tokens;
-  it.t0 = chunk * p.item_tokens;
-  it.nt = min(p.item_tokens, L - it.t0);
+  it.nc = (L + item_tokens - 1) / item_tokens;
+  it.t0 = chunk * item_tokens;
+  it.nt = min(item_tokens, L - it.t0);
   it.np = (it.nt + kPageSize - 1) / kPageSize;
   it.h0 = it.kvh * G + hg * GT;
   const int ngroups = (it.np + PPS - 1) / PPS;
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
   const int units = a.n_kv_heads * p.n_hg;
   const int G = a.n_q_heads / a.n_kv_heads;
 
-  build_prefix<kThreads>(a, p.item_tokens, units, s_prefix, s_wave);
+  const int item_tokens = plan_items<kThreads>(a, p.rule, units, s_prefix, s_wave);
   const int total = s_prefix[a.batch];
   if (blockIdx.x == 0)
     for (int b = tid; b <= a.batch; b += kThreads) p.prefix[b] = s_prefix[b];
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
 
   Buf R[kDepth];
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const Item cur = describe<PPS, GT>(p, s_prefix, item, wave, units, G);
+    const Item cur = describe<PPS, GT>(p, item_tokens, s_prefix, item, wave, units, G);
     const int pid_cur = load_pids(cur);
     load_q(cur, qb);
     // Stream the item's steps, kDepth steps' loads in flight (cur.nsteps is
@@ -600,14 +601,16 @@ hipError_t launch_gqa_decode(const DecodeArgs& a, const DecodePlan& plan, int nu
   gp.a = a;
   gp.gt = plan.gt;
   gp.n_hg = plan.n_hg;
-  gp.item_tokens = plan.item_pages * kPageSize;
+  gp.rule = ItemRule{plan.step, plan.min_pages, plan.cap_pages, plan.target};
   gp.fused = plan.fused_merge ? 1 : 0;
   gp.scale_log2 = a.sm_scale * kLog2e;
   gp.prefix = reinterpret_cast<int*>(ws + plan.off_prefix);
   gp.count = reinterpret_cast<int*>(ws + plan.off_count);
   gp.part_ml = reinterpret_cast<float*>(ws + plan.off_ml);
   gp.part_acc = reinterpret_cast<float*>(ws + plan.off_acc);
-  int64_t grid = (int64_t)num_cus * 4;
+  // about one work item per workgroup when the batch is short; a persistent
+  // grid strides over the rest
+  int64_t grid = plan.target;
   if (grid > plan.max_items) grid = plan.max_items;
   if (grid < 1) grid = 1;
   hipError_t e;

@@ -68,7 +68,8 @@ __device__ __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
 
 struct MfParams {
   DecodeArgs a;
-  int gt, n_hg, item_tokens;
+  int gt, n_hg;
+  ItemRule rule;     // work item size (see plan_items)
   int fused;         // merge split-K partials in the last workgroup (else a merge kernel)
   float scale_log2;  // sm_scale * log2(e)
   int* prefix;       // [batch + 1]
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   const int units = a.n_kv_heads * p.n_hg;
   const int G = a.n_q_heads / a.n_kv_heads;
 
-  build_prefix<kT>(a, p.item_tokens, units, s_prefix, s_wave);
+  const int item_tokens = plan_items<kT>(a, p.rule, units, s_prefix, s_wave);
   const int total = s_prefix[a.batch];
   if (blockIdx.x == 0)
     for (int b = tid; b <= a.batch; b += kT) p.prefix[b] = s_prefix[b];
@@ -193,9 +194,9 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     const int chunk = rem / units, u = rem - chunk * units;
     const int kvh = u / p.n_hg, hg = u - kvh * p.n_hg;
     const int L = clamped_len(a, b);
-    const int nc = (L + p.item_tokens - 1) / p.item_tokens;
-    const int t0 = chunk * p.item_tokens;
-    const int nt = min(p.item_tokens, L - t0);
+    const int nc = (L + item_tokens - 1) / item_tokens;
+    const int t0 = chunk * item_tokens;
+    const int nt = min(item_tokens, L - t0);
     const int np = (nt + kPageSize - 1) / kPageSize;
     const int h0 = kvh * G + hg * GT;
     const int nsteps = (np > wave) ? (np - wave + kW - 1) / kW : 0;  // pages of this wave
@@ -548,14 +549,14 @@ hipError_t launch_gqa_mfma_decode(const DecodeArgs& a, const DecodePlan& plan, i
   mp.a = a;
   mp.gt = plan.gt;
   mp.n_hg = plan.n_hg;
-  mp.item_tokens = plan.item_pages * kPageSize;
+  mp.rule = ItemRule{plan.step, plan.min_pages, plan.cap_pages, plan.target};
   mp.fused = plan.fused_merge ? 1 : 0;
   mp.scale_log2 = a.sm_scale * kLog2e;
   mp.prefix = reinterpret_cast<int*>(ws + plan.off_prefix);
   mp.count = reinterpret_cast<int*>(ws + plan.off_count);
   mp.part_ml = reinterpret_cast<float*>(ws + plan.off_ml);
   mp.part_acc = reinterpret_cast<float*>(ws + plan.off_acc);
-  int64_t grid = (int64_t)num_cus * 2;
+  int64_t grid = plan.target;
   if (grid > plan.max_items) grid = plan.max_items;
   if (grid < 1) grid = 1;
   hipError_t e;

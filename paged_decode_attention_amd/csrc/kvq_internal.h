@@ -89,7 +89,11 @@ struct DecodePlan {
   int kind;
   int gt;             // query heads per work item
   int n_hg;           // head groups per kv head (G / gt)
-  int item_pages;     // pages per split-K work item
+  int item_pages;     // pages per split-K work item (the MLA slab; GQA: the smallest)
+  // GQA: the kernels size work items from the actual lengths, about `target`
+  // items over the batch: ceil(pages x units / target), rounded up to a
+  // multiple of `step`, within [min_pages, cap_pages]
+  int step, min_pages, cap_pages, target;
   bool fused_merge;   // merge inside the split kernel (else a merge kernel)
   bool mfma;          // GQA: wide query groups on the matrix-core kernel
   int64_t max_items;  // upper bound on work items (sizes the workspace)

@@ -9,8 +9,9 @@
 // (log2-domain running max and sum) and acc_c[h][d] (fp32, unnormalized).
 // With M = max_c m_c and w_c = 2^(m_c - M):
 //   out[h][d] = sum_c w_c acc_c[h][d] / sum_c w_c l_c,  lse = (M + log2 sum_c w_c l_c) ln 2.
-// Block = (b, u, head, 64 columns); 16 groups of 16 threads take every 16th
-// chunk, a thread 4 columns, four chunk rows in flight.  The decode kernels
+// Block = (b, u, head, 16 columns); 64 groups of 4 threads take every 64th
+// chunk, a thread 4 columns; the first chunk rows are loaded while the
+// weights are formed.  The decode kernels
 // merge in their last workgroup instead when the partials of a sequence are
 // few (see plan_decode).
 #include "kvq_attn.h"
@@ -20,9 +21,11 @@
 namespace kvq {
 namespace {
 
-constexpr int kGroups = 16;
-constexpr int kCols = 64;
-constexpr int kThreads = kGroups * (kCols / 4);
+constexpr int kCols = 16;                // columns per block
+constexpr int kLanesPerRow = kCols / 4;  // a thread takes 4 columns
+constexpr int kThreads = 256;
+constexpr int kGroups = kThreads / kLanesPerRow;  // chunk rows in flight per block
+constexpr int kAhead = 4;                // chunk rows per thread loaded before the weights
 
 struct MergeParams {
   DecodeArgs a;
@@ -45,12 +48,23 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_kernel(MergeParams p) {
   if (nc <= 1) return;  // written by the decode kernel itself
   const int first = p.prefix[b] + u;  // item of chunk c: first + c * units
   __shared__ float s_w[kMergeMaxWeights];
-  __shared__ __attribute__((aligned(16))) f32x4 s_red[kGroups][kCols / 4];
+  __shared__ __attribute__((aligned(16))) f32x4 s_red[kGroups][kLanesPerRow];
   __shared__ float s_L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int G = a.n_q_heads / a.n_kv_heads;
   const int kvh = u / p.n_hg, hg = u - kvh * p.n_hg;
   const int64_t orow = (int64_t)b * a.n_q_heads + kvh * G + hg * p.gt + h;
+  const int grp = tid / kLanesPerRow, j = tid % kLanesPerRow;
+  const float* src = p.part_acc + ((int64_t)first * p.gt + h) * p.D + dchunk * kCols + 4 * j;
+  const int64_t cstride = (int64_t)p.units * p.gt * p.D;
+  // the first rows' partial sums are in flight while wave 0 forms the weights
+  f32x4 xs[kAhead];
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) {
+    const int c = grp + k * kGroups;
+    xs[k] = c < nc ? *reinterpret_cast<const f32x4*>(src + (int64_t)c * cstride)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   if (tid < 64) {
     float M = -INFINITY;
     for (int c = lane; c < nc; c += 64)
@@ -71,26 +85,22 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_kernel(MergeParams p) {
     }
   }
   __syncthreads();
-  const int grp = tid / (kCols / 4), j = tid % (kCols / 4);
-  const int d = dchunk * kCols + 4 * j;
-  const float* src = p.part_acc + ((int64_t)first * p.gt + h) * p.D + d;
-  const int64_t cstride = (int64_t)p.units * p.gt * p.D;
   f32x4 v = {0.f, 0.f, 0.f, 0.f};
-  int c = grp;
-  for (; c + 3 * kGroups < nc; c += 4 * kGroups) {
-    f32x4 xs[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) xs[k] = *reinterpret_cast<const f32x4*>(src + (int64_t)(c + k * kGroups) * cstride);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) v += s_w[c + k * kGroups] * xs[k];
+  for (int k = 0; k < kAhead; ++k) {
+    const int c = grp + k * kGroups;
+    if (c < nc) v += s_w[c] * xs[k];
   }
-  for (; c < nc; c += kGroups) v += s_w[c] * *reinterpret_cast<const f32x4*>(src + (int64_t)c * cstride);
+  for (int c = grp + kAhead * kGroups; c < nc; c += kGroups)
+    v += s_w[c] * *reinterpret_cast<const f32x4*>(src + (int64_t)c * cstride);
   s_red[grp][j] = v;
   __syncthreads();
-  if (tid < kCols / 4) {
-    f32x4 t = s_red[0][tid];
-#pragma unroll
-    for (int k = 1; k < kGroups; ++k) t += s_red[k][tid];
+  for (int half = kGroups / 2; half >= 1; half >>= 1) {
+    if (grp < half) s_red[grp][j] += s_red[grp + half][j];
+    __syncthreads();
+  }
+  if (tid < kLanesPerRow) {
+    const f32x4 t = s_red[0][tid];
     const float Ls = s_L;
     const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
     uint16_t* o = a.out + orow * p.D + dchunk * kCols + 4 * tid;
