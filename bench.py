@@ -14,8 +14,15 @@ Prints one JSON line: `value` is the step's algorithmic bytes (codes + scales
 of every token read, Q, O, page-table entries, and the store's bf16 reads and
 code/scale writes) per second, in GB/s; `roofline` is the decode call (one
 kernel launch: split-K decode with its in-kernel merge) against the 8 TB/s HBM
-peak, timed with HIP events on the stream the kernels run on; `cpu_baseline`
-is the CPU oracle on one layer of the same workload, timed on this host.
+peak, timed with HIP events on the stream the kernels run on; `store_gbps` is
+the quantize-on-store at the mixed workload's size (8192 new tokens x 8 kv
+heads x 128, K and V in one call); `cpu_baseline` is the CPU oracle on a
+bounded sample of the same workload (repeated layer decodes for about 10 s),
+timed on this host.
+
+Other modes: `--workload ragged256|single256|mla|mixed` times kvq_paged_decode
+alone on that workload and prints its own line; `--only decode|copy` and
+`--traffic-from DIR` serve the rocprofv3 counter passes (see profiles/).
 """
 from __future__ import annotations
 
@@ -64,14 +71,77 @@ def recorded_traffic():
     return rec["traffic_bytes_per_launch"]
 
 
+def _counter_means(path, name_re):
+    """Per-dispatch sums of each counter (all instances) in a rocprofv3
+    counter_collection.csv, averaged over the dispatches whose kernel name
+    matches name_re."""
+    import csv
+    import re
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if not re.search(name_re, r["Kernel_Name"]):
+                continue
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (d, c), v in per.items():
+        out.setdefault(c, []).append(v)
+    return {c: sum(v) / len(v) for c, v in out.items()}
+
+
+def write_traffic(src_dir):
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, each over the
+    decode launches and over a plain 1 GiB copy) into TRAFFIC_FILE: HBM bytes
+    per decode launch, with the counters scaled by what they read for the copy
+    of known size, tagged with the kernel sources' hash."""
+    import hashlib
+    j = os.path.join
+    dec_f = _counter_means(j(src_dir, "decode_FETCH_SIZE", "run_counter_collection.csv"),
+                           "gqa_decode_kernel")["FETCH_SIZE"]
+    dec_w = _counter_means(j(src_dir, "decode_WRITE_SIZE", "run_counter_collection.csv"),
+                           "gqa_decode_kernel")["WRITE_SIZE"]
+    cp_f = _counter_means(j(src_dir, "copy_FETCH_SIZE", "run_counter_collection.csv"),
+                          "(?i)copy")["FETCH_SIZE"]
+    cp_w = _counter_means(j(src_dir, "copy_WRITE_SIZE", "run_counter_collection.csv"),
+                          "(?i)copy")["WRITE_SIZE"]
+    gib = float(1 << 30)
+    ff, fw = gib / (cp_f * 1024), gib / (cp_w * 1024)
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    rec = {
+        "kernel": "gqa_decode_kernel<fp8_e4m3, 128, 2>",
+        "workload": "qwen3_b8_ctx16384_h16x8_d128 (one layer's pool, batch 8 x 16384 tokens)",
+        "source_hash": h.hexdigest()[:16],
+        "fetch_size_kib": round(dec_f, 1),
+        "write_size_kib": round(dec_w, 1),
+        "copy_reference": {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                           "fetch_size_kib": round(cp_f, 1), "write_size_kib": round(cp_w, 1)},
+        "fetch_factor": round(ff, 4),
+        "write_factor": round(fw, 4),
+        "traffic_bytes_per_launch": int(round(dec_f * 1024 * ff + dec_w * 1024 * fw)),
+    }
+    with open(os.path.join(ROOT, TRAFFIC_FILE), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+    return 0
+
+
 def store_bytes(n_tokens, n_heads, head_dim, qtype, tensors=2):
     per = {"bf16": 2.0, "fp8_e4m3": 1 + 1 / 16, "q8_0": 1 + 1 / 16}[qtype]
     return int(tensors * n_tokens * n_heads * head_dim * (2 + per)) + 4 * n_tokens
 
 
+CPU_SAMPLE_S = 10.0  # seconds of oracle decode timed (at least one full layer)
+
+
 def cpu_baseline(wl, qtype, k_rows, v_rows, q_bits):
-    """The oracle, as it stands, on one layer of the workload: store every slot
-    of the pool, then decode all rows.  Reports the decode part in GB/s."""
+    """The oracle, as it stands, on the workload: store every slot of one
+    layer's pool, then decode all rows of that layer repeatedly (each pass is
+    one of the step's 28 layer decodes) until CPU_SAMPLE_S seconds have
+    passed.  Reports the decode part in GB/s over the same algorithmic bytes
+    as the GPU line."""
     import oracle
     from paged_decode_attention_amd import workloads as W
     threads = oracle.default_threads()
@@ -86,21 +156,26 @@ def cpu_baseline(wl, qtype, k_rows, v_rows, q_bits):
     oracle.store(qtype, k_rows, slots, H, D, W.PAGE, wl.num_pages, kp, ks, threads=threads)
     oracle.store(qtype, v_rows, slots, H, D, W.PAGE, wl.num_pages, vp, vs, threads=threads)
     t1 = time.perf_counter()
-    oracle.paged_decode(qtype, q_bits, kp, ks, vp, vs, wl.page_table, wl.seq_lens, H, D, D,
-                        W.PAGE, wl.num_pages, wl.sm_scale, threads=threads)
-    t2 = time.perf_counter()
-    dec_bytes = wl.algorithmic_bytes(qtype)
+    passes = 0
+    while True:
+        oracle.paged_decode(qtype, q_bits, kp, ks, vp, vs, wl.page_table, wl.seq_lens, H, D, D,
+                            W.PAGE, wl.num_pages, wl.sm_scale, threads=threads)
+        passes += 1
+        t2 = time.perf_counter()
+        if t2 - t1 >= CPU_SAMPLE_S:
+            break
+    dec_bytes = wl.algorithmic_bytes(qtype) * passes
     fill_bytes = store_bytes(wl.n_slots, H, D, qtype)
     return {
         "value": round(dec_bytes / (t2 - t1) / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": ("one of the 28 layers: decode of all %d sequences x %d heads over %d tokens "
-                   "each (%.3f s, %.1f MB algorithmic); the oracle's fill of that layer's pool "
-                   "took %.3f s (%.3f GB/s)" % (wl.batch, wl.n_q_heads, int(wl.seq_lens[0]),
-                                                t2 - t1, dec_bytes / 1e6, t1 - t0,
-                                                fill_bytes / (t1 - t0) / 1e9)),
+        "sample": ("%d layer decodes (of the step's 28) of all %d sequences x %d heads over "
+                   "%d tokens each: %.2f s, %.1f MB algorithmic; the oracle's fill of that "
+                   "layer's pool took %.3f s (%.3f GB/s)" % (
+                       passes, wl.batch, wl.n_q_heads, int(wl.seq_lens[0]), t2 - t1,
+                       dec_bytes / 1e6, t1 - t0, fill_bytes / (t1 - t0) / 1e9)),
     }
 
 
@@ -123,20 +198,27 @@ def decode_only(args, wl, qtype, dev) -> int:
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
             torch.bfloat16)
 
-    slots = torch.arange(wl.n_slots, dtype=torch.int32, device=dev)
-    d_k = dev_bf16(wl.kv_rows(0, 0, wl.n_slots))
-    d_v = None if wl.shared else dev_bf16(wl.kv_rows(1, 0, wl.n_slots))
     pools = []
     for _ in range(R):
         kp, ks = kvq.alloc_pool(qtype, wl.num_pages, H, D, device=dev)
         if wl.shared:
-            kvq.store(qtype, d_k, None, slots, kp, ks)
             pools.append((kp, ks, kp, ks))
         else:
             vp, vs = kvq.alloc_pool(qtype, wl.num_pages, H, D, device=dev)
-            kvq.store(qtype, d_k, d_v, slots, kp, ks, vp, vs)
             pools.append((kp, ks, vp, vs))
-    torch.cuda.synchronize()
+    # fill every slot of every replica, 2^17 slots at a time
+    step = 1 << 17
+    for lo in range(0, wl.n_slots, step):
+        hi = min(lo + step, wl.n_slots)
+        slots = torch.arange(lo, hi, dtype=torch.int32, device=dev)
+        d_k = dev_bf16(wl.kv_rows(0, lo, hi))
+        d_v = None if wl.shared else dev_bf16(wl.kv_rows(1, lo, hi))
+        for kp, ks, vp, vs in pools:
+            if wl.shared:
+                kvq.store(qtype, d_k, None, slots, kp, ks)
+            else:
+                kvq.store(qtype, d_k, d_v, slots, kp, ks, vp, vs)
+        torch.cuda.synchronize()
     del d_k, d_v, slots
     q = dev_bf16(wl.query())
     pt = torch.from_numpy(wl.page_table).to(dev)
@@ -204,15 +286,20 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="qwen3",
-                    choices=["qwen3", "ragged256", "single256", "mla"],
+                    choices=["qwen3", "ragged256", "single256", "mla", "mixed"],
                     help="qwen3 (default) is the decode step this benchmark reports; the others "
                          "time kvq_paged_decode alone on that workload and print their own line")
     ap.add_argument("--replicas", type=int, default=0,
                     help="pool copies swept by the decode-only workloads (0: enough for 1 GB)")
+    ap.add_argument("--traffic-from", default=None, metavar="DIR",
+                    help="write the decode kernel's HBM traffic record from rocprofv3 --pmc "
+                         "FETCH_SIZE / WRITE_SIZE runs under DIR (decode_* and copy_*) and exit")
     ap.add_argument("--only", choices=["decode", "copy"], default=None,
                     help="counter passes: run just the timed decode calls, or a plain "
                          "1 GiB device copy (the reference for scaling FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
+    if args.traffic_from:
+        return write_traffic(args.traffic_from)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU form (each GPU would "
@@ -339,6 +426,26 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / K
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    # (3) the store at the mixed workload's size: 8192 new tokens (the last 128
+    # of 64 sequences) x 8 kv heads x 128, K and V in one fused kvq_store into
+    # a 2^20-slot pool, timed alone with HIP events on its stream
+    mw = W.mixed()
+    new = dev_bf16(mw.new_rows())
+    mkp, mks = kvq.alloc_pool(qtype, mw.num_pages, H, D, device=dev)
+    mvp, mvs = kvq.alloc_pool(qtype, mw.num_pages, H, D, device=dev)
+    mslots = torch.from_numpy(mw.new_tokens["slots"]).to(dev)
+    big = kvq.PreparedStore(qtype, new[0], new[1], mslots, mkp, mks, mvp, mvs, stream=strm)
+    for _ in range(args.warmup):
+        big()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s0.record(strm)
+    for _ in range(K):
+        big()
+    s1.record(strm)
+    torch.cuda.synchronize()
+    big_us = s0.elapsed_time(s1) * 1e3 / K
+    big_bytes = store_bytes(int(mslots.numel()), H, D, qtype)
     achieved = dec_bytes / (dec_avg * 1e-3) / 1e9
     log("step %.3f ms (graph), decode call %.2f us, store call %.2f us" % (ms_step, dec_avg * 1e3,
                                                                            st_avg * 1e3))
@@ -372,7 +479,14 @@ def main() -> int:
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "decode_call_us": round(dec_avg * 1e3, 3),
         "store_call_us": round(st_avg * 1e3, 3),
-        "store_gbps": round(st_bytes / (st_avg * 1e-3) / 1e9, 3),
+        "store_gbps": round(big_bytes / (big_us * 1e-6) / 1e9, 2),
+        "store": {"workload": "8192 new tokens x 8 kv heads x 128, K and V in one call, into a "
+                              "2^20-slot pool (mixed_b64 new tokens: zero and constant blocks, "
+                              "+-1e4 outliers)",
+                  "call_us": round(big_us, 3), "bytes": big_bytes,
+                  "gbps": round(big_bytes / (big_us * 1e-6) / 1e9, 2),
+                  "pct_of_hbm_peak": round(100 * big_bytes / (big_us * 1e-6) / 1e9 / PEAK_GBPS, 2),
+                  "per_step_store_of_8_tokens_us": round(st_avg * 1e3, 3)},
         "roofline": {
             "bound": "hbm",
             "kernel": "gqa_decode_kernel<fp8_e4m3, 128, 2> (one launch per kvq_paged_decode)",
