@@ -10,8 +10,8 @@
 // With M = max_c m_c and w_c = 2^(m_c - M):
 //   out[h][d] = sum_c w_c acc_c[h][d] / sum_c w_c l_c,  lse = (M + log2 sum_c w_c l_c) ln 2.
 // Block = (b, u, head, 16 columns); 64 groups of 4 threads take every 64th
-// chunk, a thread 4 columns; the first chunk rows are loaded while the
-// weights are formed.  The decode kernels
+// chunk, a thread 4 columns; the first chunk rows and every chunk's (m, l)
+// are loaded at once, before the weights are formed.  The decode kernels
 // merge in their last workgroup instead when the partials of a sequence are
 // few (see plan_decode).
 #include "kvq_attn.h"
@@ -50,6 +50,7 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_kernel(MergeParams p) {
   __shared__ float s_w[kMergeMaxWeights];
   __shared__ __attribute__((aligned(16))) f32x4 s_red[kGroups][kLanesPerRow];
   __shared__ float s_L;
+  __shared__ float s_part[kThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int G = a.n_q_heads / a.n_kv_heads;
   const int kvh = u / p.n_hg, hg = u - kvh * p.n_hg;
@@ -65,24 +66,47 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_kernel(MergeParams p) {
     xs[k] = c < nc ? *reinterpret_cast<const f32x4*>(src + (int64_t)c * cstride)
                    : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  if (tid < 64) {
-    float M = -INFINITY;
-    for (int c = lane; c < nc; c += 64)
-      M = fmaxf(M, p.part_ml[((int64_t)(first + c * p.units) * p.gt + h) * 2]);
-    M = stride_max<1>(M);
-    float Ls = 0.0f;
-    for (int c = lane; c < nc; c += 64) {
-      const float* ml = p.part_ml + ((int64_t)(first + c * p.units) * p.gt + h) * 2;
-      const float w = exp2_rel(ml[0], M);
+  // every thread loads the (m, l) of its chunks once (in flight with the rows
+  // above); block reductions give M and the weighted sum of l
+  constexpr int kMl = (kMergeMaxWeights + kThreads - 1) / kThreads;
+  float mc[kMl], lc[kMl];
+#pragma unroll
+  for (int k = 0; k < kMl; ++k) {
+    const int c = tid + k * kThreads;
+    mc[k] = -INFINITY;
+    lc[k] = 0.0f;
+    if (c < nc) {
+      const float2 ml = *reinterpret_cast<const float2*>(
+          p.part_ml + ((int64_t)(first + c * p.units) * p.gt + h) * 2);
+      mc[k] = ml.x;
+      lc[k] = ml.y;
+    }
+  }
+  float M = mc[0];
+#pragma unroll
+  for (int k = 1; k < kMl; ++k) M = fmaxf(M, mc[k]);
+  M = stride_max<1>(M);
+  if (lane == 0) s_part[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_part[0], s_part[1]), fmaxf(s_part[2], s_part[3]));
+  float Ls = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kMl; ++k) {
+    const int c = tid + k * kThreads;
+    if (c < nc) {
+      const float w = exp2_rel(mc[k], M);
       s_w[c] = w;
-      Ls += w * ml[1];
+      Ls += w * lc[k];
     }
-    Ls = stride_sum<1>(Ls);
-    if (lane == 0) {
-      s_L = Ls;
-      if (a.lse && dchunk == 0)
-        a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
-    }
+  }
+  Ls = stride_sum<1>(Ls);
+  __syncthreads();  // every wave has read s_part
+  if (lane == 0) s_part[tid >> 6] = Ls;
+  __syncthreads();
+  if (tid == 0) {
+    Ls = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+    s_L = Ls;
+    if (a.lse && dchunk == 0) a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
   }
   __syncthreads();
   f32x4 v = {0.f, 0.f, 0.f, 0.f};

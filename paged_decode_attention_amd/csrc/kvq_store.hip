@@ -12,12 +12,22 @@
 // same (token, head, block) are handled by the same lane, so a thread keeps
 // two independent 16-byte loads in flight.
 //
-// Rounding: the quotient x / s is an IEEE fp32 division (correctly rounded,
-// as hipcc emits by default), and the code is the round-to-nearest-even e4m3
-// value of the clamped quotient from the hardware packed conversion, or the
-// half-away-from-zero integer for q8_0.  This is the store the review comment
-// on [PR103] asks for; a truncating intermediate fp16 step (the bug it
-// describes) is never taken.
+// Rounding: the code is the round-to-nearest-even e4m3 value (hardware packed
+// conversion) or the half-away-from-zero integer (q8_0) of the clamped
+// quotient x / s, where the quotient is the correctly rounded fp32 one.  This
+// is the store the review comment on [PR103] asks for; a truncating
+// intermediate fp16 step (the bug it describes) is never taken.
+//
+// The quotient is formed as q0 = x * rcp(s) followed by one residual
+// correction, q = q0 + fma(-s, q0, x) * rcp(s), instead of the full IEEE
+// division sequence.  That gives the same codes: x has an 8-bit and s an
+// 11-bit significand, so x / s is either exactly a rounding midpoint of the
+// code grid (a value with at most 5 significant bits, which the corrected
+// quotient reproduces exactly) or lies at least 2^-18 (relative) away from
+// every midpoint, far more than the corrected quotient's error of one fp32
+// ulp; the clamp to +-M is monotone, and the sign is taken from x (so -0
+// stays -0).  Every (block max, element) pair of bf16 values is checked
+// against the oracle's division on the GPU.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -40,10 +50,14 @@ __device__ __forceinline__ void quantize8(const float* x, float s, uint32_t* out
     out2[1] = 0u;
     return;
   }
+  const float r = __builtin_amdgcn_rcpf(s);  // s is a normal fp32 value (an fp16 scale)
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float q = x[i] / s;  // IEEE fp32 division by the stored fp16 scale
+    const float q0 = x[i] * r;
+    // x / s (see the header); the sign is x's (s > 0), also for a -0 element,
+    // which the correction step alone would turn into +0
+    const float q = copysignf(fmaf(fmaf(-s, q0, x[i]), r, q0), x[i]);
     v[i] = fminf(fmaxf(q, -M), M);
   }
   if constexpr (QT == QT_FP8) {
@@ -89,11 +103,16 @@ __global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs a, StoreGrid 
   const int64_t off = valid ? slot - page * a.page_size : 0;
   const int64_t row = (page * a.n_heads + h) * a.page_size + off;
 
+  // the source rows exist for every token: both loads are issued at once,
+  // without waiting for the slot
+  uint4 raws[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    raws[t] = a.src[t] ? *reinterpret_cast<const uint4*>(a.src[t] + src_off) : make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     if (a.src[t] == nullptr) continue;  // uniform: V absent
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (valid) raw = *reinterpret_cast<const uint4*>(a.src[t] + src_off);
+    const uint4 raw = raws[t];
     if constexpr (QT == QT_BF16) {
       if (valid)
         *reinterpret_cast<uint4*>(a.pool[t] + (row * a.head_dim + blk * 32 + quarter * 8) * 2) = raw;
