@@ -134,6 +134,16 @@ struct ItemRule {
   int step, min_pages, cap_pages, target;
 };
 
+// Tokens per work item under rule r for a batch holding `pages` pages in
+// all, `units` items per chunk of a sequence.
+__device__ __forceinline__ int rule_item_tokens(const ItemRule& r, int64_t pages, int units) {
+  const int64_t work = pages * units;
+  int64_t ip = (work + r.target - 1) / r.target;
+  ip = (ip + r.step - 1) / r.step * r.step;
+  ip = ip < r.min_pages ? r.min_pages : (ip > r.cap_pages ? r.cap_pages : ip);
+  return (int)ip * kPageSize;
+}
+
 // Pages per work item from the batch's actual lengths, the same in every
 // workgroup: about r.target items over all (sequence, unit) pairs, a
 // multiple of r.step, within [r.min_pages, r.cap_pages]; then the exclusive
@@ -155,13 +165,47 @@ __device__ int plan_items(const DecodeArgs& a, const ItemRule& r, int units, int
 #pragma unroll
   for (int w = 0; w < kThreads / 64; ++w) total += s_wave[w];
   __syncthreads();  // s_wave is reused by the scan
-  const int64_t work = total * units;
-  int64_t ip = (work + r.target - 1) / r.target;
-  ip = (ip + r.step - 1) / r.step * r.step;
-  ip = ip < r.min_pages ? r.min_pages : (ip > r.cap_pages ? r.cap_pages : ip);
-  const int item_tokens = (int)ip * kPageSize;
+  const int item_tokens = rule_item_tokens(r, total, units);
   build_prefix<kThreads>(a, item_tokens, units, s_prefix, s_wave);
   return item_tokens;
+}
+
+// Inclusive prefix sum over the 64 lanes: DPP shifts inside each row of 16
+// (lanes shifted in from outside the row read 0), then the totals of the
+// rows below are added from scalar reads of their last lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// The work list of a batch of at most 64 sequences, built by one wave alone
+// (every wave builds the same one; no LDS, no barrier): lane b < batch gets
+// the number of items before sequence b, and *total the number of items.
+// Same rule as plan_items.  `len` is clamped_len(a, lane) for lane < batch,
+// else 0 (loaded by the caller, which may issue other loads after it).
+__device__ __forceinline__ int plan_items_wave(const ItemRule& r, int units, int len, int* pfx,
+                                               int* total) {
+  const int pages = (len + kPageSize - 1) / kPageSize;
+  const int all_pages = __builtin_amdgcn_readlane(wave_incl_scan(pages), 63);
+  const int item_tokens = rule_item_tokens(r, all_pages, units);
+  const int items = (len + item_tokens - 1) / item_tokens * units;
+  const int incl = wave_incl_scan(items);
+  *pfx = incl - items;
+  *total = __builtin_amdgcn_readlane(incl, 63);
+  return item_tokens;
+}
+
+// Sequence of work item `item` in a list built by plan_items_wave: the last
+// b < batch with pfx(b) <= item (pfx is non-decreasing over the lanes).
+__device__ __forceinline__ int wave_item_seq(int pfx, int batch, int item) {
+  const uint64_t m = __builtin_amdgcn_ballot_w64((int)(threadIdx.x & 63) < batch && pfx <= item);
+  return __builtin_popcountll(m) - 1;
 }
 
 // exp2(x - m) that is 0 (not NaN) when both are -inf.  The raw hardware

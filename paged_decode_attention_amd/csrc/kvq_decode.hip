@@ -114,23 +114,15 @@ struct Item {
 };
 
 template <int PPS, int GT>
-__device__ __forceinline__ Item describe(const GqaParams& p, int item_tokens, const int* s_prefix,
-                                         int item, int wave, int units, int G) {
-  const DecodeArgs& a = p.a;
+__device__ __forceinline__ Item describe(const GqaParams& p, int item_tokens, int item, int b,
+                                         int rem, int L, int wave, int units, int G) {
   Item it;
   it.item = item;
-  int lo = 0, hi = a.batch - 1;
-  while (lo < hi) {  // largest b with s_prefix[b] <= item
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_prefix[mid] <= item) lo = mid; else hi = mid - 1;
-  }
-  it.b = lo;
-  const int rem = item - s_prefix[it.b];
+  it.b = b;
   const int chunk = rem / units;
   it.u = rem - chunk * units;
   it.kvh = it.u / p.n_hg;
   const int hg = it.u - it.kvh * p.n_hg;
-  const int L = clamped_len(a, it.b);
   it.nc = (L + item_tokens - 1) / item_tokens;
   it.t0 = chunk * item_tokens;
   it.nt = min(item_tokens, L - it.t0);
@@ -152,8 +144,8 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
   constexpr int PPS = Gm::PPS, ROWS = Gm::ROWS, NB = Gm::NB, ESZ = Gm::ESZ;
   constexpr int CODE = gqa_code_bytes(QT, D), SCL = gqa_scale_bytes(QT, D);
   // cross-wave partial sums [kWaves][GT][D] at the end of an item, or the
-  // merge's chunk weights [chunks][GT]
-  constexpr int kRed = (kWaves * GT * D > kMergeMaxWeights) ? kWaves * GT * D : kMergeMaxWeights;
+  // merge's chunk weights and sums [2][chunks][GT]
+  constexpr int kRed = (kWaves * GT * D > 2 * kMergeMaxWeights) ? kWaves * GT * D : 2 * kMergeMaxWeights;
   extern __shared__ int s_prefix[];  // [batch + 1]
   __shared__ float s_red[kRed];
   __shared__ float s_ml[kWaves][GT][2];
@@ -172,13 +164,84 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
   const int units = a.n_kv_heads * p.n_hg;
   const int G = a.n_q_heads / a.n_kv_heads;
 
-  const int item_tokens = plan_items<kThreads>(a, p.rule, units, s_prefix, s_wave);
-  const int total = s_prefix[a.batch];
-  if (blockIdx.x == 0)
-    for (int b = tid; b <= a.batch; b += kThreads) p.prefix[b] = s_prefix[b];
+  // page ids of the wave's pages of an item: lane s*PPS+k holds step s, page
+  // k (-1: masked or past the item).  The load is issued on every lane (the
+  // column clamped into the row), so it can be issued speculatively.
+  auto load_pids = [&](const Item& it) {
+    const int st = lane / PPS, k = lane - st * PPS;
+    const int pi = (wave + st * kWaves) * PPS + k;
+    const int col = min(it.t0 / kPageSize + pi, a.max_pages - 1);
+    // the lane condition is folded into the value through a mask the
+    // compiler cannot see into, so the load is not moved under it
+    int keep = (lane < it.nsteps * PPS && pi < it.np) ? 0 : -1;
+    asm volatile("" : "+v"(keep));
+    const int v = a.page_table[(int64_t)it.b * a.pt_stride + col] | keep;
+    return (v >= 0 && (int64_t)v < a.num_pages) ? v : -1;
+  };
+  // the query slice of this lane as bf16 pairs (exact; the softmax scale is
+  // applied to each score in fp32)
+  uint32_t qb[GT][EPL / 2];
+  auto load_q = [&](const Item& it) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      const uint16_t* qrow = a.q + ((int64_t)it.b * a.n_q_heads + it.h0 + h) * D + d0;
+#pragma unroll
+      for (int e = 0; e < EPL; e += 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(qrow + e);
+        qb[h][e / 2 + 0] = v.x;
+        qb[h][e / 2 + 1] = v.y;
+        qb[h][e / 2 + 2] = v.z;
+        qb[h][e / 2 + 3] = v.w;
+      }
+    }
+  };
+
+  // The work list.  Up to 64 sequences, every wave builds it alone (lane b
+  // holds the items before sequence b, and its length): one load, no LDS,
+  // no barrier.  Beside that load, the page ids and query of this
+  // workgroup's first item are loaded as if every sequence filled its
+  // page-table row; they are used when the actual list gives the same item
+  // (the loads are unconditional and in bounds either way).  Larger batches
+  // scan seq_lens in LDS.
+  const bool small = a.batch <= 64 && (int64_t)a.batch * a.max_pages < (1 << 30);
+  int item_tokens, total, wpfx = 0, wlen = 0, pid_spec = -1;
+  Item spec;
+  spec.b = -1;
+  if (small) {
+    const int raw_len = a.seq_lens[min(lane, a.batch - 1)];
+    const int full = a.max_pages * kPageSize;
+    const int g_tokens = rule_item_tokens(p.rule, (int64_t)a.batch * a.max_pages, units);
+    const int g_per_seq = (full + g_tokens - 1) / g_tokens * units;
+    const int g_item = min((int)blockIdx.x, a.batch * g_per_seq - 1);
+    const int g_b = g_item / g_per_seq;
+    spec = describe<PPS, GT>(p, g_tokens, g_item, g_b, g_item - g_b * g_per_seq, full, wave, units, G);
+    pid_spec = load_pids(spec);
+    load_q(spec);
+    // the length is first used here, after the speculative loads are issued
+    __builtin_amdgcn_sched_barrier(0);
+    wlen = lane < a.batch ? min(max(raw_len, 0), a.max_pages * kPageSize) : 0;
+    item_tokens = plan_items_wave(p.rule, units, wlen, &wpfx, &total);
+    if ((int)blockIdx.x >= a.batch * g_per_seq) spec.b = -1;
+  } else {
+    item_tokens = plan_items<kThreads>(a, p.rule, units, s_prefix, s_wave);
+    total = s_prefix[a.batch];
+  }
+  // items before sequence b (b <= batch), uniform b
+  auto prefix_of = [&](int b) {
+    if (!small) return s_prefix[b];
+    return b < a.batch ? __builtin_amdgcn_readlane(wpfx, b) : total;
+  };
+  if (blockIdx.x == 0) {
+    if (small) {
+      if (wave == 0 && lane < a.batch) p.prefix[lane] = wpfx;
+      if (tid == 0) p.prefix[a.batch] = total;
+    } else {
+      for (int b = tid; b <= a.batch; b += kThreads) p.prefix[b] = s_prefix[b];
+    }
+  }
   // a sequence with no valid length has no items: its output is 0, lse -inf
   for (int b = blockIdx.x; b < a.batch; b += gridDim.x) {
-    if (s_prefix[b] != s_prefix[b + 1]) continue;
+    if (prefix_of(b) != prefix_of(b + 1)) continue;
     for (int i = tid; i < a.n_q_heads * D; i += kThreads)
       a.out[(int64_t)b * a.n_q_heads * D + i] = 0;
     if (a.lse)
@@ -194,36 +257,6 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
     scale_off[i] = (uint32_t)(((i * TPL + tsub) * NB + (d0 >> 5)) * 2);
   }
   const int64_t page_rows = (int64_t)a.n_kv_heads * kPageSize;
-
-  // page ids of the wave's pages of an item: lane s*PPS+k holds step s, page k
-  auto load_pids = [&](const Item& it) {
-    int pid = -1;
-    if (lane < it.nsteps * PPS) {
-      const int st = lane / PPS, k = lane - st * PPS;
-      const int pi = (wave + st * kWaves) * PPS + k;
-      if (pi < it.np) {
-        const int v = a.page_table[(int64_t)it.b * a.pt_stride + it.t0 / kPageSize + pi];
-        pid = (v >= 0 && (int64_t)v < a.num_pages) ? v : -1;
-      }
-    }
-    return pid;
-  };
-  // the query slice of this lane as bf16 pairs (exact; the softmax scale is
-  // applied to each score in fp32)
-  auto load_q = [&](const Item& it, uint32_t (*qb)[EPL / 2]) {
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      const uint16_t* qrow = a.q + ((int64_t)it.b * a.n_q_heads + it.h0 + h) * D + d0;
-#pragma unroll
-      for (int e = 0; e < EPL; e += 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(qrow + e);
-        qb[h][e / 2 + 0] = v.x;
-        qb[h][e / 2 + 1] = v.y;
-        qb[h][e / 2 + 2] = v.z;
-        qb[h][e / 2 + 3] = v.w;
-      }
-    }
-  };
 
   // A step's loads.  The scales of a (page, kv head) chunk (SCL bytes) come
   // in one 4-byte-per-lane load: lane L holds bytes [4L, 4L+4), lanes past
@@ -264,7 +297,6 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
   };
 
   float mref[GT], smax[GT], lsum[GT], acc[GT][EPL];
-  uint32_t qb[GT][EPL / 2];
 
   // Log2-domain scores of a step's rows (-inf for rows on a masked page or
   // past the item end), their validity and the V scale of each row.
@@ -387,9 +419,26 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
 
   Buf R[kDepth];
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const Item cur = describe<PPS, GT>(p, item_tokens, s_prefix, item, wave, units, G);
-    const int pid_cur = load_pids(cur);
-    load_q(cur, qb);
+    int bq;
+    if (small) {
+      bq = wave_item_seq(wpfx, a.batch, item);
+    } else {
+      int lo = 0, hi = a.batch - 1;
+      while (lo < hi) {  // largest b with s_prefix[b] <= item
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_prefix[mid] <= item) lo = mid; else hi = mid - 1;
+      }
+      bq = lo;
+    }
+    const int L = small ? __builtin_amdgcn_readlane(wlen, bq) : clamped_len(a, bq);
+    const Item cur = describe<PPS, GT>(p, item_tokens, item, bq, item - prefix_of(bq), L, wave, units, G);
+    const bool hit = cur.b == spec.b && cur.u == spec.u && cur.t0 == spec.t0 && cur.nt == spec.nt;
+    spec.b = -1;  // the speculative loads serve the first item only
+    int pid_cur = pid_spec;
+    if (!hit) {
+      pid_cur = load_pids(cur);
+      load_q(cur);
+    }
     // Stream the item's steps, kDepth steps' loads in flight (cur.nsteps is
     // a multiple of kDepth).  The softmax reference of each head stays fixed
     // over a pass: the largest score of the wave's first step (0 when it has
@@ -514,10 +563,24 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
       }
       __syncthreads();
       if (s_last) {
-        const int first = s_prefix[b] + u;  // item of chunk c: first + c * units
+        const int first = prefix_of(b) + u;  // item of chunk c: first + c * units
+        const int64_t cstride = (int64_t)units * GT * D;  // between chunks of this group
+        // All of the merge's first loads are issued before any is used: this
+        // thread's first output column over the first 16 chunks, and every
+        // chunk's (m, l).
+        float x0[16];
+        {
+          const int idx = min(tid, GT * D - 1), h = idx / D, d = idx - h * D;
+          const float* src = p.part_acc + ((int64_t)first * GT + h) * D + d;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) x0[j] = (j < nc) ? load_agent(src + j * cstride) : 0.0f;
+        }
+        float* s_l = s_red + kMergeMaxWeights;
         for (int idx = tid; idx < nc * GT; idx += kThreads) {
           const int c = idx / GT, h = idx - c * GT;
-          s_red[idx] = load_agent(&p.part_ml[((int64_t)(first + c * units) * GT + h) * 2]);
+          const float* ml = &p.part_ml[((int64_t)(first + c * units) * GT + h) * 2];
+          s_red[idx] = load_agent(ml);
+          s_l[idx] = load_agent(ml + 1);
         }
         __syncthreads();
         for (int h = wave; h < GT; h += kWaves) {
@@ -527,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
           float Ls = 0.0f;
           for (int c = lane; c < nc; c += 64) {
             const float w = exp2_rel(s_red[c * GT + h], M);
-            Ls += w * load_agent(&p.part_ml[((int64_t)(first + c * units) * GT + h) * 2 + 1]);
+            Ls += w * s_l[c * GT + h];
             s_red[c * GT + h] = w;
           }
           Ls = stride_sum<1>(Ls);
@@ -540,13 +603,17 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
         for (int idx = tid; idx < GT * D; idx += kThreads) {
           const int h = idx / D, d = idx - h * D;
           const float* src = p.part_acc + ((int64_t)first * GT + h) * D + d;
-          const int64_t cstride = (int64_t)units * GT * D;  // between chunks of this group
           float v = 0.0f;
           for (int c0 = 0; c0 < nc; c0 += 16) {  // 16 loads in flight per thread
             float x[16];
+            if (idx == tid && c0 == 0) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-              x[j] = (c0 + j < nc) ? load_agent(src + (c0 + j) * cstride) : 0.0f;
+              for (int j = 0; j < 16; ++j) x[j] = x0[j];
+            } else {
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+                x[j] = (c0 + j < nc) ? load_agent(src + (c0 + j) * cstride) : 0.0f;
+            }
 #pragma unroll
             for (int j = 0; j < 16; ++j)
               if (c0 + j < nc) v += s_red[(c0 + j) * GT + h] * x[j];
@@ -608,9 +675,14 @@ hipError_t launch_gqa_decode(const DecodeArgs& a, const DecodePlan& plan, int nu
   gp.count = reinterpret_cast<int*>(ws + plan.off_count);
   gp.part_ml = reinterpret_cast<float*>(ws + plan.off_ml);
   gp.part_acc = reinterpret_cast<float*>(ws + plan.off_acc);
-  // about one work item per workgroup when the batch is short; a persistent
-  // grid strides over the rest
-  int64_t grid = plan.target;
+  // Items are sized for about one per compute unit (plan.target); the grid
+  // holds two workgroups per compute unit.  When the items are that few, the
+  // second half finds no item and exits after the prologue, so each compute
+  // unit streams one item alone; when there are many more items (long or
+  // many sequences), the persistent grid strides over them with two
+  // workgroups per compute unit, one streaming while the other is between
+  // items.
+  int64_t grid = 2 * (int64_t)num_cus;
   if (grid > plan.max_items) grid = plan.max_items;
   if (grid < 1) grid = 1;
   hipError_t e;
