@@ -133,6 +133,10 @@ __device__ __forceinline__ void ds_write8(uint32_t addr, u32x2 v) {
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 constexpr int kAhead = 4;  // operand reads in flight
+// The next tile's codes are loaded from inside the S^T multiplies, after
+// read kLoadAt: any register reload the compiler places at the top of the
+// tile then waits for its own load only, not for this tile's prefetch.
+constexpr int kLoadAt = 3;
 constexpr int kRing = kAhead + 1;
 // Dequantization micro-steps of the next tile (one LDS write each), run from
 // P V step kStoreAt on.
@@ -443,6 +447,9 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
             constexpr int n = r + kAhead;
             ds_read16<(n % 2) * 16 * kKS * 2 + (n / 2) * 64>(ring[n % kRing], ka);
           }
+          // tile j+1's codes (dequantized during the P V multiplies below)
+          if constexpr (r == kLoadAt)
+            if (j + 1 < ntiles && j > 0) load_tile(j + 1, R);
         });
       }
       mfma16_v_settle(S[0][0], S[0][1], S[1][0], S[1][1]);
@@ -502,7 +509,6 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
           if constexpr (dt >= kStoreAt) store_step(std::integral_constant<int, dt - kStoreAt>{}, R);
         });
       }
-      if (j + 2 < ntiles) load_tile(j + 2, R);
     };
 
     MlaRaw<QT> R;
