@@ -137,6 +137,44 @@ __device__ __forceinline__ Item describe(const GqaParams& p, int item_tokens, in
   return it;
 }
 
+// One level of a reduce-scatter over lane pairs that differ in lane bit B:
+// of the N values a lane holds, it keeps the first half (bit B clear) or the
+// second half (bit B set), each summed with the partner lane's copy.  Bits 5
+// and 4 pair rows through the gfx950 permlane swaps (the pair they return
+// holds, in every lane, its kept value and the partner's); bit 3 pairs
+// lanes 8 apart inside a row of 16 through a DPP rotation.
+template <int B, int N>
+__device__ __forceinline__ void reduce_scatter_level(float* x) {
+  constexpr int H = N / 2;
+  static_assert(N % 2 == 0 && B >= 3 && B <= 5, "reduce-scatter level");
+  if constexpr (B == 5) {
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i + H]),
+                                                      false, false);
+      x[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  } else if constexpr (B == 4) {
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[i]), __float_as_uint(x[i + H]),
+                                                      false, false);
+      x[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  } else {
+    const bool hi = (threadIdx.x & 8) != 0;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const float send = hi ? x[i] : x[i + H], keep = hi ? x[i + H] : x[i];
+      x[i] = keep + dpp<kRowRor<8>>(send);
+    }
+  }
+}
+
+// The last workgroup of a split sequence merges up to this many chunks per
+// thread straight from global memory.
+constexpr int kSmallMerge = 16;
+
 template <int QT, int D, int GT>
 __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
   using Gm = Geo<QT, D>;
@@ -147,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
   // merge's chunk weights and sums [2][chunks][GT]
   constexpr int kRed = (kWaves * GT * D > 2 * kMergeMaxWeights) ? kWaves * GT * D : 2 * kMergeMaxWeights;
   extern __shared__ int s_prefix[];  // [batch + 1]
-  __shared__ float s_red[kRed];
+  __shared__ __attribute__((aligned(16))) float s_red[kRed];
   __shared__ float s_ml[kWaves][GT][2];
   __shared__ float s_hm[GT][2];
   __shared__ int s_wave[kWaves];
@@ -497,18 +535,41 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
     for (int h = 0; h < GT; ++h) m[h] = (M[h] == -INFINITY) ? -INFINITY : mref[h];
 
     // ---- merge the rows held by other lanes, then the four waves ------------------
+    // Row sums over the TPL lanes of a column slice; the accumulators by a
+    // reduce-scatter when those lanes differ in lane bits 3..5 (LPT >= 8):
+    // lane (tsub, seg) ends with NK consecutive values of its slice, the
+    // sums of X[tsub * NK ..] over the TPL lanes, X[h * EPL + e] = acc[h][e].
+    constexpr int NX = GT * EPL;
+    constexpr bool kScatter = LPT >= 8;
+    constexpr int NK = kScatter ? NX / TPL : NX;
+    float xs[NX];
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
       lsum[h] = stride_sum<LPT>(lsum[h]);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = stride_sum<LPT>(acc[h][e]);
+      for (int e = 0; e < EPL; ++e) xs[h * EPL + e] = acc[h][e];
+    }
+    if constexpr (kScatter) {
+      reduce_scatter_level<5, NX>(xs);
+      if constexpr (LPT <= 16) reduce_scatter_level<4, NX / 2>(xs);
+      if constexpr (LPT <= 8) reduce_scatter_level<3, NX / 4>(xs);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NX; ++j) xs[j] = stride_sum<LPT>(xs[j]);
     }
     __syncthreads();  // s_red / s_ml of the previous item are free
-    if (tsub == 0)
+    if (kScatter || tsub == 0) {
+      const int j0 = kScatter ? tsub * NK : 0;
 #pragma unroll
-      for (int h = 0; h < GT; ++h)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) s_red[(wave * GT + h) * D + d0 + e] = acc[h][e];
+      for (int i = 0; i < NK; i += (NK % 4 == 0 ? 4 : 1)) {
+        const int j = j0 + i, h = j / EPL, e = j - h * EPL;
+        float* dst = &s_red[(wave * GT + h) * D + d0 + e];
+        if constexpr (NK % 4 == 0)
+          *reinterpret_cast<f32x4*>(dst) = f32x4{xs[i], xs[i + 1], xs[i + 2], xs[i + 3]};
+        else
+          *dst = xs[i];
+      }
+    }
     if (lane == 0)
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
@@ -516,26 +577,25 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
         s_ml[wave][h][1] = lsum[h];
       }
     __syncthreads();
-    if (tid < GT) {
-      float M = s_ml[0][tid][0];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_ml[w][tid][0]);
-      float Ls = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) Ls += exp2_rel(s_ml[w][tid][0], M) * s_ml[w][tid][1];
-      s_hm[tid][0] = M;
-      s_hm[tid][1] = Ls;
-    }
-    __syncthreads();
+    // every thread weighs the four waves itself: M = max m_w, weights
+    // 2^(m_w - M) (LDS broadcast reads; no further barrier)
     const int b = cur.b, u = cur.u, nc = cur.nc, h0 = cur.h0;
     for (int idx = tid; idx < GT * D; idx += kThreads) {
       const int h = idx / D, d = idx - h * D;
-      const float M = s_hm[h][0];
-      float v = 0.0f;
+      float mw[kWaves], M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) v += exp2_rel(s_ml[w][h][0], M) * s_red[(w * GT + h) * D + d];
+      for (int w = 0; w < kWaves; ++w) {
+        mw[w] = s_ml[w][h][0];
+        M = fmaxf(M, mw[w]);
+      }
+      float v = 0.0f, Ls = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float wt = exp2_rel(mw[w], M);
+        v += wt * s_red[(w * GT + h) * D + d];
+        Ls += wt * s_ml[w][h][1];
+      }
       if (nc == 1) {
-        const float Ls = s_hm[h][1];
         const int64_t orow = (int64_t)b * a.n_q_heads + h0 + h;
         a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
         if (d == 0 && a.lse) a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
@@ -543,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
         store_agent(&p.part_acc[((int64_t)item * GT + h) * D + d], v);
         if (d == 0) {
           store_agent(&p.part_ml[((int64_t)item * GT + h) * 2 + 0], M);
-          store_agent(&p.part_ml[((int64_t)item * GT + h) * 2 + 1], s_hm[h][1]);
+          store_agent(&p.part_ml[((int64_t)item * GT + h) * 2 + 1], Ls);
         }
       }
     }
@@ -565,64 +625,83 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
       if (s_last) {
         const int first = prefix_of(b) + u;  // item of chunk c: first + c * units
         const int64_t cstride = (int64_t)units * GT * D;  // between chunks of this group
-        // All of the merge's first loads are issued before any is used: this
-        // thread's first output column over the first 16 chunks, and every
-        // chunk's (m, l).
-        float x0[16];
-        {
-          const int idx = min(tid, GT * D - 1), h = idx / D, d = idx - h * D;
-          const float* src = p.part_acc + ((int64_t)first * GT + h) * D + d;
+        if (nc <= kSmallMerge) {
+          // Each thread merges its own columns from global memory: the
+          // chunks' partial sums and (m, l) are loaded together, then
+          // M = max m_c, weights 2^(m_c - M).  No LDS, no barrier.
+          for (int idx = tid; idx < GT * D; idx += kThreads) {
+            const int h = idx / D, d = idx - h * D;
+            const float* src = p.part_acc + ((int64_t)first * GT + h) * D + d;
+            const float* ml = p.part_ml + ((int64_t)first * GT + h) * 2;
+            float x[kSmallMerge], mc[kSmallMerge], lc[kSmallMerge];
 #pragma unroll
-          for (int j = 0; j < 16; ++j) x0[j] = (j < nc) ? load_agent(src + j * cstride) : 0.0f;
-        }
-        float* s_l = s_red + kMergeMaxWeights;
-        for (int idx = tid; idx < nc * GT; idx += kThreads) {
-          const int c = idx / GT, h = idx - c * GT;
-          const float* ml = &p.part_ml[((int64_t)(first + c * units) * GT + h) * 2];
-          s_red[idx] = load_agent(ml);
-          s_l[idx] = load_agent(ml + 1);
-        }
-        __syncthreads();
-        for (int h = wave; h < GT; h += kWaves) {
-          float M = -INFINITY;
-          for (int c = lane; c < nc; c += 64) M = fmaxf(M, s_red[c * GT + h]);
-          M = stride_max<1>(M);
-          float Ls = 0.0f;
-          for (int c = lane; c < nc; c += 64) {
-            const float w = exp2_rel(s_red[c * GT + h], M);
-            Ls += w * s_l[c * GT + h];
-            s_red[c * GT + h] = w;
-          }
-          Ls = stride_sum<1>(Ls);
-          if (lane == 0) {
-            s_hm[h][0] = M;
-            s_hm[h][1] = Ls;
-          }
-        }
-        __syncthreads();
-        for (int idx = tid; idx < GT * D; idx += kThreads) {
-          const int h = idx / D, d = idx - h * D;
-          const float* src = p.part_acc + ((int64_t)first * GT + h) * D + d;
-          float v = 0.0f;
-          for (int c0 = 0; c0 < nc; c0 += 16) {  // 16 loads in flight per thread
-            float x[16];
-            if (idx == tid && c0 == 0) {
+            for (int c = 0; c < kSmallMerge; ++c) {
+              x[c] = (c < nc) ? load_agent(src + c * cstride) : 0.0f;
+              mc[c] = (c < nc) ? load_agent(ml + c * units * GT * 2) : -INFINITY;
+              lc[c] = (c < nc) ? load_agent(ml + c * units * GT * 2 + 1) : 0.0f;
+            }
+            float M = mc[0];
 #pragma unroll
-              for (int j = 0; j < 16; ++j) x[j] = x0[j];
-            } else {
+            for (int c = 1; c < kSmallMerge; ++c) M = fmaxf(M, mc[c]);
+            float v = 0.0f, Ls = 0.0f;
+#pragma unroll
+            for (int c = 0; c < kSmallMerge; ++c) {
+              const float w = exp2_rel(mc[c], M);
+              v += w * x[c];
+              Ls += w * lc[c];
+            }
+            const int64_t orow = (int64_t)b * a.n_q_heads + h0 + h;
+            a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
+            if (d == 0 && a.lse)
+              a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
+          }
+        } else {
+          // Many chunks: their (m, l) go through LDS, one wave per head
+          // forms the weights, then each thread sums its columns.
+          float* s_l = s_red + kMergeMaxWeights;
+          for (int idx = tid; idx < nc * GT; idx += kThreads) {
+            const int c = idx / GT, h = idx - c * GT;
+            const float* ml = &p.part_ml[((int64_t)(first + c * units) * GT + h) * 2];
+            s_red[idx] = load_agent(ml);
+            s_l[idx] = load_agent(ml + 1);
+          }
+          __syncthreads();
+          for (int h = wave; h < GT; h += kWaves) {
+            float M = -INFINITY;
+            for (int c = lane; c < nc; c += 64) M = fmaxf(M, s_red[c * GT + h]);
+            M = stride_max<1>(M);
+            float Ls = 0.0f;
+            for (int c = lane; c < nc; c += 64) {
+              const float w = exp2_rel(s_red[c * GT + h], M);
+              Ls += w * s_l[c * GT + h];
+              s_red[c * GT + h] = w;
+            }
+            Ls = stride_sum<1>(Ls);
+            if (lane == 0) {
+              s_hm[h][0] = M;
+              s_hm[h][1] = Ls;
+            }
+          }
+          __syncthreads();
+          for (int idx = tid; idx < GT * D; idx += kThreads) {
+            const int h = idx / D, d = idx - h * D;
+            const float* src = p.part_acc + ((int64_t)first * GT + h) * D + d;
+            float v = 0.0f;
+            for (int c0 = 0; c0 < nc; c0 += 16) {  // 16 loads in flight per thread
+              float x[16];
 #pragma unroll
               for (int j = 0; j < 16; ++j)
                 x[j] = (c0 + j < nc) ? load_agent(src + (c0 + j) * cstride) : 0.0f;
-            }
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-              if (c0 + j < nc) v += s_red[(c0 + j) * GT + h] * x[j];
+              for (int j = 0; j < 16; ++j)
+                if (c0 + j < nc) v += s_red[(c0 + j) * GT + h] * x[j];
+            }
+            const float M = s_hm[h][0], Ls = s_hm[h][1];
+            const int64_t orow = (int64_t)b * a.n_q_heads + h0 + h;
+            a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
+            if (d == 0 && a.lse)
+              a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
           }
-          const float M = s_hm[h][0], Ls = s_hm[h][1];
-          const int64_t orow = (int64_t)b * a.n_q_heads + h0 + h;
-          a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
-          if (d == 0 && a.lse)
-            a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
         }
         if (tid == 0)  // ready for the next call
           __hip_atomic_store(&p.count[(int64_t)b * units + u], 0, __ATOMIC_RELAXED,
