@@ -45,12 +45,21 @@ struct ihipStream_t;
 typedef struct ihipStream_t* kvq_stream_t;
 
 /* Storage type of a pool.  KVQ_BF16 stores rows unchanged (no scales); the
- * two 8-bit types share one scale layout, store kernel and dequant path
- * [PR103 §What]. */
+ * two block-scaled 8-bit types share one scale layout, store kernel and
+ * dequant path [PR103 §What].  The two cast types store each element itself
+ * as an 8-bit float (a per-tensor scale of 1.0) and have no scale buffer:
+ * one byte per element, twice bf16's tokens in the same bytes [PR126 "Add fp8
+ * KV-cache quantization (--kv-dtype)" §Summary (e4m3 or e5m2), §How it works
+ * (the store casts with scale 1.0), §Benchmark (2.00x the token budget)].
+ * The cast rounds to nearest even; a magnitude beyond the format's largest
+ * finite value stores that value (448 for e4m3, 57344 for e5m2), the same
+ * saturation the block-scaled store applies.  Inputs must be finite. */
 typedef enum {
-  KVQ_BF16 = 0,     /* 2 bytes per element, no scale buffer                     */
-  KVQ_FP8_E4M3 = 1, /* e4m3fn codes, scale = max|x| / 448 per 32-block          */
-  KVQ_Q8_0 = 2      /* int8 codes in [-127, 127], scale = max|x| / 127          */
+  KVQ_BF16 = 0,          /* 2 bytes per element, no scale buffer                  */
+  KVQ_FP8_E4M3 = 1,      /* e4m3fn codes, scale = max|x| / 448 per 32-block       */
+  KVQ_Q8_0 = 2,          /* int8 codes in [-127, 127], scale = max|x| / 127       */
+  KVQ_FP8_E4M3_CAST = 3, /* e4m3fn code of x itself, no scale buffer              */
+  KVQ_FP8_E5M2_CAST = 4  /* e5m2 code of x itself, no scale buffer                */
 } kvq_dtype;
 
 typedef enum {
@@ -72,7 +81,8 @@ typedef enum {
  *   scales: [num_pages][n_heads][page_size][head_dim / 32] fp16 (IEEE binary16
  *           bit patterns), a separate buffer beside the codes [PR103 §What:
  *           parallel scale buffers; PR113 §What this adds: one scale array
- *           beside the single MLA slab].
+ *           beside the single MLA slab].  The block-scaled types only; the
+ *           cast types and KVQ_BF16 have none.
  * A token lives at slot = page * page_size + offset.  For the MLA latent slab
  * (one KV head, K and V the same row) n_heads = 1 and head_dim = 576.
  * ------------------------------------------------------------------------- */
@@ -82,7 +92,8 @@ typedef enum {
  * function, so that the budget and the pool cannot disagree [PR113 §One
  * ordering trap worth knowing about; PR103 §What: unit_bytes()/kv_cost() on
  * effective bytes].  Host-only, pure.  *code_bytes and *scale_bytes (each
- * nullable) receive the two parts; scale bytes are 0 for KVQ_BF16.
+ * nullable) receive the two parts; scale bytes are 0 for KVQ_BF16 and the
+ * cast types.
  * Returns -1 (and sets the error message) on invalid arguments:
  * num_pages < 0, page_size < 1, n_heads < 1, head_dim < 1, head_dim not a
  * multiple of 32 for an 8-bit type, or an unknown dtype. */
@@ -100,7 +111,9 @@ int64_t kvq_pool_bytes(kvq_dtype dtype, int64_t num_pages, int page_size, int n_
  *     code_i = round(clamp(fp32(x_i / s), -M, M)), e4m3: nearest even,
  *         q8_0: half away from zero; s == 0 gives all-zero codes.
  * Both quotients are IEEE fp32 divisions; the result is bit-exact and
- * deterministic.  KVQ_BF16 copies the row unchanged.
+ * deterministic.  KVQ_BF16 copies the row unchanged.  The cast types store
+ *     code_i = round(clamp(x_i, -M, M)), nearest even, M = 448 (e4m3) or
+ *         57344 (e5m2), and write no scale.
  *
  *   k_src, v_src : device, bf16 [n_tokens][..] rows; head h of token n starts
  *                  at element n * src_token_stride + h * head_dim.  v_src may
@@ -112,7 +125,7 @@ int64_t kvq_pool_bytes(kvq_dtype dtype, int64_t num_pages, int page_size, int n_
  *                  page_size is skipped.  Two tokens with the same slot in
  *                  one call leave that slot undefined.
  *   k_pool/v_pool, k_scales/v_scales : device, layout above; scales are
- *                  ignored (may be NULL) for KVQ_BF16.
+ *                  ignored (may be NULL) for KVQ_BF16 and the cast types.
  * Supported: head_dim a multiple of 32 (any multiple of 8 for KVQ_BF16) up
  * to 1024, n_heads >= 1, page_size 1..1024, n_tokens >= 0 (0 is a no-op).
  * Errors: KVQ_ERR_ARG, KVQ_ERR_HIP. */
@@ -124,8 +137,10 @@ int kvq_store(kvq_dtype dtype, const void* k_src, const void* v_src,
 /* Gather-dequantize rows to bf16 [PR103 §What: dequant path; PR126 §How it
  * works: dequantize on read].  out[n][h][d] = bf16_rne(code * s) for the row
  * at slot_mapping[n]; an invalid slot gives a row of zeros.  code * s is exact
- * in fp32, so the only rounding is the final one to bf16.
- *   pool, scales : device, layout above (scales ignored for KVQ_BF16).
+ * in fp32, so the only rounding is the final one to bf16 (s = 1 for the cast
+ * types, whose codes are exact in bf16).
+ *   pool, scales : device, layout above (scales ignored for KVQ_BF16 and the
+ *                  cast types).
  *   out_bf16     : device bf16 [n_tokens][n_heads][head_dim], 16-byte aligned.
  * Supported and errors as kvq_store. */
 int kvq_dequant(kvq_dtype dtype, const void* pool, const uint16_t* scales,

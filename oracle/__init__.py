@@ -22,8 +22,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "kvq_oracle.c")
 LIB = os.path.join(HERE, "libkvq_oracle.so")
 
-BF16, FP8_E4M3, Q8_0 = 0, 1, 2
-QTYPES = {"bf16": BF16, "fp8_e4m3": FP8_E4M3, "q8_0": Q8_0}
+BF16, FP8_E4M3, Q8_0, FP8_E4M3_CAST, FP8_E5M2_CAST = 0, 1, 2, 3, 4
+QTYPES = {"bf16": BF16, "fp8_e4m3": FP8_E4M3, "q8_0": Q8_0, "fp8_e4m3_cast": FP8_E4M3_CAST,
+          "fp8_e5m2_cast": FP8_E5M2_CAST}
+# storage types with a scale buffer beside the pool
+SCALED = ("fp8_e4m3", "q8_0")
 
 _lib = None
 
@@ -92,6 +95,14 @@ def _declare(L):
     L.kvo_e4m3_encode_array.restype = None
     L.kvo_q8_encode_array.argtypes = [P, c.c_int64, P]
     L.kvo_q8_encode_array.restype = None
+    L.kvo_e5m2_value.argtypes = [c.c_uint8]
+    L.kvo_e5m2_value.restype = c.c_double
+    L.kvo_e5m2_encode.argtypes = [c.c_float]
+    L.kvo_e5m2_encode.restype = c.c_uint8
+    L.kvo_cast_encode.argtypes = [c.c_int, c.c_float]
+    L.kvo_cast_encode.restype = c.c_uint8
+    L.kvo_cast_encode_array.argtypes = [c.c_int, P, c.c_int64, P]
+    L.kvo_cast_encode_array.restype = None
 
 
 def default_threads() -> int:
@@ -126,6 +137,18 @@ def q8_encode(v: np.ndarray) -> np.ndarray:
     out = np.empty(v.shape, dtype=np.int8)
     lib().kvo_q8_encode_array(_ptr(v), v.size, _ptr(out))
     return out
+
+
+def cast_encode(qtype, v: np.ndarray) -> np.ndarray:
+    """The cast store of each element (per-tensor scale 1.0): clamp, round."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().kvo_cast_encode_array(_qt(qtype), _ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e5m2_value(code: int) -> float:
+    return lib().kvo_e5m2_value(code)
 
 
 def e4m3_value(code: int) -> float:

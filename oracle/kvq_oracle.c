@@ -38,6 +38,11 @@
 #define KVO_BF16 0
 #define KVO_FP8_E4M3 1
 #define KVO_Q8_0 2
+/* Per-tensor scale 1.0: each element cast to fp8 itself, no scale buffer
+ * [PR126 §How it works: the store casts the bf16 k/v to the pool's fp8 dtype
+ * with scale 1.0; §Summary: fp8_e4m3 or fp8_e5m2]. */
+#define KVO_FP8_E4M3_CAST 3
+#define KVO_FP8_E5M2_CAST 4
 
 /* Quantization block length along head_dim, and the two format maxima:
  * 448 is the largest finite e4m3 magnitude, 127 the int8 limit [PR103 §What;
@@ -46,6 +51,9 @@
 #define KVO_E4M3_MAX 448.0f
 #define KVO_Q8_MAX 127.0f
 #define KVO_F16_MAX 65504.0
+/* Largest finite e5m2 magnitude: 1.75 * 2^15 (the exponent field 31 holds
+ * the infinities and NaNs). */
+#define KVO_E5M2_MAX 57344.0f
 
 /* ------------------------------------------------------------------------ */
 /* Rounding onto a binary floating-point grid.                               */
@@ -149,6 +157,45 @@ uint8_t kvo_e4m3_encode(float v) {
   return s | (uint8_t)(E << 3) | m;
 }
 
+/* ---- fp8 e5m2 ------------------------------------------------------------
+ * Bias 15, 2 fraction bits, IEEE-like: exponent field 31 is infinity (m = 0)
+ * or NaN.  Normal codes: (1 + m/4) * 2^(e-15), e = 1..30; subnormal: m * 2^-16.
+ * [PR126 §Summary: --kv-dtype fp8_e5m2.] */
+double kvo_e5m2_value(uint8_t c) {
+  int s = c >> 7, e = (c >> 2) & 0x1f, m = c & 3;
+  double v;
+  if (e == 31) v = m ? NAN : INFINITY;
+  else if (e == 0)
+    v = ldexp((double)m, -16);
+  else
+    v = ldexp(1.0 + m / 4.0, e - 15);
+  return s ? -v : v;
+}
+
+/* Encode v (|v| <= 57344, finite) as the nearest e5m2 code, ties to the code
+ * with an even last fraction bit; the sign is kept (-0 encodes as 0x80). */
+uint8_t kvo_e5m2_encode(float v) {
+  uint8_t s = signbit(v) ? 0x80 : 0;
+  double r = round_to_grid(fabs((double)v), 2, -14);
+  if (r < ldexp(1.0, -14)) return s | (uint8_t)(r * 65536.0); /* m * 2^-16 */
+  int e;
+  double f = frexp(r, &e);
+  int E = e - 1 + 15;
+  uint8_t m = (uint8_t)((f * 2.0 - 1.0) * 4.0);
+  return s | (uint8_t)(E << 2) | m;
+}
+
+/* The cast store of one element (per-tensor scale 1.0).  The pages leave a
+ * value beyond the format's range open (their k/v "sit well inside" it); the
+ * reading taken is the saturation the block-scaled store applies: clamp to
+ * the largest finite magnitude, then round to nearest even. */
+uint8_t kvo_cast_encode(int qtype, float x) {
+  float M = (qtype == KVO_FP8_E5M2_CAST) ? KVO_E5M2_MAX : KVO_E4M3_MAX;
+  if (x > M) x = M;
+  if (x < -M) x = -M;
+  return (qtype == KVO_FP8_E5M2_CAST) ? kvo_e5m2_encode(x) : kvo_e4m3_encode(x);
+}
+
 /* ---- q8_0 ----------------------------------------------------------------
  * Round half away from zero (the GGUF Q8_0 convention the review comment on
  * [PR103] names, §"A bug on sm_89"), for |v| <= 127.  |v| + 0.5 is exact in
@@ -208,6 +255,8 @@ void kvo_quantize_block(int qtype, const uint16_t* x, int n, uint8_t* codes,
  * Both factors have few significant bits, so the product is exact in double
  * (and in fp32).  bf16 pools store the value itself. */
 double kvo_element_value(int qtype, uint8_t code, uint16_t scale) {
+  if (qtype == KVO_FP8_E4M3_CAST) return kvo_e4m3_value(code);
+  if (qtype == KVO_FP8_E5M2_CAST) return kvo_e5m2_value(code);
   if (qtype == KVO_Q8_0) return (double)(int8_t)code * kvo_f16_value(scale);
   return kvo_e4m3_value(code) * kvo_f16_value(scale);
 }
@@ -290,6 +339,11 @@ static void kvo_store_unit(void* p, int64_t n) {
       memcpy(c->pool + r * c->head_dim * 2, row, (size_t)c->head_dim * 2);
       continue;
     }
+    if (c->qtype == KVO_FP8_E4M3_CAST || c->qtype == KVO_FP8_E5M2_CAST) {
+      for (int d = 0; d < c->head_dim; ++d)
+        c->pool[r * c->head_dim + d] = kvo_cast_encode(c->qtype, (float)kvo_bf16_value(row[d]));
+      continue;
+    }
     for (int j = 0; j < nb; ++j)
       kvo_quantize_block(c->qtype, row + j * KVO_BLOCK, KVO_BLOCK,
                          c->pool + r * c->head_dim + j * KVO_BLOCK, c->scales + r * nb + j);
@@ -327,6 +381,8 @@ static double kvo_pool_value(int qtype, const uint8_t* pool, const uint16_t* sca
     memcpy(&b, pool + (row * head_dim + d) * 2, 2);
     return kvo_bf16_value(b);
   }
+  if (qtype == KVO_FP8_E4M3_CAST || qtype == KVO_FP8_E5M2_CAST)
+    return kvo_element_value(qtype, pool[row * head_dim + d], 0);
   int nb = head_dim / KVO_BLOCK;
   return kvo_element_value(qtype, pool[row * head_dim + d], scales[row * nb + d / KVO_BLOCK]);
 }
@@ -463,4 +519,7 @@ void kvo_e4m3_encode_array(const float* v, int64_t n, uint8_t* out) {
 }
 void kvo_q8_encode_array(const float* v, int64_t n, int8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = kvo_q8_encode(v[i]);
+}
+void kvo_cast_encode_array(int qtype, const float* v, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = kvo_cast_encode(qtype, v[i]);
 }

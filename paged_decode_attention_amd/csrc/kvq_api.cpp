@@ -39,7 +39,12 @@ int ok() {
   return KVQ_OK;
 }
 
-bool known_dtype(int d) { return d == KVQ_BF16 || d == KVQ_FP8_E4M3 || d == KVQ_Q8_0; }
+bool known_dtype(int d) {
+  return d == KVQ_BF16 || d == KVQ_FP8_E4M3 || d == KVQ_Q8_0 || d == KVQ_FP8_E4M3_CAST ||
+         d == KVQ_FP8_E5M2_CAST;
+}
+// a scale buffer beside the pool (the block-scaled types)
+bool scaled(int d) { return d == KVQ_FP8_E4M3 || d == KVQ_Q8_0; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -212,7 +217,7 @@ int64_t kvq_pool_bytes(kvq_dtype dtype, int64_t num_pages, int page_size, int n_
     return fail(-1, "kvq_pool_bytes: head_dim %d is not a multiple of %d", head_dim, KVQ_BLOCK);
   const int64_t elems = num_pages * page_size * (int64_t)n_heads * head_dim;
   const int64_t codes = (dtype == KVQ_BF16) ? 2 * elems : elems;
-  const int64_t scales = (dtype == KVQ_BF16) ? 0 : (elems / KVQ_BLOCK) * 2;
+  const int64_t scales = scaled(dtype) ? (elems / KVQ_BLOCK) * 2 : 0;
   if (code_bytes) *code_bytes = codes;
   if (scale_bytes) *scale_bytes = scales;
   g_err.clear();
@@ -227,8 +232,8 @@ int kvq_store(kvq_dtype dtype, const void* k_src, const void* v_src, int64_t src
   if (rc != KVQ_OK) return rc;
   if (n_tokens == 0) return ok();
   if (!k_src || !slot_mapping || !k_pool) return fail(KVQ_ERR_ARG, "kvq_store: null pointer");
-  if (dtype != KVQ_BF16 && !k_scales) return fail(KVQ_ERR_ARG, "kvq_store: null k_scales");
-  if (v_src && (!v_pool || (dtype != KVQ_BF16 && !v_scales)))
+  if (scaled(dtype) && !k_scales) return fail(KVQ_ERR_ARG, "kvq_store: null k_scales");
+  if (v_src && (!v_pool || (scaled(dtype) && !v_scales)))
     return fail(KVQ_ERR_ARG, "kvq_store: v_src given without v_pool/v_scales");
   if (src_token_stride < (int64_t)n_heads * head_dim || src_token_stride % 8 != 0)
     return fail(KVQ_ERR_ARG,
@@ -238,7 +243,7 @@ int kvq_store(kvq_dtype dtype, const void* k_src, const void* v_src, int64_t src
     return fail(KVQ_ERR_ARG, "kvq_store: k_src/v_src must be 16-byte aligned");
   if (!aligned(k_pool, 16) || (v_src && !aligned(v_pool, 16)))
     return fail(KVQ_ERR_ARG, "kvq_store: pools must be 16-byte aligned");
-  if (dtype != KVQ_BF16 && (!aligned(k_scales, 2) || (v_src && !aligned(v_scales, 2))))
+  if (scaled(dtype) && (!aligned(k_scales, 2) || (v_src && !aligned(v_scales, 2))))
     return fail(KVQ_ERR_ARG, "kvq_store: scales must be 2-byte aligned");
   kvq::StoreArgs a;
   a.qtype = dtype;
@@ -266,7 +271,7 @@ int kvq_dequant(kvq_dtype dtype, const void* pool, const uint16_t* scales,
   int rc = check_rows(dtype, n_tokens, n_heads, head_dim, page_size, num_pages, "kvq_dequant");
   if (rc != KVQ_OK) return rc;
   if (n_tokens == 0) return ok();
-  if (!pool || !slot_mapping || !out_bf16 || (dtype != KVQ_BF16 && !scales))
+  if (!pool || !slot_mapping || !out_bf16 || (scaled(dtype) && !scales))
     return fail(KVQ_ERR_ARG, "kvq_dequant: null pointer");
   if (!aligned(pool, 16) || !aligned(out_bf16, 16))
     return fail(KVQ_ERR_ARG, "kvq_dequant: pool and out must be 16-byte aligned");
@@ -330,10 +335,10 @@ int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
     return fail(KVQ_ERR_ARG, "kvq_paged_decode: sm_scale is not finite");
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out_bf16)
     return fail(KVQ_ERR_ARG, "kvq_paged_decode: null pointer");
-  if (dtype != KVQ_BF16 && (!k_scales || !v_scales))
+  if (scaled(dtype) && (!k_scales || !v_scales))
     return fail(KVQ_ERR_ARG, "kvq_paged_decode: null scales");
   const bool shared = (k_pool == v_pool);
-  if (shared != (k_scales == v_scales) && dtype != KVQ_BF16)
+  if (shared != (k_scales == v_scales) && scaled(dtype))
     return fail(KVQ_ERR_ARG, "kvq_paged_decode: k_pool == v_pool requires k_scales == v_scales");
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out_bf16, 4))
     return fail(KVQ_ERR_ARG, "kvq_paged_decode: q and pools must be 16-byte aligned");

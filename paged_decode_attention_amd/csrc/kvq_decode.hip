@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
   __shared__ int s_wave[kWaves];
   __shared__ int s_last;
   // per-wave staging of a step's K and V scales
-  __shared__ __attribute__((aligned(16))) uint8_t s_scl[kWaves][(QT == QT_BF16 ? 1 : 2 * PPS * SCL)];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scl[kWaves][(qt_scaled(QT) ? 2 * PPS * SCL : 1)];
 
   const DecodeArgs& a = p.a;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
         X.k[k * LPP + i] = buf_load<NDW>(rk, code_off[i]);
         X.v[k * LPP + i] = buf_load<NDW>(rv, code_off[i]);
       }
-      if constexpr (QT != QT_BF16) {
+      if constexpr (qt_scaled(QT)) {
         const auto rks = page_rsrc(a.k_scales + row0 * NB, live ? SCL : 0);
         const auto rvs = page_rsrc(a.v_scales + row0 * NB, live ? SCL : 0);
         X.ks[k] = __builtin_amdgcn_raw_buffer_load_b32(rks, lane * 4, 0, 0);
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
                     float* vsf) {
     // scales of this step's pages -> this wave's LDS area -> one per row
     float ksf[ROWS];
-    if constexpr (QT != QT_BF16) {
+    if constexpr (qt_scaled(QT)) {
       uint8_t* sw = s_scl[wave];
 #pragma unroll
       for (int k = 0; k < PPS; ++k) {
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
         lsum[h] += pr;
         w[r][h] = ok[r] ? pr * vsf[r] : 0.0f;
       }
-    if constexpr (QT == QT_FP8 && ROWS % 2 == 0) {
+    if constexpr (qt_f8(QT) && ROWS % 2 == 0) {
       // two rows at a time: each element's two codes form one bf16 pair
       // (exact) and meet the two rows' weights (rounded to bf16) in a dot2
 #pragma unroll
@@ -430,8 +430,8 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
           const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
           const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
           uint32_t vp[4];
-          decode_dword_bf16x2<QT_FP8>(lo, vp);
-          decode_dword_bf16x2<QT_FP8>(hi, vp + 2);
+          decode_dword_bf16x2<QT>(lo, vp);
+          decode_dword_bf16x2<QT>(hi, vp + 2);
 #pragma unroll
           for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -768,6 +768,8 @@ hipError_t launch_gqa_decode(const DecodeArgs& a, const DecodePlan& plan, int nu
   switch (a.qtype) {
     case QT_BF16: e = launch_d<QT_BF16>(gp, (int)grid, s); break;
     case QT_FP8: e = launch_d<QT_FP8>(gp, (int)grid, s); break;
+    case QT_FP8C: e = launch_d<QT_FP8C>(gp, (int)grid, s); break;
+    case QT_BF8C: e = launch_d<QT_BF8C>(gp, (int)grid, s); break;
     default: e = launch_d<QT_Q8>(gp, (int)grid, s); break;
   }
   if (e != hipSuccess || plan.fused_merge) return e;

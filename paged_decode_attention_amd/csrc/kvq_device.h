@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kvq_internal.h"
+
 namespace kvq {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -40,6 +42,16 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
   o[3] = b.y;
 }
 
+// e5m2: the same through the bf8 conversion.
+__device__ __forceinline__ void bf8x4_to_f32(uint32_t w, float* o) {
+  f32x2 a = __builtin_amdgcn_cvt_pk_f32_bf8(w, false);
+  f32x2 b = __builtin_amdgcn_cvt_pk_f32_bf8(w, true);
+  o[0] = a.x;
+  o[1] = a.y;
+  o[2] = b.x;
+  o[3] = b.y;
+}
+
 // int8: sign-extend each byte.
 __device__ __forceinline__ void q8x4_to_f32(uint32_t w, float* o) {
   o[0] = (float)(int32_t)(int8_t)(w & 0xff);
@@ -50,15 +62,19 @@ __device__ __forceinline__ void q8x4_to_f32(uint32_t w, float* o) {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// Four 8-bit codes (or two bf16) -> bf16 pairs, exactly: e4m3 and int8 values
-// all fit bf16's 8-bit significand.  e4m3 uses the gfx950 scaled packed
-// conversion with scale 1.0; int8 goes through fp32.
+// Four 8-bit codes (or two bf16) -> bf16 pairs, exactly: e4m3, e5m2 and int8
+// values all fit bf16's 8-bit significand and exponent range.  e4m3 / e5m2
+// use the gfx950 scaled packed conversions with scale 1.0; int8 goes through
+// fp32.
 template <int QT>
 __device__ __forceinline__ void decode_dword_bf16x2(uint32_t w, uint32_t* o) {
-  if constexpr (QT == 1) {
+  if constexpr (QT == QT_FP8 || QT == QT_FP8C) {
     o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
     o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
-  } else if constexpr (QT == 2) {
+  } else if constexpr (QT == QT_BF8C) {
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true));
+  } else if constexpr (QT == QT_Q8) {
     float f[4];
     q8x4_to_f32(w, f);
     // |int8| <= 127 is exact in bf16: truncating the low 16 bits is exact
@@ -84,9 +100,11 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 template <int QT>
 __device__ __forceinline__ void decode_dword(uint32_t w, float* o) {
-  if constexpr (QT == 1) {
+  if constexpr (QT == QT_FP8 || QT == QT_FP8C) {
     fp8x4_to_f32(w, o);
-  } else if constexpr (QT == 2) {
+  } else if constexpr (QT == QT_BF8C) {
+    bf8x4_to_f32(w, o);
+  } else if constexpr (QT == QT_Q8) {
     q8x4_to_f32(w, o);
   } else {
     o[0] = bf16_lo(w);

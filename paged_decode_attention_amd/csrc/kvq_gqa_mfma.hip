@@ -90,7 +90,7 @@ struct MfGeo {
   static constexpr int KLD = (ESZ == 1) ? D / 64 : NKS;  // K loads per lane per page
   static constexpr int VDW = (D / 16) * ESZ / 4;  // dwords of a lane's V slice per token
   static constexpr int CODE = kPageSize * D * ESZ;
-  static constexpr int SCL = (QT == QT_BF16) ? 4 : kPageSize * NKS * 2;
+  static constexpr int SCL = qt_scaled(QT) ? kPageSize * NKS * 2 : 4;
 };
 
 template <int QT, int D>
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
       for (int m = 0; m < KLD; ++m) bload<4, kNonTemporal>(rk, koff + 64 * m, R.k[m]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) bload<VDW, kNonTemporal>(rv, voff + r * D * ESZ, R.v[r]);
-      if constexpr (QT != QT_BF16) {
+      if constexpr (qt_scaled(QT)) {
         const auto rks = page_rsrc(a.k_scales + row0 * NKS, pid >= 0 ? SCL : 0);
         const auto rvs = page_rsrc(a.v_scales + row0 * NKS, pid >= 0 ? SCL : 0);
         R.ks = __builtin_amdgcn_raw_buffer_load_b32(rks, ksoff, 0, 0);
@@ -268,6 +268,23 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
           S = mfma_k32(u32x4{R.k[ks][0], R.k[ks][1], R.k[ks][2], R.k[ks][3]}, qb[ks], S);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[r] = S[r];
+      } else if constexpr (!qt_scaled(QT)) {
+        // cast codes (no scales): one product chain over the k-steps, the
+        // codes handed to the lane groups as below
+        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int m = ks >> 1;
+          const auto x0 = __builtin_amdgcn_permlane32_swap(R.k[m][0], R.k[m][2], false, false);
+          const auto x1 = __builtin_amdgcn_permlane32_swap(R.k[m][1], R.k[m][3], false, false);
+          const uint32_t c0 = (ks & 1) ? x0[1] : x0[0], c1 = (ks & 1) ? x1[1] : x1[0];
+          uint32_t kb[4];
+          decode_dword_bf16x2<QT>(c0, kb);
+          decode_dword_bf16x2<QT>(c1, kb + 2);
+          S = mfma_k32(u32x4{kb[0], kb[1], kb[2], kb[3]}, qb[ks], S);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[r] = S[r];
       } else {
@@ -353,7 +370,7 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
         uint32_t w[4][VDW];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          sv[r] = f16_bits_to_f32((uint16_t)((R.vs[r] >> vshift) & keep[r]));
+          sv[r] = qt_scaled(QT) ? f16_bits_to_f32((uint16_t)((R.vs[r] >> vshift) & keep[r])) : 1.0f;
 #pragma unroll
           for (int k = 0; k < VDW; ++k) w[r][k] = R.v[r][k] & keep[r];
         }
@@ -364,10 +381,17 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
           transpose4x4(in, col);
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            float f[4];
-            decode_dword<QT>(col[c], f);
-            const u32x2 e = u32x2{pack_bf16x2(f[0] * sv[0], f[1] * sv[1]),
-                                  pack_bf16x2(f[2] * sv[2], f[3] * sv[3])};
+            u32x2 e;
+            if constexpr (qt_scaled(QT)) {
+              float f[4];
+              decode_dword<QT>(col[c], f);
+              e = u32x2{pack_bf16x2(f[0] * sv[0], f[1] * sv[1]),
+                        pack_bf16x2(f[2] * sv[2], f[3] * sv[3])};
+            } else {  // cast codes: exact bf16 pairs of tokens (0, 1) and (2, 3)
+              uint32_t pr2[2];
+              decode_dword_bf16x2<QT>(col[c], pr2);
+              e = u32x2{pr2[0], pr2[1]};
+            }
             acc[4 * k + c] = mfma_k16(e, pt, acc[4 * k + c]);
           }
         }
@@ -563,6 +587,8 @@ hipError_t launch_gqa_mfma_decode(const DecodeArgs& a, const DecodePlan& plan, i
   switch (a.qtype) {
     case QT_BF16: e = launch_q<QT_BF16>(mp, (int)grid, s); break;
     case QT_FP8: e = launch_q<QT_FP8>(mp, (int)grid, s); break;
+    case QT_FP8C: e = launch_q<QT_FP8C>(mp, (int)grid, s); break;
+    case QT_BF8C: e = launch_q<QT_BF8C>(mp, (int)grid, s); break;
     default: e = launch_q<QT_Q8>(mp, (int)grid, s); break;
   }
   if (e != hipSuccess || plan.fused_merge) return e;

@@ -7,7 +7,13 @@
 
 namespace kvq {
 
-enum { QT_BF16 = 0, QT_FP8 = 1, QT_Q8 = 2 };
+enum { QT_BF16 = 0, QT_FP8 = 1, QT_Q8 = 2, QT_FP8C = 3, QT_BF8C = 4 };
+// block-scaled 8-bit codes (a scale buffer beside the pool)
+__host__ __device__ constexpr bool qt_scaled(int qt) { return qt == QT_FP8 || qt == QT_Q8; }
+// 8-bit float codes (e4m3 or e5m2), block-scaled or cast
+__host__ __device__ constexpr bool qt_f8(int qt) {
+  return qt == QT_FP8 || qt == QT_FP8C || qt == QT_BF8C;
+}
 
 // Token rows per page supported by the decode kernels.
 constexpr int kPageSize = 16;
@@ -45,7 +51,7 @@ __host__ __device__ constexpr int gqa_code_bytes(int qtype, int d) {
   return kPageSize * d * gqa_elem_bytes(qtype);
 }
 __host__ __device__ constexpr int gqa_scale_bytes(int qtype, int d) {
-  return qtype == QT_BF16 ? 0 : kPageSize * (d / 32) * 2;
+  return qt_scaled(qtype) ? kPageSize * (d / 32) * 2 : 0;
 }
 constexpr int kGqaStepBytes = 8704;  // K and V bytes a wave loads per step (at least a page)
 constexpr int kGqaDepth = 2;         // steps in flight per wave, including the one computed

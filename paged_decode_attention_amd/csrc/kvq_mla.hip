@@ -203,6 +203,8 @@ template <int QT>
 __device__ __forceinline__ void dequant_dword(uint32_t w, float s, uint32_t* o) {
   if constexpr (QT == QT_BF16) {
     o[0] = w;
+  } else if constexpr (!qt_scaled(QT)) {  // cast codes: exact, no scale
+    decode_dword_bf16x2<QT>(w, o);
   } else {
     float f[4];
     decode_dword<QT>(w, f);
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) buf_load_dw<VW>(rc, vbase + i * ROWB, R.v[i]);
       buf_load_dw<RW>(rc, roff, R.r);
-      if constexpr (QT != QT_BF16) {
+      if constexpr (qt_scaled(QT)) {
         const auto rs = page_rsrc(a.k_scales + (int64_t)P * (SCLB / 2), SCLB);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         st.ok[i] = page_ok && (kTile * j + 4 * q + i < nt);
-        st.sv[i] = (QT == QT_BF16) ? 1.0f : scale_half(R.vs[i], ((u >> 1) & 1) * 16);
+        st.sv[i] = qt_scaled(QT) ? scale_half(R.vs[i], ((u >> 1) & 1) * 16) : 1.0f;
       }
       st.okr = page_ok && (kTile * j + rt < nt);
     };
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
         ds_write8<e * kVR * 2>(st.vb + (uint32_t)(h * 8 * kVR * 2), u32x2{w01, w23});
       } else {  // rope
         const int t = opaque(tid);
-        const float s = (QT == QT_BF16) ? 1.0f : scale_half(R.rs, ((t & 7) >> 2) * 16);
+        const float s = qt_scaled(QT) ? scale_half(R.rs, ((t & 7) >> 2) * 16) : 1.0f;
         uint32_t rw[4];
 #pragma unroll
         for (int k = 0; k < RW; ++k) dequant_dword<QT>(R.r[k], s, &rw[k * EPD]);
@@ -701,6 +703,8 @@ hipError_t launch_mla_decode(const DecodeArgs& a, const DecodePlan& plan, int nu
   switch (a.qtype) {
     case QT_BF16: return launch_q<QT_BF16>(mp, (int)grid, merge_grid, s);
     case QT_FP8: return launch_q<QT_FP8>(mp, (int)grid, merge_grid, s);
+    case QT_FP8C: return launch_q<QT_FP8C>(mp, (int)grid, merge_grid, s);
+    case QT_BF8C: return launch_q<QT_BF8C>(mp, (int)grid, merge_grid, s);
     default: return launch_q<QT_Q8>(mp, (int)grid, merge_grid, s);
   }
 }

@@ -12,6 +12,12 @@
 // same (token, head, block) are handled by the same lane, so a thread keeps
 // two independent 16-byte loads in flight.
 //
+// The cast types (a per-tensor scale of 1.0, [PR126] "Add fp8 KV-cache
+// quantization (--kv-dtype)" §How it works) take the same lanes without the
+// block max or a scale: each element is clamped to the format's largest
+// finite magnitude (448 e4m3, 57344 e5m2) and rounded to nearest even by the
+// packed e4m3 / e5m2 conversion.
+//
 // Rounding: the code is the round-to-nearest-even e4m3 value (hardware packed
 // conversion) or the half-away-from-zero integer (q8_0) of the clamped
 // quotient x / s, where the quotient is the correctly rounded fp32 one.  This
@@ -116,6 +122,29 @@ __global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs a, StoreGrid 
     if constexpr (QT == QT_BF16) {
       if (valid)
         *reinterpret_cast<uint4*>(a.pool[t] + (row * a.head_dim + blk * 32 + quarter * 8) * 2) = raw;
+    } else if constexpr (!qt_scaled(QT)) {
+      constexpr float M = (QT == QT_BF8C) ? 57344.0f : 448.0f;
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint32_t codes[2];
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          v[2 * i] = fminf(fmaxf(bf16_lo(w[2 * d + i]), -M), M);
+          v[2 * i + 1] = fminf(fmaxf(bf16_hi(w[2 * d + i]), -M), M);
+        }
+        if constexpr (QT == QT_BF8C) {
+          const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(v[0], v[1], 0, false);
+          codes[d] = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(v[2], v[3], lo, true);
+        } else {
+          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+          codes[d] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
+        }
+      }
+      if (valid)
+        *reinterpret_cast<uint2*>(a.pool[t] + row * a.head_dim + blk * 32 + quarter * 8) =
+            make_uint2(codes[0], codes[1]);
     } else {
       float x[8];
       const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -170,7 +199,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, Dequan
       outv = *reinterpret_cast<const uint4*>(a.pool + (row * a.head_dim + e8 * 8) * 2);
     } else {
       const uint2 raw = *reinterpret_cast<const uint2*>(a.pool + row * a.head_dim + e8 * 8);
-      const float s = f16_bits_to_f32(a.scales[row * (a.head_dim >> 5) + (e8 >> 2)]);
+      const float s =
+          qt_scaled(QT) ? f16_bits_to_f32(a.scales[row * (a.head_dim >> 5) + (e8 >> 2)]) : 1.0f;
       float x[8];
       decode_dword<QT>(raw.x, x);
       decode_dword<QT>(raw.y, x + 4);
@@ -210,6 +240,8 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t s) {
     switch (a.qtype) {
       case QT_BF16: store_kernel<QT_BF16><<<blocks, kThreads, 0, s>>>(sub, g); break;
       case QT_FP8: store_kernel<QT_FP8><<<blocks, kThreads, 0, s>>>(sub, g); break;
+      case QT_FP8C: store_kernel<QT_FP8C><<<blocks, kThreads, 0, s>>>(sub, g); break;
+      case QT_BF8C: store_kernel<QT_BF8C><<<blocks, kThreads, 0, s>>>(sub, g); break;
       default: store_kernel<QT_Q8><<<blocks, kThreads, 0, s>>>(sub, g); break;
     }
     hipError_t e = hipGetLastError();
@@ -237,6 +269,8 @@ hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {
     switch (a.qtype) {
       case QT_BF16: dequant_kernel<QT_BF16><<<blocks, kThreads, 0, s>>>(sub, g); break;
       case QT_FP8: dequant_kernel<QT_FP8><<<blocks, kThreads, 0, s>>>(sub, g); break;
+      case QT_FP8C: dequant_kernel<QT_FP8C><<<blocks, kThreads, 0, s>>>(sub, g); break;
+      case QT_BF8C: dequant_kernel<QT_BF8C><<<blocks, kThreads, 0, s>>>(sub, g); break;
       default: dequant_kernel<QT_Q8><<<blocks, kThreads, 0, s>>>(sub, g); break;
     }
     hipError_t e = hipGetLastError();

@@ -10,7 +10,8 @@ Tensor conventions (device tensors unless noted):
   pool    uint8 [num_pages, n_heads, page_size, head_dim] (8-bit codes) or
           bfloat16 of the same shape for dtype "bf16"
   scales  any 2-byte dtype [num_pages, n_heads, page_size, head_dim // 32]
-          holding IEEE fp16 bit patterns (None for "bf16")
+          holding IEEE fp16 bit patterns (None for "bf16" and the cast types
+          "fp8_e4m3_cast" / "fp8_e5m2_cast", which store each element itself)
   q       bfloat16 [batch, n_q_heads, head_dim_qk]
   page_table int32 [batch, max_pages] (-1 = masked), seq_lens int32 [batch]
 """
@@ -24,7 +25,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
-DTYPES = {"bf16": 0, "fp8_e4m3": 1, "q8_0": 2}
+DTYPES = {"bf16": 0, "fp8_e4m3": 1, "q8_0": 2, "fp8_e4m3_cast": 3, "fp8_e5m2_cast": 4}
+SCALED = ("fp8_e4m3", "q8_0")  # storage types with a scale buffer
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
 
@@ -129,6 +131,9 @@ def alloc_pool(dtype, num_pages: int, n_heads: int, head_dim: int, page_size: in
         return pool, None
     pool = torch.empty((num_pages, n_heads, page_size, head_dim), dtype=torch.uint8,
                        device=device)
+    if sb == 0:  # the cast types: no scale buffer
+        assert pool.numel() == cb
+        return pool, None
     scales = torch.empty((num_pages, n_heads, page_size, head_dim // 32), dtype=torch.int16,
                          device=device)
     assert pool.numel() == cb and scales.numel() * 2 == sb

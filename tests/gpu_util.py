@@ -48,14 +48,18 @@ def host_u16(t: torch.Tensor) -> np.ndarray:
 def np_pool(qtype, num_pages, H, D, fill_code=0, fill_scale=0):
     if qtype == "bf16":
         return np.full((num_pages, H, W.PAGE, D), fill_scale, np.uint16), None
-    return (np.full((num_pages, H, W.PAGE, D), fill_code, np.uint8),
-            np.full((num_pages, H, W.PAGE, D // 32), fill_scale, np.uint16))
+    codes = np.full((num_pages, H, W.PAGE, D), fill_code, np.uint8)
+    if qtype not in oracle.SCALED:  # the cast types: no scale buffer
+        return codes, None
+    return codes, np.full((num_pages, H, W.PAGE, D // 32), fill_scale, np.uint16)
 
 
 def gpu_pool_from(np_pool_arr, np_scales):
     """Upload oracle-layout pool arrays (used for poison fills)."""
     if np_pool_arr.dtype == np.uint16:
         return dev_bf16(np_pool_arr), None
+    if np_scales is None:
+        return torch.from_numpy(np_pool_arr).cuda(), None
     return (torch.from_numpy(np_pool_arr).cuda(),
             torch.from_numpy(np_scales.view(np.int16)).cuda())
 

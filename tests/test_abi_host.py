@@ -51,7 +51,7 @@ def test_pool_bytes_is_17_16_per_element_and_32_17_vs_bf16():
     assert abs(budget // per_tok - FACTS["pool_tokens_8bit"]) < 16
 
 
-@pytest.mark.parametrize("dtype", ["fp8_e4m3", "q8_0"])
+@pytest.mark.parametrize("dtype", ["fp8_e4m3", "q8_0", "fp8_e4m3_cast", "fp8_e5m2_cast"])
 def test_head_dim_not_multiple_of_32_is_rejected_up_front(dtype):
     with pytest.raises(ValueError, match="multiple of"):
         kvq.pool_bytes(dtype, 4, 16, 1, 48)
@@ -117,3 +117,19 @@ def test_python_errors_are_typed():
         kvq.pool_bytes("int4", 1, 16, 1, 32)
     with pytest.raises(NotImplementedError):
         kvq.workspace_bytes("fp8_e4m3", 1, 8, 1, 64, 64, 8, 4)
+
+
+def test_only_block_scaled_types_carry_scales():
+    """Scale bytes: 2 per 32 elements for the block-scaled types, none for
+    bf16 and the cast types [PR126 "Add fp8 KV-cache quantization
+    (--kv-dtype)" §How it works: scale 1.0]; a block-scaled store without a
+    scale buffer is rejected before any launch."""
+    for dtype, code_b, scale_b in (("fp8_e4m3", 1, 2 / 32), ("q8_0", 1, 2 / 32), ("bf16", 2, 0),
+                                   ("fp8_e4m3_cast", 1, 0), ("fp8_e5m2_cast", 1, 0)):
+        total, codes, scales = kvq.pool_bytes(dtype, 10, 16, 4, 128)
+        n = 10 * 16 * 4 * 128
+        assert codes == code_b * n and scales == scale_b * n and total == codes + scales
+    for dtype in ("fp8_e4m3", "q8_0"):
+        rc = kvq.LIB.kvq_store(kvq.DTYPES[dtype], 16, None, 128, 16, 4, 1, 128, 16, 4, 16, None,
+                               None, None, None)
+        assert rc == kvq.ERR_ARG and "k_scales" in kvq.last_error()

@@ -56,7 +56,7 @@ def check(wl, qtype, rows=None, tol=TOL):
     return g_out, pools
 
 
-@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0", "bf16"])
+@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0", "bf16", "fp8_e4m3_cast", "fp8_e5m2_cast"])
 @pytest.mark.parametrize("D,Hq,Hkv", [(32, 4, 4), (64, 8, 2), (128, 16, 8), (128, 8, 1),
                                       (256, 16, 2), (128, 12, 2), (64, 6, 2),
                                       # 8+ query heads per kv head: the matrix-core kernel
@@ -163,9 +163,10 @@ def test_tiny_workload_all_rows(qtype):
     check(W.tiny(), qtype)
 
 
-def test_qwen3_workload_sampled_rows():
+@pytest.mark.parametrize("qtype", ["fp8_e4m3", "fp8_e4m3_cast", "fp8_e5m2_cast"])
+def test_qwen3_workload_sampled_rows(qtype):
     wl = W.qwen3(replicas=1)
-    check(wl, "fp8_e4m3", rows=sample_rows(wl, 3, np.random.default_rng(1)))
+    check(wl, qtype, rows=sample_rows(wl, 3, np.random.default_rng(1)))
 
 
 @pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0"])

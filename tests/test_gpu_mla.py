@@ -58,7 +58,7 @@ def check(wl, qtype, rows=None, tol=TOL):
     return g_out, pools
 
 
-@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0", "bf16"])
+@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0", "bf16", "fp8_e4m3_cast", "fp8_e5m2_cast"])
 @pytest.mark.parametrize("Hq", [128, 64, 16])
 def test_mla_small_matches_oracle(qtype, Hq):
     """Ragged lengths around the page (16) and tile (32) edges, masked pages,

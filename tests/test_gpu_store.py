@@ -19,6 +19,7 @@ from tests.gpu_util import (dev_bf16, dev_i32, host_u16, host_u8, kvq, np_pool, 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
 QT8 = ["fp8_e4m3", "q8_0"]
+CASTS = ["fp8_e4m3_cast", "fp8_e5m2_cast"]
 
 
 def tricky_rows(rng, n, H, D):
@@ -53,7 +54,7 @@ def tricky_rows(rng, n, H, D):
     return bits
 
 
-@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0", "bf16"])
+@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0", "bf16"] + CASTS)
 @pytest.mark.parametrize("H,D", [(1, 32), (2, 64), (8, 128), (2, 256), (1, 576), (3, 96)])
 def test_store_bitexact(qtype, H, D):
     rng = np.random.default_rng(1000 + D + H)
@@ -70,7 +71,8 @@ def test_store_bitexact(qtype, H, D):
         kp.view(torch.int16).fill_(0x5A5A)
     else:
         kp.fill_(0xA5)
-        ks.fill_(0x5A5A)
+        if ks is not None:
+            ks.fill_(0x5A5A)
     say("store_bitexact", qtype, H, D)
     k.store(qtype, dev_bf16(src), None, dev_i32(slots), kp, ks)
     torch.cuda.synchronize()
@@ -78,11 +80,15 @@ def test_store_bitexact(qtype, H, D):
     if qtype == "bf16":
         assert np.array_equal(host_u16(kp), okp)
     else:
-        got_c, got_s = host_u8(kp), host_u16(ks)
+        got_c = host_u8(kp)
+        got_s = host_u16(ks) if ks is not None else None
         bad = np.nonzero(got_c != okp)
         assert bad[0].size == 0, "first code mismatch at %s: gpu %#x oracle %#x" % (
             [int(b[0]) for b in bad], got_c[bad][0], okp[bad][0])
-        assert np.array_equal(got_s, oks)
+        if oks is not None:
+            assert np.array_equal(got_s, oks)
+        else:
+            assert ks is None
 
 
 @pytest.mark.parametrize("qtype", QT8)
@@ -146,7 +152,7 @@ def test_store_every_bf16_pair_over_the_scale_range(qtype):
     assert np.array_equal(host_u16(ks).reshape(-1)[:n], oks.reshape(-1)[:n])
 
 
-@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0", "bf16"])
+@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0", "bf16"] + CASTS)
 def test_dequant_bitexact(qtype):
     rng = np.random.default_rng(88)
     H, D, n_pages = 2, 128, 30
@@ -195,3 +201,58 @@ def test_store_mixed_workload_full_size(qtype):
         assert np.array_equal(host_u16(gs.index_select(0, idx)), oks)
         other = torch.from_numpy(np.setdiff1d(np.arange(0, wl.num_pages, 97), pages)).cuda()
         assert bool((gp.index_select(0, other) == 0x3C).all())
+
+
+@pytest.mark.parametrize("qtype", CASTS)
+def test_cast_store_of_every_bf16_value(qtype):
+    """Every finite bf16 pattern (in range, saturating and both zeros), K and
+    V in one call, against the oracle's cast: bit-exact codes, no scales
+    [PR126 "Add fp8 KV-cache quantization (--kv-dtype)" §How it works]."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = (bits.astype(np.uint32) << 16).view(np.float32)
+    bits = bits[np.isfinite(f)]
+    bits = np.concatenate([bits, np.zeros((-len(bits)) % 32, np.uint16)])
+    src = bits.reshape(-1, 1, 32)
+    srcv = np.ascontiguousarray(src[::-1])
+    n = src.shape[0]
+    n_pages = (n + W.PAGE - 1) // W.PAGE
+    slots = np.arange(n, dtype=np.int32)
+    k = kvq()
+    kp, ks = k.alloc_pool(qtype, n_pages, 1, 32)
+    vp, vs = k.alloc_pool(qtype, n_pages, 1, 32)
+    assert ks is None and vs is None
+    say("cast_store_exhaustive", qtype, "rows", n)
+    k.store(qtype, dev_bf16(src), dev_bf16(srcv), dev_i32(slots), kp, None, vp, None)
+    torch.cuda.synchronize()
+    for gp, s in ((kp, src), (vp, srcv)):
+        okp, _ = np_pool(qtype, n_pages, 1, 32)
+        oracle.store(qtype, s, slots, 1, 32, W.PAGE, n_pages, okp, None)
+        got = host_u8(gp).reshape(-1, 32)[:n]
+        exp = okp.reshape(-1, 32)[:n]
+        bad = np.nonzero(got != exp)
+        if bad[0].size:
+            r, c = bad[0][0], bad[1][0]
+            pytest.fail("%d mismatches; first: x %#06x gpu %#04x oracle %#04x" % (
+                bad[0].size, s[r, 0, c], got[r, c], exp[r, c]))
+
+
+@pytest.mark.parametrize("qtype", CASTS)
+def test_cast_dequant_of_every_code(qtype):
+    """All 256 codes in a pool (NaN codes of the format excluded) read back
+    through kvq_dequant as the oracle's exact values in bf16."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = np.array([oracle.e5m2_value(int(c)) if qtype == "fp8_e5m2_cast" else
+                     oracle.e4m3_value(int(c)) for c in codes])
+    codes = codes[np.isfinite(vals)]
+    codes = np.concatenate([codes, np.zeros((-len(codes)) % 32, np.uint8)])
+    n = len(codes) // 32
+    pool = np.zeros(((n + W.PAGE - 1) // W.PAGE, 1, W.PAGE, 32), np.uint8)
+    pool.reshape(-1, 32)[:n] = codes.reshape(n, 32)
+    n_pages = pool.shape[0]
+    slots = np.arange(n, dtype=np.int32)
+    k = kvq()
+    say("cast_dequant_codes", qtype)
+    out = k.dequant(qtype, torch.from_numpy(pool).cuda(), None, dev_i32(slots))
+    torch.cuda.synchronize()
+    _, ob = oracle.dequant(qtype, pool, None, slots, 1, 32, W.PAGE, n_pages)
+    assert np.array_equal(host_u16(out), ob)

@@ -46,6 +46,14 @@ MUTANTS = [
     ("lse without log", "c->lse[i] = zmax + log(denom);", "c->lse[i] = zmax + denom;"),
     ("bf16 fraction bits", "double r = round_to_grid(fabs(x), 7, -126);",
      "double r = round_to_grid(fabs(x), 8, -126);"),
+    ("e5m2 exponent bias 16", "v = ldexp(1.0 + m / 4.0, e - 15);", "v = ldexp(1.0 + m / 4.0, e - 16);"),
+    ("e5m2 maximum 61440", "#define KVO_E5M2_MAX 57344.0f", "#define KVO_E5M2_MAX 61440.0f"),
+    ("e5m2 three fraction bits", "double r = round_to_grid(fabs((double)v), 2, -14);",
+     "double r = round_to_grid(fabs((double)v), 3, -14);"),
+    ("cast without the clamp", "  if (x > M) x = M;\n  if (x < -M) x = -M;", ""),
+    ("cast formats swapped",
+     "return (qtype == KVO_FP8_E5M2_CAST) ? kvo_e5m2_encode(x) : kvo_e4m3_encode(x);",
+     "return (qtype == KVO_FP8_E5M2_CAST) ? kvo_e4m3_encode(x) : kvo_e5m2_encode(x);"),
 ]
 
 
@@ -62,7 +70,8 @@ def _run_mutant(case):
                     "-w", "-o", so, c_path, "-lm"], check=True)
     env = dict(os.environ, KVQ_ORACLE_LIB=so, OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py", "tests/test_oracle_attention_pins.py"],
+                        "tests/test_oracle_pins.py", "tests/test_oracle_attention_pins.py",
+                        "tests/test_oracle_cast_pins.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
     return name, r.returncode
 
