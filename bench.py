@@ -131,7 +131,8 @@ def write_traffic(src_dir):
 
 
 def store_bytes(n_tokens, n_heads, head_dim, qtype, tensors=2):
-    per = {"bf16": 2.0, "fp8_e4m3": 1 + 1 / 16, "q8_0": 1 + 1 / 16}[qtype]
+    per = {"bf16": 2.0, "fp8_e4m3": 1 + 1 / 16, "q8_0": 1 + 1 / 16, "fp8_e4m3_cast": 1.0,
+           "fp8_e5m2_cast": 1.0}[qtype]
     return int(tensors * n_tokens * n_heads * head_dim * (2 + per)) + 4 * n_tokens
 
 
@@ -152,7 +153,8 @@ def cpu_baseline(wl, qtype, k_rows, v_rows, q_bits):
     code_t = np.uint16 if qtype == "bf16" else np.uint8
     kp = np.zeros((wl.num_pages, H, W.PAGE, D), code_t)
     vp = np.zeros_like(kp)
-    ks = None if qtype == "bf16" else np.zeros((wl.num_pages, H, W.PAGE, D // 32), np.uint16)
+    ks = (np.zeros((wl.num_pages, H, W.PAGE, D // 32), np.uint16) if qtype in oracle.SCALED
+          else None)
     vs = None if ks is None else np.zeros_like(ks)
     t0 = time.perf_counter()
     oracle.store(qtype, k_rows, slots, H, D, W.PAGE, wl.num_pages, kp, ks, threads=threads)
@@ -284,7 +286,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--qtype", default="fp8_e4m3", choices=["fp8_e4m3", "q8_0", "bf16"])
+    ap.add_argument("--qtype", default="fp8_e4m3",
+                    choices=["fp8_e4m3", "q8_0", "bf16", "fp8_e4m3_cast", "fp8_e5m2_cast"])
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="qwen3",
@@ -490,7 +493,8 @@ def main() -> int:
                         "x %d-token contexts, %d q / %d kv heads, head_dim %d, page 16, "
                         "random-permutation page tables (%s)" % (L, B, int(wl.seq_lens[0]),
                                                                  wl.n_q_heads, H, D, wl.name),
-            "kv_storage": qtype + ("" if qtype == "bf16" else ", fp16 scale per 32 elements"),
+            "kv_storage": qtype + (", fp16 scale per 32 elements" if qtype in ("fp8_e4m3", "q8_0")
+                                   else "" if qtype == "bf16" else ", per-tensor scale 1.0"),
             "layers": L,
             "batch": B,
             "context": int(wl.seq_lens[0]),
@@ -511,7 +515,7 @@ def main() -> int:
                   "per_step_store_of_8_tokens_us": round(st_avg * 1e3, 3)},
         "roofline": {
             "bound": "hbm",
-            "kernel": "gqa_decode_kernel<fp8_e4m3, 128, 2> (one launch per kvq_paged_decode)",
+            "kernel": "gqa_decode_kernel<%s, 128, 2> (one launch per kvq_paged_decode)" % qtype,
             "achieved": round(achieved, 2),
             "peak": PEAK_GBPS,
             "unit": "GB/s",

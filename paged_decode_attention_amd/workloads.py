@@ -145,7 +145,8 @@ class Workload:
         every kv head (K and V, or the one shared row), Q, O, the page-table
         entries walked and seq_lens.  Masked pages are not counted."""
         D, Dv = self.head_dim_qk, self.head_dim_v
-        per = {"bf16": 2.0, "fp8_e4m3": 17 / 16, "q8_0": 17 / 16}[qtype]
+        per = {"bf16": 2.0, "fp8_e4m3": 17 / 16, "q8_0": 17 / 16, "fp8_e4m3_cast": 1.0,
+               "fp8_e5m2_cast": 1.0}[qtype]
         n_valid = 0
         for b in range(self.batch):
             L = min(int(self.seq_lens[b]), self.max_pages * PAGE)
