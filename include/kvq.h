@@ -201,6 +201,50 @@ int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
                      void* out_bf16, float* lse, void* workspace, size_t workspace_bytes,
                      kvq_stream_t stream);
 
+/* Workspace bytes kvq_sparse_mla_decode needs: the gathered rows of every
+ * list (codes and scales), their page table and lengths, and the split-K
+ * partials of the slab decode over them.  0 if the shapes are invalid (see
+ * kvq_sparse_mla_decode).  Host-only. */
+size_t kvq_sparse_mla_decode_workspace_bytes(kvq_dtype dtype, int batch, int n_q_heads,
+                                             int topk);
+
+/* Sparse top-k decode over the shared MLA slab [PR25 "Experimental FP8 KV
+ * Cache": SPARSE_MLA_DECODE, D=576 Hq=128 Hkv=1 Dv=512, K=256 tokens selected
+ * out of the cache for each query; PR113 "feat(kvcache): 8-bit DSV4
+ * window/compressed KV behind --kv-cache-dtype" §What this adds (one slab, K
+ * and V the same row), §Testing (masked (-1) columns)].
+ *
+ * Sequence b attends only to the tokens listed in topk_idx[b][0 .. topk):
+ * token positions within the sequence, read through the page table as in
+ * kvq_paged_decode.  An entry is taken when 0 <= t < seq_lens[b] (clamped to
+ * max_pages * page_size) and its page id lies in [0, num_pages); any other
+ * entry (-1 pads a short list) is skipped.  Taken entries count as listed (a
+ * position listed twice counts twice).  With k_t the taken rows and v_t their
+ * first 512 elements:
+ *     z_t = sm_scale * q[b][h] . k_t,  out[b][h] = sum_t softmax(z)_t v_t,
+ *     lse[b][h] = log sum_t exp(z_t);  no entry taken: out = 0, lse = -inf.
+ *
+ *   q         : device bf16 [batch][n_q_heads][576], 16-byte aligned.
+ *   slab, scales : device, the pool layout above with n_heads = 1 and
+ *               head_dim = 576 (scales ignored, may be NULL, for KVQ_BF16 and
+ *               the cast types).
+ *   topk_idx  : device int32 [batch][topk_stride], topk_stride >= topk.
+ *   page_table, seq_lens, out_bf16 ([batch][n_q_heads][512]), lse: as
+ *               kvq_paged_decode.
+ *   workspace : device, >= kvq_sparse_mla_decode_workspace_bytes(), 256-byte
+ *               aligned; overwritten by every call (no zeroing needed).
+ * Supported: topk 1..2048, n_q_heads a multiple of 16 up to 128, batch up to
+ * 1024, page_size 16.  The listed rows are gathered into the workspace (codes
+ * moved unchanged) and attended to by the slab decode.  Errors: KVQ_ERR_ARG,
+ * KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP; validation completes
+ * before any launch. */
+int kvq_sparse_mla_decode(kvq_dtype dtype, const void* q, const void* slab,
+                          const uint16_t* scales, const int32_t* page_table, int64_t pt_stride,
+                          const int32_t* seq_lens, const int32_t* topk_idx, int64_t topk_stride,
+                          int topk, int batch, int n_q_heads, int page_size, int max_pages,
+                          int64_t num_pages, float sm_scale, void* out_bf16, float* lse,
+                          void* workspace, size_t workspace_bytes, kvq_stream_t stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* kvq_last_error(void);
 

@@ -95,6 +95,10 @@ def _declare(L):
     L.kvo_e4m3_encode_array.restype = None
     L.kvo_q8_encode_array.argtypes = [P, c.c_int64, P]
     L.kvo_q8_encode_array.restype = None
+    L.kvo_sparse_mla_decode.argtypes = [c.c_int, P, P, P, P, c.c_int64, P, P, c.c_int64, c.c_int,
+                                        c.c_int, c.c_int, c.c_int, c.c_int, c.c_int, c.c_int,
+                                        c.c_int64, c.c_double, P, P, c.c_int]
+    L.kvo_sparse_mla_decode.restype = None
     L.kvo_e5m2_value.argtypes = [c.c_uint8]
     L.kvo_e5m2_value.restype = c.c_double
     L.kvo_e5m2_encode.argtypes = [c.c_float]
@@ -228,4 +232,26 @@ def paged_decode(qtype, q_bf16: np.ndarray, k_pool: np.ndarray, k_scales, v_pool
                            B, Hq, n_kv_heads, head_dim_qk, head_dim_v, page_size, pt.shape[1],
                            num_pages, float(sm_scale), _ptr(rows_a), n_rows, _ptr(out),
                            _ptr(lse), threads or default_threads())
+    return out, lse
+
+
+def sparse_mla_decode(qtype, q_bf16: np.ndarray, slab: np.ndarray, scales, page_table: np.ndarray,
+                      seq_lens: np.ndarray, topk: np.ndarray, head_dim_qk: int, head_dim_v: int,
+                      page_size: int, num_pages: int, sm_scale: float,
+                      threads: int | None = None):
+    """Sparse top-k decode over the shared slab, in double.  topk: int32
+    [B][k] token positions (-1 = padding).  Returns (out float64 [B*Hq][Dv],
+    lse float64 [B*Hq])."""
+    q = np.ascontiguousarray(q_bf16, dtype=np.uint16)
+    B, Hq = q.shape[0], q.shape[1]
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    tk = np.ascontiguousarray(topk, dtype=np.int32)
+    out = np.empty((B * Hq, head_dim_v), dtype=np.float64)
+    lse = np.empty(B * Hq, dtype=np.float64)
+    lib().kvo_sparse_mla_decode(_qt(qtype), _ptr(q), _ptr(slab), _ptr(scales), _ptr(pt),
+                                pt.shape[1], _ptr(sl), _ptr(tk), tk.shape[1], tk.shape[1], B, Hq,
+                                head_dim_qk, head_dim_v, page_size, pt.shape[1], num_pages,
+                                float(sm_scale), _ptr(out), _ptr(lse),
+                                threads or default_threads())
     return out, lse

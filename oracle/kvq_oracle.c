@@ -511,6 +511,97 @@ void kvo_paged_decode(int qtype, const uint16_t* q, const uint8_t* k_pool,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Sparse top-k decode over the shared MLA slab.                              */
+/* ------------------------------------------------------------------------ */
+/* Sequence b attends only to the tokens listed in topk[b][0..k): positions
+ * within the sequence, read through the page table [PR25 "Experimental FP8
+ * KV Cache": SPARSE_MLA_DECODE D=576 Hq=128 Hkv=1 Dv=512 K=256].  An entry is
+ * taken when 0 <= t < seq_len (clamped to max_pages * page_size) and its page
+ * id is in [0, num_pages); other entries (-1 pads a list) are skipped [PR113
+ * §Testing: masked (-1) columns].  Taken entries count as listed (a position
+ * listed twice counts twice).  K is the whole row, V its first head_dim_v
+ * elements; scores, softmax and the weighted sum in double, as above. */
+
+typedef struct {
+  int qtype;
+  const uint16_t* q;
+  const uint8_t* slab;
+  const uint16_t* scales;
+  const int32_t* page_table;
+  int64_t pt_stride;
+  const int32_t* seq_lens;
+  const int32_t* topk;
+  int64_t topk_stride;
+  int k, n_q_heads, head_dim_qk, head_dim_v, page_size, max_pages;
+  int64_t num_pages;
+  double sm_scale;
+  double* out;
+  double* lse;
+} kvo_sparse_ctx;
+
+static void kvo_sparse_unit(void* p, int64_t row) {
+  kvo_sparse_ctx* c = (kvo_sparse_ctx*)p;
+  int b = (int)(row / c->n_q_heads);
+  int64_t L = c->seq_lens[b];
+  int64_t cap = (int64_t)c->max_pages * c->page_size;
+  if (L > cap) L = cap;
+  if (L < 0) L = 0;
+  const uint16_t* qrow = c->q + row * (int64_t)c->head_dim_qk;
+  int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(c->k > 0 ? c->k : 1));
+  double* z = (double*)malloc(sizeof(double) * (size_t)(c->k > 0 ? c->k : 1));
+  int n = 0;
+  double zmax = -INFINITY;
+  for (int i = 0; i < c->k; ++i) {
+    int64_t t = c->topk[(int64_t)b * c->topk_stride + i];
+    if (t < 0 || t >= L) continue;
+    int64_t page = c->page_table[(int64_t)b * c->pt_stride + t / c->page_size];
+    if (page < 0 || page >= c->num_pages) continue;
+    int64_t r = page * c->page_size + t % c->page_size; /* one kv head */
+    double dot = 0.0;
+    for (int d = 0; d < c->head_dim_qk; ++d)
+      dot += kvo_bf16_value(qrow[d]) *
+             kvo_pool_value(c->qtype, c->slab, c->scales, r, c->head_dim_qk, d);
+    rows[n] = r;
+    z[n] = c->sm_scale * dot;
+    if (z[n] > zmax) zmax = z[n];
+    ++n;
+  }
+  double* o = c->out + row * (int64_t)c->head_dim_v;
+  for (int d = 0; d < c->head_dim_v; ++d) o[d] = 0.0;
+  if (n == 0) {
+    if (c->lse) c->lse[row] = -INFINITY;
+    free(rows);
+    free(z);
+    return;
+  }
+  double denom = 0.0;
+  for (int j = 0; j < n; ++j) {
+    double w = exp(z[j] - zmax);
+    denom += w;
+    for (int d = 0; d < c->head_dim_v; ++d)
+      o[d] += w * kvo_pool_value(c->qtype, c->slab, c->scales, rows[j], c->head_dim_qk, d);
+  }
+  for (int d = 0; d < c->head_dim_v; ++d) o[d] /= denom;
+  if (c->lse) c->lse[row] = zmax + log(denom);
+  free(rows);
+  free(z);
+}
+
+/* out: double [batch * n_q_heads][head_dim_v]; lse: double [batch * n_q_heads] or NULL. */
+void kvo_sparse_mla_decode(int qtype, const uint16_t* q, const uint8_t* slab,
+                           const uint16_t* scales, const int32_t* page_table, int64_t pt_stride,
+                           const int32_t* seq_lens, const int32_t* topk, int64_t topk_stride,
+                           int k, int batch, int n_q_heads, int head_dim_qk, int head_dim_v,
+                           int page_size, int max_pages, int64_t num_pages, double sm_scale,
+                           double* out, double* lse, int threads) {
+  kvo_sparse_ctx c = {qtype,      q,           slab,      scales,    page_table, pt_stride,
+                      seq_lens,   topk,        topk_stride, k,       n_q_heads,  head_dim_qk,
+                      head_dim_v, page_size,   max_pages, num_pages, sm_scale,   out,
+                      lse};
+  kvo_parallel_for((int64_t)batch * n_q_heads, threads, kvo_sparse_unit, &c);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Bulk helpers for tests: apply the scalar encoders to arrays.               */
 /* ------------------------------------------------------------------------ */
 

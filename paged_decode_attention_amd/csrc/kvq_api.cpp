@@ -202,6 +202,31 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
   return true;
 }
 
+bool plan_sparse(int qtype, int batch, int n_q_heads, int k, SparseLayout* lay,
+                 const char** why) {
+  static thread_local char msg[256];
+  if (k < 1 || k > kSparseMaxK) {
+    snprintf(msg, sizeof msg, "top-k count %d outside 1..%d", k, kSparseMaxK);
+    *why = msg;
+    return false;
+  }
+  SparseLayout L{};
+  L.kk = (k + kPageSize - 1) / kPageSize * kPageSize;
+  const int gpages = L.kk / kPageSize;
+  if (!plan_decode(qtype, batch, n_q_heads, 1, kMlaDqk, kMlaDv, kPageSize, gpages, &L.dense, why))
+    return false;
+  L.row_bytes = kMlaDqk * (qtype == KVQ_BF16 ? 2 : 1);
+  const size_t rows = (size_t)batch * L.kk;
+  L.off_dense = 0;
+  L.off_slab = align256(L.dense.bytes);
+  L.off_scales = L.off_slab + align256(rows * L.row_bytes);
+  L.off_pt = L.off_scales + align256(scaled(qtype) ? rows * (kMlaDqk / KVQ_BLOCK) * 2 : 0);
+  L.off_len = L.off_pt + align256((size_t)batch * gpages * sizeof(int32_t));
+  L.bytes = L.off_len + align256((size_t)batch * sizeof(int32_t));
+  *lay = L;
+  return true;
+}
+
 }  // namespace kvq
 
 extern "C" {
@@ -383,6 +408,98 @@ int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
                  : plan.mfma                 ? kvq::launch_gqa_mfma_decode(a, plan, cus, stream)
                                              : kvq::launch_gqa_decode(a, plan, cus, stream);
   if (e != hipSuccess) return hip_fail(e, "kvq_paged_decode");
+  return ok();
+}
+
+size_t kvq_sparse_mla_decode_workspace_bytes(kvq_dtype dtype, int batch, int n_q_heads,
+                                             int topk) {
+  kvq::SparseLayout lay;
+  const char* why = nullptr;
+  if (!kvq::plan_sparse(dtype, batch, n_q_heads, topk, &lay, &why)) {
+    fail(KVQ_ERR_UNSUPPORTED, "kvq_sparse_mla_decode_workspace_bytes: %s", why);
+    return 0;
+  }
+  g_err.clear();
+  return lay.bytes;
+}
+
+int kvq_sparse_mla_decode(kvq_dtype dtype, const void* q, const void* slab,
+                          const uint16_t* scales, const int32_t* page_table, int64_t pt_stride,
+                          const int32_t* seq_lens, const int32_t* topk_idx, int64_t topk_stride,
+                          int topk, int batch, int n_q_heads, int page_size, int max_pages,
+                          int64_t num_pages, float sm_scale, void* out_bf16, float* lse,
+                          void* workspace, size_t workspace_bytes, kvq_stream_t stream) {
+  if (!known_dtype(dtype))
+    return fail(KVQ_ERR_ARG, "kvq_sparse_mla_decode: unknown dtype %d", dtype);
+  if (batch < 1 || n_q_heads < 1 || max_pages < 1 || page_size < 1 || topk < 1)
+    return fail(KVQ_ERR_ARG, "kvq_sparse_mla_decode: sizes must be >= 1");
+  if (topk_stride < topk)
+    return fail(KVQ_ERR_ARG, "kvq_sparse_mla_decode: topk_stride %lld < topk %d",
+                (long long)topk_stride, topk);
+  if (pt_stride < max_pages)
+    return fail(KVQ_ERR_ARG, "kvq_sparse_mla_decode: pt_stride %lld < max_pages %d",
+                (long long)pt_stride, max_pages);
+  if (page_size != kvq::kPageSize)
+    return fail(KVQ_ERR_UNSUPPORTED, "kvq_sparse_mla_decode: page_size %d is not supported",
+                page_size);
+  if (num_pages < 1 || num_pages * (int64_t)page_size > INT32_MAX)
+    return fail(KVQ_ERR_ARG, "kvq_sparse_mla_decode: num_pages must be in 1..2^31/page_size");
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
+    return fail(KVQ_ERR_ARG, "kvq_sparse_mla_decode: sm_scale is not finite");
+  if (!q || !slab || !page_table || !seq_lens || !topk_idx || !out_bf16 ||
+      (scaled(dtype) && !scales))
+    return fail(KVQ_ERR_ARG, "kvq_sparse_mla_decode: null pointer");
+  if (!aligned(q, 16) || !aligned(slab, 16) || !aligned(out_bf16, 4) ||
+      (scaled(dtype) && !aligned(scales, 4)))
+    return fail(KVQ_ERR_ARG, "kvq_sparse_mla_decode: q and slab must be 16-byte aligned, "
+                             "scales 4-byte aligned");
+  kvq::SparseLayout lay;
+  const char* why = nullptr;
+  if (!kvq::plan_sparse(dtype, batch, n_q_heads, topk, &lay, &why))
+    return fail(KVQ_ERR_UNSUPPORTED, "kvq_sparse_mla_decode: %s", why);
+  if (!workspace || workspace_bytes < lay.bytes)
+    return fail(KVQ_ERR_WORKSPACE, "kvq_sparse_mla_decode: workspace of %zu bytes needed, %zu given",
+                lay.bytes, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256))
+    return fail(KVQ_ERR_WORKSPACE, "kvq_sparse_mla_decode: workspace must be 256-byte aligned");
+  kvq::SparseArgs s;
+  s.topk = topk_idx;
+  s.topk_stride = topk_stride;
+  s.k = topk;
+  s.page_table = page_table;
+  s.pt_stride = pt_stride;
+  s.seq_lens = seq_lens;
+  s.max_pages = max_pages;
+  s.num_pages = num_pages;
+  s.slab = static_cast<const uint8_t*>(slab);
+  s.scales = scaled(dtype) ? scales : nullptr;
+  s.workspace = workspace;
+  hipError_t e = kvq::launch_sparse_gather(s, lay, batch, stream);
+  if (e != hipSuccess) return hip_fail(e, "kvq_sparse_mla_decode");
+  char* ws = static_cast<char*>(workspace);
+  const int gpages = lay.kk / kvq::kPageSize;
+  kvq::DecodeArgs a;
+  a.qtype = dtype;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = a.v_pool = reinterpret_cast<const uint8_t*>(ws + lay.off_slab);
+  a.k_scales = a.v_scales = scaled(dtype) ? reinterpret_cast<const uint16_t*>(ws + lay.off_scales)
+                                          : nullptr;
+  a.page_table = reinterpret_cast<const int32_t*>(ws + lay.off_pt);
+  a.pt_stride = gpages;
+  a.seq_lens = reinterpret_cast<const int32_t*>(ws + lay.off_len);
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = 1;
+  a.head_dim_qk = kvq::kMlaDqk;
+  a.head_dim_v = kvq::kMlaDv;
+  a.max_pages = gpages;
+  a.num_pages = (int64_t)batch * gpages;
+  a.sm_scale = sm_scale;
+  a.out = static_cast<uint16_t*>(out_bf16);
+  a.lse = lse;
+  a.workspace = ws + lay.off_dense;
+  e = kvq::launch_mla_decode(a, lay.dense, num_cus_current(), stream);
+  if (e != hipSuccess) return hip_fail(e, "kvq_sparse_mla_decode");
   return ok();
 }
 

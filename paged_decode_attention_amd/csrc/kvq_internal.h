@@ -138,4 +138,34 @@ hipError_t launch_gqa_mfma_decode(const DecodeArgs& a, const DecodePlan& p, int 
 hipError_t launch_mla_decode(const DecodeArgs& a, const DecodePlan& p, int num_cus,
                              hipStream_t s);
 
+// ---- sparse top-k decode over the MLA slab -------------------------------------
+// The listed rows of every sequence are gathered into a compact slab in the
+// workspace (kk rows per sequence: k rounded up to a page), which the slab
+// decode then attends to in full.
+constexpr int kSparseMaxK = 2048;
+
+struct SparseArgs {
+  const int32_t* topk;
+  int64_t topk_stride;
+  int k;
+  const int32_t* page_table;
+  int64_t pt_stride;
+  const int32_t* seq_lens;
+  int max_pages;
+  int64_t num_pages;
+  const uint8_t* slab;
+  const uint16_t* scales;  // null for the types without a scale buffer
+  void* workspace;
+};
+
+struct SparseLayout {
+  int kk, row_bytes;
+  DecodePlan dense;  // the slab decode over the compact sequences
+  size_t off_dense, off_slab, off_scales, off_pt, off_len, bytes;
+};
+
+bool plan_sparse(int qtype, int batch, int n_q_heads, int k, SparseLayout* lay, const char** why);
+hipError_t launch_sparse_gather(const SparseArgs& s, const SparseLayout& lay, int batch,
+                                hipStream_t stream);
+
 }  // namespace kvq

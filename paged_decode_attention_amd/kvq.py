@@ -56,6 +56,11 @@ def _load() -> ctypes.CDLL:
     lib.kvq_paged_decode.argtypes = [I, P, P, P, P, P, P, I64, P, I, I, I, I, I, I, I, I64,
                                      c.c_float, P, P, P, c.c_size_t, P]
     lib.kvq_paged_decode.restype = I
+    lib.kvq_sparse_mla_decode_workspace_bytes.argtypes = [I, I, I, I]
+    lib.kvq_sparse_mla_decode_workspace_bytes.restype = c.c_size_t
+    lib.kvq_sparse_mla_decode.argtypes = [I, P, P, P, P, I64, P, P, I64, I, I, I, I, I, I64,
+                                          c.c_float, P, P, P, c.c_size_t, P]
+    lib.kvq_sparse_mla_decode.restype = I
     lib.kvq_last_error.argtypes = []
     lib.kvq_last_error.restype = c.c_char_p
     return lib
@@ -65,7 +70,8 @@ LIB = _load()
 
 # every symbol the public header declares
 EXPORTS = ("kvq_pool_bytes", "kvq_store", "kvq_dequant", "kvq_paged_decode_workspace_bytes",
-           "kvq_paged_decode", "kvq_last_error")
+           "kvq_paged_decode", "kvq_sparse_mla_decode_workspace_bytes", "kvq_sparse_mla_decode",
+           "kvq_last_error")
 
 
 def last_error() -> str:
@@ -204,6 +210,40 @@ def paged_decode(dtype, q, k_pool, k_scales, v_pool, v_scales, page_table, seq_l
                               head_dim_v, page_size, max_pages, num_pages, float(sm_scale),
                               _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                               _stream(q.device, stream))
+    _check(rc)
+    return out, lse
+
+
+def sparse_workspace_bytes(dtype, batch, n_q_heads, topk) -> int:
+    n = LIB.kvq_sparse_mla_decode_workspace_bytes(_dt(dtype), batch, n_q_heads, topk)
+    if n == 0:
+        raise NotImplementedError(last_error())
+    return n
+
+
+def sparse_mla_decode(dtype, q, slab, scales, page_table, seq_lens, topk_idx, sm_scale,
+                      out=None, lse=None, workspace=None, stream=None):
+    """Sparse top-k decode over the shared 576/512 slab: sequence b attends to
+    the token positions listed in topk_idx[b] (int32 [batch, k], -1 = none)."""
+    batch, n_q_heads, head_dim_qk = q.shape
+    num_pages, _, page_size, _ = slab.shape
+    max_pages = page_table.shape[1]
+    topk = topk_idx.shape[1]
+    if out is None:
+        out = torch.empty((batch, n_q_heads, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((batch, n_q_heads), dtype=torch.float32, device=q.device)
+    need = sparse_workspace_bytes(dtype, batch, n_q_heads, topk)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    pt_stride = page_table.stride(0) if batch > 1 else max_pages
+    tk_stride = topk_idx.stride(0) if batch > 1 else topk
+    rc = LIB.kvq_sparse_mla_decode(_dt(dtype), _ptr(q), _ptr(slab), _ptr(scales),
+                                   _ptr(page_table), pt_stride, _ptr(seq_lens), _ptr(topk_idx),
+                                   tk_stride, topk, batch, n_q_heads, page_size, max_pages,
+                                   num_pages, float(sm_scale), _ptr(out), _ptr(lse),
+                                   _ptr(workspace), workspace.numel(),
+                                   _stream(q.device, stream))
     _check(rc)
     return out, lse
 

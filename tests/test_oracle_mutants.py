@@ -51,6 +51,11 @@ MUTANTS = [
     ("e5m2 three fraction bits", "double r = round_to_grid(fabs((double)v), 2, -14);",
      "double r = round_to_grid(fabs((double)v), 3, -14);"),
     ("cast without the clamp", "  if (x > M) x = M;\n  if (x < -M) x = -M;", ""),
+    ("sparse length bound", "if (t < 0 || t >= L) continue;", "if (t < 0 || t > L) continue;"),
+    ("sparse V row stride",
+     "o[d] += w * kvo_pool_value(c->qtype, c->slab, c->scales, rows[j], c->head_dim_qk, d);",
+     "o[d] += w * kvo_pool_value(c->qtype, c->slab, c->scales, rows[j], c->head_dim_v, d);"),
+    ("sparse softmax scale dropped", "z[n] = c->sm_scale * dot;", "z[n] = dot;"),
     ("cast formats swapped",
      "return (qtype == KVO_FP8_E5M2_CAST) ? kvo_e5m2_encode(x) : kvo_e4m3_encode(x);",
      "return (qtype == KVO_FP8_E5M2_CAST) ? kvo_e4m3_encode(x) : kvo_e5m2_encode(x);"),
@@ -71,7 +76,7 @@ def _run_mutant(case):
     env = dict(os.environ, KVQ_ORACLE_LIB=so, OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_pins.py", "tests/test_oracle_attention_pins.py",
-                        "tests/test_oracle_cast_pins.py"],
+                        "tests/test_oracle_cast_pins.py", "tests/test_oracle_sparse_pins.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
     return name, r.returncode
 
