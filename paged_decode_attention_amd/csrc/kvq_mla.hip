@@ -556,6 +556,11 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
     // are staged in LDS (the tile buffers are free after the loop's last
     // barrier) so that every global store writes 1 KB contiguous per wave.
     {
+      // Lane-dependent offsets are recomputed here from an opaque copy of
+      // tid: values kept from the prologue end up spilled, and each reload is
+      // a memory round trip that also waits for every earlier store.
+      const int t = opaque(tid);
+      const int l = t & 63, nn = l & 15, gg = l >> 4;
       uint16_t* stage = s_tiles + wave * (32 * kStageRow);
       float Lh[2];
 #pragma unroll
@@ -563,7 +568,7 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
         const float Ls = sum_xor32(sum_xor16(lsum[ht]));
         Lh[ht] = Ls;
         const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-        uint16_t* srow = stage + (16 * ht + n16) * kStageRow + 4 * g;
+        uint16_t* srow = stage + (16 * ht + nn) * kStageRow + 4 * gg;
 #pragma unroll
         for (int dt = 0; dt < kDv / 16; ++dt) {
           const f32x4 v = acc[dt][ht];
@@ -573,27 +578,36 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
       }
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) {
-        const int h = 32 * wave + 16 * ht + n16;
-        if (g == 0 && h < Hq) {
+        const int h = 32 * wave + 16 * ht + nn;
+        if (gg == 0 && h < Hq) {
           if (nc == 1) {
             if (a.lse)
               a.lse[(int64_t)b * Hq + h] =
                   (mref[ht] == -INFINITY) ? -INFINITY : (mref[ht] + log2f(Lh[ht])) * kLn2;
           } else {
-            p.part_ml[((int64_t)item * Hq + h) * 2 + 0] = mref[ht];
-            p.part_ml[((int64_t)item * Hq + h) * 2 + 1] = Lh[ht];
+            *reinterpret_cast<float2*>(p.part_ml + ((int64_t)item * Hq + h) * 2) =
+                make_float2(mref[ht], Lh[ht]);
           }
         }
       }
       __builtin_amdgcn_wave_barrier();  // the stage is private to the wave
-      uint16_t* dst = (nc == 1) ? a.out + (int64_t)b * Hq * kDv
-                                : p.part_out + (int64_t)item * Hq * kDv;
-      for (int r = 0; r < 32; ++r) {
-        const int h = 32 * wave + r;
-        if (h >= Hq) break;
-        *reinterpret_cast<u32x4*>(dst + (int64_t)h * kDv + 8 * lane) =
-            *reinterpret_cast<const u32x4*>(stage + r * kStageRow + 8 * lane);
-      }
+      // The wave's 32 rows: every LDS read first, then the global stores as
+      // buffer stores through a descriptor that covers only the wave's heads
+      // below Hq (stores past it are dropped), so no store waits on another.
+      const int rows = __builtin_amdgcn_readfirstlane(min(32, max(Hq - 32 * wave, 0)));
+      const uint64_t da = reinterpret_cast<uint64_t>(
+          ((nc == 1) ? a.out + (int64_t)b * Hq * kDv : p.part_out + (int64_t)item * Hq * kDv) +
+          (int64_t)32 * wave * kDv);
+      const uint64_t dsa = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(da >> 32)) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)da);
+      const auto rd = page_rsrc(reinterpret_cast<const void*>(dsa), rows * kDv * 2);
+      const uint16_t* src = stage + 8 * l;
+      u32x4 o[32];
+#pragma unroll
+      for (int r = 0; r < 32; ++r) o[r] = *reinterpret_cast<const u32x4*>(src + r * kStageRow);
+#pragma unroll
+      for (int r = 0; r < 32; ++r)
+        __builtin_amdgcn_raw_buffer_store_b128(o[r], rd, r * kDv * 2 + 16 * l, 0, 0);
     }
   }
 }
