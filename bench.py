@@ -186,9 +186,15 @@ def cpu_baseline(wl, qtype, k_rows, v_rows, q_bits):
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
-def decode_only(args, wl, qtype, dev) -> int:
+SPARSE_K = 256  # tokens listed per query by the sparse MLA workload
+
+
+def decode_only(args, wl, qtype, dev, sparse_k=0) -> int:
     """Time kvq_paged_decode alone on `wl`, sweeping pool replicas so that
-    each call reads its KV from HBM, and print one JSON line."""
+    each call reads its KV from HBM, and print one JSON line.  sparse_k > 0:
+    time kvq_sparse_mla_decode over the slab instead, each query listing
+    sparse_k distinct random positions of its sequence, the calls of all
+    replicas captured in one HIP graph (a call takes microseconds)."""
     import torch
     from paged_decode_attention_amd import kvq
     from paged_decode_attention_amd import workloads as W
@@ -229,6 +235,18 @@ def decode_only(args, wl, qtype, dev) -> int:
     sl = torch.from_numpy(wl.seq_lens).to(dev)
     ws = None
     calls = []
+    if sparse_k:
+        rng = np.random.default_rng(sparse_k)
+        topk_np = np.stack([rng.choice(int(L), sparse_k, replace=False) for L in wl.seq_lens])
+        topk = torch.from_numpy(topk_np.astype(np.int32)).to(dev)
+        # the calls are bound to the stream the graph captures
+        strm = torch.cuda.Stream(device=dev)
+        for kp, ks, _, _ in pools:
+            d = kvq.PreparedSparse(qtype, q, kp, ks, pt, sl, topk, wl.sm_scale, workspace=ws,
+                                   stream=strm)
+            ws = d.workspace
+            calls.append(d)
+        return sparse_timing(args, wl, qtype, calls, topk_np, strm)
     for kp, ks, vp, vs in pools:
         d = kvq.PreparedDecode(qtype, q, kp, ks, vp, vs, pt, sl, wl.sm_scale, head_dim_v=Dv,
                                workspace=ws)
@@ -281,6 +299,61 @@ def decode_only(args, wl, qtype, dev) -> int:
     return 0
 
 
+def sparse_timing(args, wl, qtype, calls, topk_np, strm) -> int:
+    """Replays of one graph holding every replica's sparse call, timed by HIP
+    events around the replays (which run on the current stream)."""
+    import torch
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=strm):
+        for c in calls:
+            c()
+    for _ in range(args.warmup):
+        graph.replay()
+    K, R = args.steps, len(calls)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(K):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / (K * R)
+    # algorithmic bytes: the listed rows (codes + scales), their page-table
+    # entries, the lists, seq_lens, Q and O
+    per_row = {"bf16": 2 * 576, "fp8_e4m3": 612, "q8_0": 612, "fp8_e4m3_cast": 576,
+               "fp8_e5m2_cast": 576}[qtype]
+    n = topk_np.size
+    nbytes = (n * (per_row + 4 + 4) + 4 * wl.batch +
+              wl.batch * wl.n_q_heads * (wl.head_dim_qk + wl.head_dim_v) * 2)
+    flops = 2.0 * wl.n_q_heads * n * (wl.head_dim_qk + wl.head_dim_v)
+    res = {
+        "metric": "sparse top-k MLA decode call time, 1 GPU",
+        "value": round(us, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "higher_is_better": False,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "sparse top-%d decode over the %s slab (%d queries x %d heads, "
+                               "%d distinct random positions each)" % (
+                                   topk_np.shape[1], wl.name, wl.batch, wl.n_q_heads,
+                                   topk_np.shape[1]),
+                   "kv_storage": qtype, "replicas": R},
+        "call_us": round(us, 3),
+        "gbps": round(nbytes / (us * 1e-6) / 1e9, 2),
+        "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+        "algorithmic_bytes_per_call": int(nbytes),
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,7 +364,7 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="qwen3",
-                    choices=["qwen3", "ragged256", "single256", "mla", "mixed"],
+                    choices=["qwen3", "ragged256", "single256", "mla", "mixed", "mla_sparse"],
                     help="qwen3 (default) is the decode step this benchmark reports; the others "
                          "time kvq_paged_decode alone on that workload and print their own line")
     ap.add_argument("--replicas", type=int, default=0,
@@ -327,6 +400,8 @@ def main() -> int:
         torch.cuda.synchronize()
         log("copied %d x %d bytes" % (args.steps, src.numel()))
         return 0
+    if args.workload == "mla_sparse":
+        return decode_only(args, W.mla(), qtype, dev, sparse_k=SPARSE_K)
     if args.workload != "qwen3":
         return decode_only(args, W.BY_NAME[args.workload](), qtype, dev)
     wl = W.qwen3(replicas=args.layers)

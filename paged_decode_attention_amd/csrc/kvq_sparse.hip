@@ -10,14 +10,16 @@
 //
 // Softmax attention over a set of rows does not depend on their order, so
 // attending to the listed rows equals attending, in full, to a sequence made
-// of exactly those rows.  One workgroup per sequence walks its list in chunks
-// of 256 entries: an entry is taken when it is a position below the
-// sequence's length on a page that is present; the taken ones of a chunk get
-// consecutive places (a ballot count inside each wave, the wave totals
-// through LDS), and the workgroup copies their code rows (16-byte moves) and
-// scale rows into the workspace.  It then writes an identity page table for
-// the compact sequence and its length.  The codes are moved, not decoded, so
-// the decode sees exactly the stored rows.
+// of exactly those rows.  An entry is taken when it is a position below the
+// sequence's length on a page that is present; taken entries keep their list
+// order and get consecutive places in the compact sequence.  Each list is cut
+// into slices of 64 entries, one workgroup per slice: the workgroup counts the
+// taken entries before its slice itself (no workgroup waits for another),
+// places its own with one ballot, then copies their code rows (16-byte moves,
+// every load of a thread issued before its first store) and scale rows into
+// the workspace.  The first slice's workgroup writes the compact sequence's
+// identity page table, the last one its length.  The codes are moved, not
+// decoded, so the decode sees exactly the stored rows.
 #include "kvq_attn.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -26,11 +28,13 @@ namespace kvq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kSlice = 64;  // list entries per workgroup: one wave's ballot
 
 struct GatherArgs {
   const int32_t* topk;
   int64_t topk_stride;
   int k, kk;  // entries per list, and rows per compact sequence (k rounded up to a page)
+  int slices; // workgroups per list
   const int32_t* page_table;
   int64_t pt_stride;
   const int32_t* seq_lens;
@@ -46,54 +50,88 @@ struct GatherArgs {
 };
 
 constexpr int kNB = kMlaDqk / 32;  // scales per row
+constexpr int kScalePerThread = (kSlice * (kNB / 2) + kThreads - 1) / kThreads;
 
+// Slot of list entry i of sequence b in the slab, or -1 when it is skipped.
+__device__ __forceinline__ int64_t entry_slot(const GatherArgs& g, int b, int64_t L, int i) {
+  if (i >= g.k) return -1;
+  const int64_t t = g.topk[(int64_t)b * g.topk_stride + i];
+  if (t < 0 || t >= L) return -1;
+  const int64_t page = g.page_table[(int64_t)b * g.pt_stride + t / kPageSize];
+  if (page < 0 || page >= g.num_pages) return -1;
+  return page * kPageSize + t % kPageSize;
+}
+
+// kUnits: 16-byte moves per row (36 for 8-bit codes, 72 for bf16).
+template <int kUnits>
 __global__ __launch_bounds__(kThreads) void sparse_gather_kernel(GatherArgs g) {
-  __shared__ int64_t s_src[kThreads];
+  constexpr int kPerThread = (kSlice * kUnits + kThreads - 1) / kThreads;
+  constexpr int kRowBytes = kUnits * 16;
+  __shared__ int64_t s_src[kSlice];
   __shared__ int s_wave[kThreads / 64];
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int s_own;
+  const int b = blockIdx.x / g.slices, sl = blockIdx.x - b * g.slices;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int64_t L = g.seq_lens[b];
   const int64_t cap = (int64_t)g.max_pages * kPageSize;
   L = L < 0 ? 0 : (L > cap ? cap : L);
-  const int gpages = g.kk / kPageSize;
-  int count = 0;  // rows placed so far (uniform)
-  for (int i0 = 0; i0 < g.k; i0 += kThreads) {
-    const int i = i0 + tid;
-    const int64_t t = (i < g.k) ? g.topk[(int64_t)b * g.topk_stride + i] : -1;
-    bool take = t >= 0 && t < L;
-    int64_t page = -1;
-    if (take) page = g.page_table[(int64_t)b * g.pt_stride + t / kPageSize];
-    take = take && page >= 0 && page < g.num_pages;
-    const uint64_t m = __builtin_amdgcn_ballot_w64(take);
-    const int before = __builtin_popcountll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) s_wave[wave] = __builtin_popcountll(m);
-    __syncthreads();
-    int base = 0, chunk = 0;
-#pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) {
-      base += (w < wave) ? s_wave[w] : 0;
-      chunk += s_wave[w];
-    }
-    if (take) s_src[base + before] = page * kPageSize + t % kPageSize;
-    __syncthreads();
-    // code rows, 16 bytes per thread per turn
-    const int units = g.row_bytes / 16;
-    for (int u = tid; u < chunk * units; u += kThreads) {
-      const int r = u / units, c = u - r * units;
-      const uint4 v = *reinterpret_cast<const uint4*>(g.slab + s_src[r] * g.row_bytes + c * 16);
-      *reinterpret_cast<uint4*>(g.g_slab + ((int64_t)b * g.kk + count + r) * g.row_bytes + c * 16) = v;
-    }
-    if (g.scales) {
-      for (int u = tid; u < chunk * (kNB / 2); u += kThreads) {  // two fp16 per turn
-        const int r = u / (kNB / 2), c = u - r * (kNB / 2);
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(g.scales + s_src[r] * kNB + 2 * c);
-        *reinterpret_cast<uint32_t*>(g.g_scales + ((int64_t)b * g.kk + count + r) * kNB + 2 * c) = v;
-      }
-    }
-    count += chunk;
-    __syncthreads();  // s_src and s_wave are reused by the next chunk
+  const int start = sl * kSlice;
+  // wave 0 places this slice's entries; every thread counts entries before it
+  if (wave == 0) {
+    const int64_t src = entry_slot(g, b, L, start + lane);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(src >= 0);
+    if (src >= 0) s_src[__builtin_popcountll(m & ((1ull << lane) - 1ull))] = src;
+    if (lane == 0) s_own = __builtin_popcountll(m);
   }
-  for (int p = tid; p < gpages; p += kThreads) g.g_pt[(int64_t)b * gpages + p] = b * gpages + p;
-  if (tid == 0) g.g_len[b] = count;
+  int before = 0;
+  for (int i = tid; i < start; i += kThreads) before += entry_slot(g, b, L, i) >= 0 ? 1 : 0;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) before += __shfl_xor(before, o, 64);
+  if (lane == 0) s_wave[wave] = before;
+  __syncthreads();
+  int prefix = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) prefix += s_wave[w];
+  const int n = s_own;
+  const int64_t dst0 = (int64_t)b * g.kk + prefix;
+  // Code rows: every load of a thread first, then the stores.  The slice's
+  // rows land contiguously, so a move's offset in the destination is its
+  // index times 16; an index past the slice's rows reads the slice's first
+  // row again and its store falls outside the destination's buffer
+  // descriptor, which drops it.  No load or store sits under a branch.
+  if (n > 0) {
+    const auto dst = page_rsrc(g.g_slab + dst0 * kRowBytes, n * kRowBytes);
+    u32x4 v[kPerThread];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      int u = tid + j * kThreads;
+      u = u < n * kUnits ? u : 0;
+      const int r = u / kUnits, c = u - r * kUnits;
+      v[j] = *reinterpret_cast<const u32x4*>(g.slab + s_src[r] * kRowBytes + c * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+      __builtin_amdgcn_raw_buffer_store_b128(v[j], dst, (tid + j * kThreads) * 16, 0, 0);
+    if (g.scales) {  // two fp16 per move
+      const auto sdst = page_rsrc(g.g_scales + dst0 * kNB, n * kNB * 2);
+      uint32_t w[kScalePerThread];
+#pragma unroll
+      for (int j = 0; j < kScalePerThread; ++j) {
+        int u = tid + j * kThreads;
+        u = u < n * (kNB / 2) ? u : 0;
+        const int r = u / (kNB / 2), c = u - r * (kNB / 2);
+        w[j] = *reinterpret_cast<const uint32_t*>(g.scales + s_src[r] * kNB + 2 * c);
+      }
+#pragma unroll
+      for (int j = 0; j < kScalePerThread; ++j)
+        __builtin_amdgcn_raw_buffer_store_b32(w[j], sdst, (tid + j * kThreads) * 4, 0, 0);
+    }
+  }
+  if (sl == 0) {
+    const int gpages = g.kk / kPageSize;
+    for (int p = tid; p < gpages; p += kThreads) g.g_pt[(int64_t)b * gpages + p] = b * gpages + p;
+  }
+  if (sl == g.slices - 1 && tid == 0) g.g_len[b] = prefix + n;
 }
 
 }  // namespace
@@ -105,6 +143,7 @@ hipError_t launch_sparse_gather(const SparseArgs& s, const SparseLayout& lay, in
   g.topk_stride = s.topk_stride;
   g.k = s.k;
   g.kk = lay.kk;
+  g.slices = (s.k + kSlice - 1) / kSlice;
   g.page_table = s.page_table;
   g.pt_stride = s.pt_stride;
   g.seq_lens = s.seq_lens;
@@ -118,7 +157,11 @@ hipError_t launch_sparse_gather(const SparseArgs& s, const SparseLayout& lay, in
   g.g_scales = s.scales ? reinterpret_cast<uint16_t*>(ws + lay.off_scales) : nullptr;
   g.g_pt = reinterpret_cast<int32_t*>(ws + lay.off_pt);
   g.g_len = reinterpret_cast<int32_t*>(ws + lay.off_len);
-  sparse_gather_kernel<<<batch, kThreads, 0, stream>>>(g);
+  const dim3 grid((unsigned)((int64_t)batch * g.slices));
+  if (lay.row_bytes == kMlaDqk * 2)
+    sparse_gather_kernel<kMlaDqk * 2 / 16><<<grid, kThreads, 0, stream>>>(g);
+  else
+    sparse_gather_kernel<kMlaDqk / 16><<<grid, kThreads, 0, stream>>>(g);
   return hipGetLastError();
 }
 

@@ -278,6 +278,34 @@ class PreparedDecode:
         _check(LIB.kvq_paged_decode(*self.args))
 
 
+class PreparedSparse:
+    """kvq_sparse_mla_decode with every argument resolved once."""
+
+    def __init__(self, dtype, q, slab, scales, page_table, seq_lens, topk_idx, sm_scale,
+                 out=None, lse=None, workspace=None, stream=None):
+        batch, n_q_heads, _ = q.shape
+        num_pages, _, page_size, _ = slab.shape
+        max_pages, topk = page_table.shape[1], topk_idx.shape[1]
+        self.out = out if out is not None else torch.empty(
+            (batch, n_q_heads, 512), dtype=torch.bfloat16, device=q.device)
+        self.lse = lse if lse is not None else torch.empty(
+            (batch, n_q_heads), dtype=torch.float32, device=q.device)
+        need = sparse_workspace_bytes(dtype, batch, n_q_heads, topk)
+        self.workspace = workspace if workspace is not None else torch.empty(
+            need, dtype=torch.uint8, device=q.device)
+        pt_stride = page_table.stride(0) if batch > 1 else max_pages
+        tk_stride = topk_idx.stride(0) if batch > 1 else topk
+        self._keep = (q, slab, scales, page_table, seq_lens, topk_idx)
+        self.args = (_dt(dtype), _ptr(q), _ptr(slab), _ptr(scales), _ptr(page_table), pt_stride,
+                     _ptr(seq_lens), _ptr(topk_idx), tk_stride, topk, batch, n_q_heads,
+                     page_size, max_pages, num_pages, float(sm_scale), _ptr(self.out),
+                     _ptr(self.lse), _ptr(self.workspace), self.workspace.numel(),
+                     _stream(q.device, stream))
+
+    def __call__(self):
+        _check(LIB.kvq_sparse_mla_decode(*self.args))
+
+
 class PreparedStore:
     """kvq_store with every argument resolved once."""
 
