@@ -18,12 +18,14 @@ peak: its average launch duration from HIP events around replays of a graph
 holding the 28 layers' decode launches back to back (gaps between launches
 included), on the stream the kernels run on; `store_gbps` is
 the quantize-on-store at the mixed workload's size (8192 new tokens x 8 kv
-heads x 128, K and V in one call); `cpu_baseline` is the CPU oracle on a
+heads x 128, K and V in one call), timed from graph replays as the decode;
+`cpu_baseline` is the CPU oracle on a
 bounded sample of the same workload (repeated layer decodes for about 10 s),
 timed on this host.
 
 Other modes: `--workload ragged256|single256|mla|mixed` times kvq_paged_decode
-alone on that workload and prints its own line; `--only decode|copy` and
+alone on that workload and prints its own line; `--workload mla_sparse` times
+kvq_sparse_mla_decode (256 listed positions per query over the mla slab); `--only decode|copy` and
 `--traffic-from DIR` serve the rocprofv3 counter passes (see profiles/).
 """
 from __future__ import annotations
@@ -526,7 +528,9 @@ def main() -> int:
     dec_graph = d_start.elapsed_time(d_end) / (K * L)  # ms per decode launch
     # (3) the store at the mixed workload's size: 8192 new tokens (the last 128
     # of 64 sequences) x 8 kv heads x 128, K and V in one fused kvq_store into
-    # a 2^20-slot pool, timed alone with HIP events on its stream
+    # a 2^20-slot pool, timed alone: 8 calls captured back to back in one
+    # graph (eager calls would time the host's launch rate), replayed K times
+    # between two HIP events
     mw = W.mixed()
     new = dev_bf16(mw.new_rows())
     mkp, mks = kvq.alloc_pool(qtype, mw.num_pages, H, D, device=dev)
@@ -535,14 +539,21 @@ def main() -> int:
     big = kvq.PreparedStore(qtype, new[0], new[1], mslots, mkp, mks, mvp, mvs, stream=strm)
     for _ in range(args.warmup):
         big()
+    torch.cuda.synchronize()
+    sgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(sgraph, stream=strm):
+        for _ in range(8):
+            big()
+    for _ in range(args.warmup):
+        sgraph.replay()
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    s0.record(strm)
+    s0.record()
     for _ in range(K):
-        big()
-    s1.record(strm)
+        sgraph.replay()
+    s1.record()
     torch.cuda.synchronize()
-    big_us = s0.elapsed_time(s1) * 1e3 / K
+    big_us = s0.elapsed_time(s1) * 1e3 / (K * 8)
     big_bytes = store_bytes(int(mslots.numel()), H, D, qtype)
     achieved = dec_bytes / (dec_graph * 1e-3) / 1e9
     log("step %.3f ms (graph), decode launch %.2f us (decode-only graph; %.2f us with an event "
