@@ -441,18 +441,14 @@ typedef struct {
   double* lse;
 } kvo_dec_ctx;
 
-static void kvo_dec_unit(void* p, int64_t i) {
-  kvo_dec_ctx* c = (kvo_dec_ctx*)p;
-  int64_t row = c->rows ? c->rows[i] : i; /* row = b * Hq + h */
-  int b = (int)(row / c->n_q_heads), h = (int)(row % c->n_q_heads);
+/* Attention of one query row over the first L positions of sequence b, for
+ * query head h: scores, softmax and the weighted sum of V, as stated above. */
+static void kvo_attend(const kvo_dec_ctx* c, int b, int h, int64_t L, const uint16_t* qrow,
+                       double* o, double* lse_out) {
   int g = h / (c->n_q_heads / c->n_kv_heads);
-  int64_t L = c->seq_lens[b];
-  int64_t cap = (int64_t)c->max_pages * c->page_size;
-  if (L > cap) L = cap;
-  if (L < 0) L = 0;
   int shared = (c->v_pool == c->k_pool);
   int v_row_dim = shared ? c->head_dim_qk : c->head_dim_v;
-  const uint16_t* qrow = c->q + row * (int64_t)c->head_dim_qk;
+  if (L < 0) L = 0;
   double* z = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
   char* ok = (char*)malloc((size_t)(L > 0 ? L : 1));
   double zmax = -INFINITY;
@@ -469,10 +465,9 @@ static void kvo_dec_unit(void* p, int64_t i) {
     z[t] = c->sm_scale * dot;
     if (z[t] > zmax) zmax = z[t];
   }
-  double* o = c->out + i * (int64_t)c->head_dim_v;
   for (int d = 0; d < c->head_dim_v; ++d) o[d] = 0.0;
   if (zmax == -INFINITY) { /* no valid token */
-    if (c->lse) c->lse[i] = -INFINITY;
+    if (lse_out) *lse_out = -INFINITY;
     free(z);
     free(ok);
     return;
@@ -489,9 +484,25 @@ static void kvo_dec_unit(void* p, int64_t i) {
       o[d] += w * kvo_pool_value(c->qtype, c->v_pool, c->v_scales, r, v_row_dim, d);
   }
   for (int d = 0; d < c->head_dim_v; ++d) o[d] /= denom;
-  if (c->lse) c->lse[i] = zmax + log(denom);
+  if (lse_out) *lse_out = zmax + log(denom);
   free(z);
   free(ok);
+}
+
+static int64_t kvo_clamped_len(const kvo_dec_ctx* c, int b) {
+  int64_t L = c->seq_lens[b];
+  int64_t cap = (int64_t)c->max_pages * c->page_size;
+  if (L > cap) L = cap;
+  if (L < 0) L = 0;
+  return L;
+}
+
+static void kvo_dec_unit(void* p, int64_t i) {
+  kvo_dec_ctx* c = (kvo_dec_ctx*)p;
+  int64_t row = c->rows ? c->rows[i] : i; /* row = b * Hq + h */
+  int b = (int)(row / c->n_q_heads), h = (int)(row % c->n_q_heads);
+  kvo_attend(c, b, h, kvo_clamped_len(c, b), c->q + row * (int64_t)c->head_dim_qk,
+             c->out + i * (int64_t)c->head_dim_v, c->lse ? c->lse + i : NULL);
 }
 
 /* rows: optional list of (b * n_q_heads + h) to compute (NULL = all rows, in
@@ -508,6 +519,55 @@ void kvo_paged_decode(int qtype, const uint16_t* q, const uint8_t* k_pool,
                    rows,       out,        lse};
   if (!rows) n_rows = (int64_t)batch * n_q_heads;
   kvo_parallel_for(n_rows, threads, kvo_dec_unit, &c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Extend (prefill) attention over the quantized pool.                        */
+/* ------------------------------------------------------------------------ */
+/* The pool is read by prefill / extend attention as well as by the decode
+ * [PR103 §What: the quantized path covers the four attention kernels;
+ * PR113 §Testing: prefill].  Sequence b holds L_b = seq_lens[b] tokens in the
+ * pool (clamped as in the decode), of which the last E_b = q_start[b+1] -
+ * q_start[b] are new; their queries are rows q_start[b] .. q_start[b+1] - 1
+ * of q ([rows][n_q_heads][head_dim]).  New token i sits at position
+ * P_b + i, P_b = L_b - E_b, and attends causally to positions 0 .. P_b + i:
+ * the decode of that query over the sequence's first P_b + i + 1 positions
+ * (none when that is <= 0: o = 0, lse = -inf).  q_start[0] = 0, q_start is
+ * nondecreasing; out and lse have q_start[batch] * n_q_heads rows. */
+
+typedef struct {
+  kvo_dec_ctx d;
+  const int32_t* q_start;
+} kvo_ext_ctx;
+
+static void kvo_ext_unit(void* p, int64_t r) {
+  kvo_ext_ctx* e = (kvo_ext_ctx*)p;
+  const kvo_dec_ctx* c = &e->d;
+  int64_t j = r / c->n_q_heads; /* query token */
+  int h = (int)(r % c->n_q_heads);
+  int b = 0;
+  while (b + 1 < c->batch && e->q_start[b + 1] <= j) ++b;
+  int64_t E = e->q_start[b + 1] - e->q_start[b];
+  int64_t i = j - e->q_start[b];
+  int64_t len = kvo_clamped_len(c, b) - E + i + 1;
+  kvo_attend(c, b, h, len, c->q + r * (int64_t)c->head_dim_qk, c->out + r * (int64_t)c->head_dim_v,
+             c->lse ? c->lse + r : NULL);
+}
+
+void kvo_extend_attention(int qtype, const uint16_t* q, const int32_t* q_start,
+                          const uint8_t* k_pool, const uint16_t* k_scales, const uint8_t* v_pool,
+                          const uint16_t* v_scales, const int32_t* page_table, int64_t pt_stride,
+                          const int32_t* seq_lens, int batch, int n_q_heads, int n_kv_heads,
+                          int head_dim, int page_size, int max_pages, int64_t num_pages,
+                          double sm_scale, double* out, double* lse, int threads) {
+  kvo_ext_ctx e;
+  kvo_dec_ctx c = {qtype,     q,          k_pool,    v_pool,    k_scales,  v_scales,
+                   page_table, pt_stride, seq_lens,  batch,     n_q_heads, n_kv_heads,
+                   head_dim,  head_dim,   page_size, max_pages, num_pages, sm_scale,
+                   NULL,      out,        lse};
+  e.d = c;
+  e.q_start = q_start;
+  kvo_parallel_for((int64_t)q_start[batch] * n_q_heads, threads, kvo_ext_unit, &e);
 }
 
 /* ------------------------------------------------------------------------ */

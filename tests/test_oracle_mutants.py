@@ -43,7 +43,7 @@ MUTANTS = [
     ("fp16 subnormal step", "(uint16_t)(r * 16777216.0)", "(uint16_t)(r * 8388608.0)"),
     ("no subnormal floor", "if (e < emin) e = emin;", ";"),
     ("zero scale not special", "if (s == 0.0f) {", "if (0) {"),
-    ("lse without log", "c->lse[i] = zmax + log(denom);", "c->lse[i] = zmax + denom;"),
+    ("lse without log", "*lse_out = zmax + log(denom);", "*lse_out = zmax + denom;"),
     ("bf16 fraction bits", "double r = round_to_grid(fabs(x), 7, -126);",
      "double r = round_to_grid(fabs(x), 8, -126);"),
     ("e5m2 exponent bias 16", "v = ldexp(1.0 + m / 4.0, e - 15);", "v = ldexp(1.0 + m / 4.0, e - 16);"),
@@ -56,6 +56,13 @@ MUTANTS = [
      "o[d] += w * kvo_pool_value(c->qtype, c->slab, c->scales, rows[j], c->head_dim_qk, d);",
      "o[d] += w * kvo_pool_value(c->qtype, c->slab, c->scales, rows[j], c->head_dim_v, d);"),
     ("sparse softmax scale dropped", "z[n] = c->sm_scale * dot;", "z[n] = dot;"),
+    ("extend position off by one", "int64_t len = kvo_clamped_len(c, b) - E + i + 1;",
+     "int64_t len = kvo_clamped_len(c, b) - E + i;"),
+    ("extend without the causal limit", "int64_t len = kvo_clamped_len(c, b) - E + i + 1;",
+     "int64_t len = kvo_clamped_len(c, b);"),
+    ("extend token mapped to the next sequence",
+     "while (b + 1 < c->batch && e->q_start[b + 1] <= j) ++b;",
+     "while (b + 1 < c->batch && e->q_start[b + 1] < j) ++b;"),
     ("cast formats swapped",
      "return (qtype == KVO_FP8_E5M2_CAST) ? kvo_e5m2_encode(x) : kvo_e4m3_encode(x);",
      "return (qtype == KVO_FP8_E5M2_CAST) ? kvo_e4m3_encode(x) : kvo_e5m2_encode(x);"),
@@ -76,7 +83,8 @@ def _run_mutant(case):
     env = dict(os.environ, KVQ_ORACLE_LIB=so, OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_pins.py", "tests/test_oracle_attention_pins.py",
-                        "tests/test_oracle_cast_pins.py", "tests/test_oracle_sparse_pins.py"],
+                        "tests/test_oracle_cast_pins.py", "tests/test_oracle_sparse_pins.py",
+                        "tests/test_oracle_extend_pins.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
     return name, r.returncode
 
