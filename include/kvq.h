@@ -245,6 +245,54 @@ int kvq_sparse_mla_decode(kvq_dtype dtype, const void* q, const void* slab,
                           int64_t num_pages, float sm_scale, void* out_bf16, float* lse,
                           void* workspace, size_t workspace_bytes, kvq_stream_t stream);
 
+/* Workspace bytes kvq_extend_attention needs (the split-K partials and
+ * counters of the matrix-core kernel over max_new_tokens x G query rows per
+ * kv head).  0 if the shapes are invalid (see kvq_extend_attention).
+ * Host-only. */
+size_t kvq_extend_attention_workspace_bytes(kvq_dtype dtype, int batch, int n_q_heads,
+                                            int n_kv_heads, int head_dim, int page_size,
+                                            int max_pages, int max_new_tokens);
+
+/* Causal extend (prefill) attention over the quantized pool [PR103
+ * "feat(kvcache): 8-bit KV cache (q8_0 / fp8_e4m3) behind --kv-cache-dtype"
+ * §What: the quantized pool feeds the prefill / extend attention kernels as
+ * well as the decode; PR113 "feat(kvcache): 8-bit DSV4 window/compressed KV
+ * behind --kv-cache-dtype" §Testing: prefill, masked (-1) columns].
+ *
+ * The new tokens' K and V are already in the pool (kvq_store).  Sequence b
+ * holds L = seq_lens[b] tokens (clamped to max_pages * page_size), of which
+ * the last E = q_start[b+1] - q_start[b] are new; new token i sits at position
+ * P + i, P = L - E, and attends to positions 0 .. P + i of its sequence:
+ *     z_t = sm_scale * q[j][h] . k_t[kv(h)],  out[j][h] = sum_t softmax(z)_t v_t,
+ *     lse[j][h] = log sum_t exp(z_t),  j = q_start[b] + i, kv(h) = h / (Hq/Hkv);
+ * a token with no visible position (P + i < 0, or all pages masked): out = 0,
+ * lse = -inf.  Masked (-1) page-table entries are skipped as in the decode.
+ * E = L (no prefix) is a prefill.
+ *
+ *   q          : device bf16 [T][n_q_heads][head_dim], T = q_start[batch],
+ *                16-byte aligned: the new tokens of every sequence, back to back.
+ *   q_start    : device int32 [batch + 1]: q_start[0] = 0, nondecreasing, each
+ *                difference at most max_new_tokens (rows past max_new_tokens of
+ *                a sequence are not written).
+ *   k_pool, v_pool, scales, page_table, seq_lens, num_pages: as kvq_paged_decode
+ *                (separate K and V pools, head_dim 64, 128 or 256).
+ *   out_bf16   : device bf16 [T][n_q_heads][head_dim]; lse: device fp32
+ *                [T][n_q_heads] or NULL.
+ *   workspace  : as kvq_paged_decode, sized by
+ *                kvq_extend_attention_workspace_bytes(): zeroed once, left at
+ *                zero by every call; calls sharing it must not overlap.
+ * The query rows of a kv head (token-major, max_new_tokens x G of them) run on
+ * the matrix cores in tiles of 16; each tile streams the sequence's K/V once.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP;
+ * validation completes before any launch. */
+int kvq_extend_attention(kvq_dtype dtype, const void* q, const int32_t* q_start,
+                         int max_new_tokens, const void* k_pool, const uint16_t* k_scales,
+                         const void* v_pool, const uint16_t* v_scales, const int32_t* page_table,
+                         int64_t pt_stride, const int32_t* seq_lens, int batch, int n_q_heads,
+                         int n_kv_heads, int head_dim, int page_size, int max_pages,
+                         int64_t num_pages, float sm_scale, void* out_bf16, float* lse,
+                         void* workspace, size_t workspace_bytes, kvq_stream_t stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* kvq_last_error(void);
 

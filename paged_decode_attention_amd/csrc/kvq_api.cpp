@@ -96,7 +96,7 @@ namespace kvq {
 
 bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_dim_qk,
                  int head_dim_v, int page_size, int max_pages, DecodePlan* plan,
-                 const char** why) {
+                 const char** why, int ext_new) {
   static thread_local char msg[256];
   auto no = [&](const char* fmt, ...) {
     va_list ap;
@@ -119,6 +119,11 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
   if (head_dim_v > head_dim_qk) return no("head_dim_v %d > head_dim_qk %d", head_dim_v, head_dim_qk);
   DecodePlan p{};
   const int G = n_q_heads / n_kv_heads;
+  if (ext_new > 0 && !(head_dim_qk == head_dim_v &&
+                       (head_dim_qk == 64 || head_dim_qk == 128 || head_dim_qk == 256)))
+    return no("extend attention needs separate K/V pools with head_dim 64, 128 or 256 (got "
+              "%d/%d)", head_dim_qk, head_dim_v);
+  if (ext_new > kExtendMaxNew) return no("max_new_tokens %d exceeds %d", ext_new, kExtendMaxNew);
   if (head_dim_qk == kMlaDqk && head_dim_v == kMlaDv && n_kv_heads == 1) {
     if (n_q_heads % 16 != 0 || n_q_heads > 128)
       return no("the 576/512 slab needs n_q_heads a multiple of 16 up to 128 (got %d)", n_q_heads);
@@ -146,12 +151,21 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
     p.kind = DK_GQA;
     // 8 or more query heads per kv head (up to 16, or a multiple of 16) run
     // on the matrix-core kernel, the G heads as one padded 16-wide tile
-    p.mfma = G >= 8 && head_dim_qk >= 64 && (G <= 16 || G % 16 == 0);
-    if (p.mfma)
-      p.gt = (G <= 16) ? G : 16;
-    else
-      p.gt = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-    p.n_hg = G / p.gt;
+    // Extend attention: the ext_new x G query rows of a kv head (token-major)
+    // form ceil(rows / 16) tiles of up to 16 columns on the matrix cores.
+    if (ext_new > 0) {
+      const int64_t rows = (int64_t)ext_new * G;
+      p.mfma = true;
+      p.gt = rows <= 16 ? (int)rows : 16;
+      p.n_hg = (int)((rows + p.gt - 1) / p.gt);
+    } else {
+      p.mfma = G >= 8 && head_dim_qk >= 64 && (G <= 16 || G % 16 == 0);
+      if (p.mfma)
+        p.gt = (G <= 16) ? G : 16;
+      else
+        p.gt = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+      p.n_hg = G / p.gt;
+    }
     const int64_t seq_units = (int64_t)n_kv_heads * p.n_hg;  // (kv head, head group) pairs
     const int64_t units = (int64_t)batch * seq_units;
     // Work items are sized on the device from the actual lengths (about
@@ -408,6 +422,95 @@ int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
                  : plan.mfma                 ? kvq::launch_gqa_mfma_decode(a, plan, cus, stream)
                                              : kvq::launch_gqa_decode(a, plan, cus, stream);
   if (e != hipSuccess) return hip_fail(e, "kvq_paged_decode");
+  return ok();
+}
+
+size_t kvq_extend_attention_workspace_bytes(kvq_dtype dtype, int batch, int n_q_heads,
+                                            int n_kv_heads, int head_dim, int page_size,
+                                            int max_pages, int max_new_tokens) {
+  kvq::DecodePlan p;
+  const char* why = nullptr;
+  if (max_new_tokens < 1) {
+    fail(KVQ_ERR_ARG, "kvq_extend_attention_workspace_bytes: max_new_tokens must be >= 1");
+    return 0;
+  }
+  if (!kvq::plan_decode(dtype, batch, n_q_heads, n_kv_heads, head_dim, head_dim, page_size,
+                        max_pages, &p, &why, max_new_tokens)) {
+    fail(KVQ_ERR_UNSUPPORTED, "kvq_extend_attention_workspace_bytes: %s", why);
+    return 0;
+  }
+  g_err.clear();
+  return p.bytes;
+}
+
+int kvq_extend_attention(kvq_dtype dtype, const void* q, const int32_t* q_start,
+                         int max_new_tokens, const void* k_pool, const uint16_t* k_scales,
+                         const void* v_pool, const uint16_t* v_scales, const int32_t* page_table,
+                         int64_t pt_stride, const int32_t* seq_lens, int batch, int n_q_heads,
+                         int n_kv_heads, int head_dim, int page_size, int max_pages,
+                         int64_t num_pages, float sm_scale, void* out_bf16, float* lse,
+                         void* workspace, size_t workspace_bytes, kvq_stream_t stream) {
+  if (!known_dtype(dtype))
+    return fail(KVQ_ERR_ARG, "kvq_extend_attention: unknown dtype %d", dtype);
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || max_pages < 1 || head_dim < 1 ||
+      page_size < 1 || max_new_tokens < 1)
+    return fail(KVQ_ERR_ARG, "kvq_extend_attention: sizes must be >= 1");
+  if (n_q_heads % n_kv_heads != 0)
+    return fail(KVQ_ERR_ARG, "kvq_extend_attention: n_q_heads %d is not a multiple of n_kv_heads %d",
+                n_q_heads, n_kv_heads);
+  if (dtype != KVQ_BF16 && head_dim % KVQ_BLOCK)
+    return fail(KVQ_ERR_ARG, "kvq_extend_attention: head_dim %d is not a multiple of the %d-element block",
+                head_dim, KVQ_BLOCK);
+  if (pt_stride < max_pages)
+    return fail(KVQ_ERR_ARG, "kvq_extend_attention: pt_stride %lld < max_pages %d",
+                (long long)pt_stride, max_pages);
+  if (num_pages < 1 || num_pages * (int64_t)page_size > INT32_MAX)
+    return fail(KVQ_ERR_ARG, "kvq_extend_attention: num_pages must be in 1..2^31/page_size");
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
+    return fail(KVQ_ERR_ARG, "kvq_extend_attention: sm_scale is not finite");
+  if (!q || !q_start || !k_pool || !v_pool || !page_table || !seq_lens || !out_bf16)
+    return fail(KVQ_ERR_ARG, "kvq_extend_attention: null pointer");
+  if (scaled(dtype) && (!k_scales || !v_scales))
+    return fail(KVQ_ERR_ARG, "kvq_extend_attention: null scales");
+  if (k_pool == v_pool)
+    return fail(KVQ_ERR_UNSUPPORTED, "kvq_extend_attention: needs separate K and V pools");
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out_bf16, 4))
+    return fail(KVQ_ERR_ARG, "kvq_extend_attention: q and pools must be 16-byte aligned");
+  kvq::DecodePlan plan;
+  const char* why = nullptr;
+  if (!kvq::plan_decode(dtype, batch, n_q_heads, n_kv_heads, head_dim, head_dim, page_size,
+                        max_pages, &plan, &why, max_new_tokens))
+    return fail(KVQ_ERR_UNSUPPORTED, "kvq_extend_attention: %s", why);
+  if (!workspace || workspace_bytes < plan.bytes)
+    return fail(KVQ_ERR_WORKSPACE, "kvq_extend_attention: workspace of %zu bytes needed, %zu given",
+                plan.bytes, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256))
+    return fail(KVQ_ERR_WORKSPACE, "kvq_extend_attention: workspace must be 256-byte aligned");
+  kvq::DecodeArgs a;
+  a.qtype = dtype;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = static_cast<const uint8_t*>(k_pool);
+  a.k_scales = k_scales;
+  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.v_scales = v_scales;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.head_dim_qk = head_dim;
+  a.head_dim_v = head_dim;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.sm_scale = sm_scale;
+  a.out = static_cast<uint16_t*>(out_bf16);
+  a.lse = lse;
+  a.workspace = workspace;
+  a.q_start = q_start;
+  a.max_new = max_new_tokens;
+  hipError_t e = kvq::launch_gqa_mfma_decode(a, plan, num_cus_current(), stream);
+  if (e != hipSuccess) return hip_fail(e, "kvq_extend_attention");
   return ok();
 }
 

@@ -214,6 +214,26 @@ __device__ __forceinline__ float exp2_rel(float x, float m) {
   return (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - m);
 }
 
+// Query rows of a kv head.  Column c (0 .. n_hg * gt) of kv head kvh is,
+// for the decode, query head kvh * G + c of sequence b; for extend attention
+// it is new token i = c / G of the sequence, head kvh * G + c % G (rows are
+// token-major, so a 16-column tile holds 16 / G consecutive new tokens).
+// query_row gives its row of q / out ([rows][Hq]), -1 for a padding column;
+// query_end the exclusive end of the positions it may attend to: the length
+// L for the decode, P + i + 1 for new token i at position P + i = L - E + i.
+__device__ __forceinline__ int64_t query_row(const DecodeArgs& a, int b, int kvh, int c, int G) {
+  if (!a.q_start) return (int64_t)b * a.n_q_heads + kvh * G + c;
+  const int qs = a.q_start[b], E = min(a.q_start[b + 1] - qs, a.max_new);
+  const int i = c / G;
+  return i < E ? (int64_t)(qs + i) * a.n_q_heads + kvh * G + (c - i * G) : -1;
+}
+__device__ __forceinline__ int query_end(const DecodeArgs& a, int b, int L, int c, int G) {
+  if (!a.q_start) return L;
+  const int E = a.q_start[b + 1] - a.q_start[b];
+  const int i = c / G;
+  return i < min(E, a.max_new) ? L - E + i + 1 : 0;
+}
+
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
 constexpr int kNonTemporal = 2;         // cache policy: streaming (read once)
 

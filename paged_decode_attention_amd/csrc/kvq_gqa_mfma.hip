@@ -133,7 +133,9 @@ __device__ __forceinline__ void transpose4x4(const uint32_t* in, uint32_t* out) 
   out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
-template <int QT, int D>
+// EXT: extend attention (query rows are new tokens x heads, each with its own
+// causal end); false: the decode, whose item end is uniform over the wave.
+template <int QT, int D, bool EXT>
 __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   using Gm = MfGeo<QT, D>;
   constexpr int ESZ = Gm::ESZ, NKS = Gm::NKS, NT = Gm::NT, VDW = Gm::VDW, KLD = Gm::KLD;
@@ -166,9 +168,15 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     for (int b = tid; b <= a.batch; b += kT) p.prefix[b] = s_prefix[b];
   for (int b = blockIdx.x; b < a.batch; b += gridDim.x) {
     if (s_prefix[b] != s_prefix[b + 1]) continue;
-    for (int i = tid; i < a.n_q_heads * D; i += kT) a.out[(int64_t)b * a.n_q_heads * D + i] = 0;
+    // its query rows: one per head (decode), or per head of each new token
+    int64_t r0 = (int64_t)b * a.n_q_heads, nr = a.n_q_heads;
+    if (a.q_start) {
+      r0 = (int64_t)a.q_start[b] * a.n_q_heads;
+      nr = (int64_t)max(min(a.q_start[b + 1] - a.q_start[b], a.max_new), 0) * a.n_q_heads;
+    }
+    for (int64_t i = tid; i < nr * D; i += kT) a.out[r0 * D + i] = 0;
     if (a.lse)
-      for (int h = tid; h < a.n_q_heads; h += kT) a.lse[(int64_t)b * a.n_q_heads + h] = -INFINITY;
+      for (int64_t h = tid; h < nr; h += kT) a.lse[r0 + h] = -INFINITY;
   }
 
   // per-lane offsets inside a (page, kv head) chunk
@@ -198,7 +206,18 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     const int t0 = chunk * item_tokens;
     const int nt = min(item_tokens, L - t0);
     const int np = (nt + kPageSize - 1) / kPageSize;
-    const int h0 = kvh * G + hg * GT;
+    // extend attention: a tile of query rows past the sequence's new tokens
+    // has nothing to compute or write (uniform over the block; every chunk
+    // of the tile skips, so its split-K counter stays untouched)
+    if (EXT && hg * GT / G >= min(a.q_start[b + 1] - a.q_start[b], a.max_new)) continue;
+    // this lane's query row and the item tokens it may attend to (the
+    // decode's: the item's own tokens, a wave-uniform bound)
+    const int64_t qrow_lane = (n16 < GT) ? (EXT ? query_row(a, b, kvh, hg * GT + n16, G)
+                                                : (int64_t)b * a.n_q_heads + kvh * G + hg * GT + n16)
+                                         : -1;
+    int col_lim = nt;
+    if constexpr (EXT)
+      col_lim = (n16 < GT) ? max(min(nt, query_end(a, b, L, hg * GT + n16, G) - t0), 0) : 0;
     const int nsteps = (np > wave) ? (np - wave + kW - 1) / kW : 0;  // pages of this wave
 
     // page ids of this wave's steps: lane k holds the id of step k (page
@@ -218,14 +237,19 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     // every path through it issues the same loads
     const int nst = max((nsteps + NBUF - 1) / NBUF * NBUF, NBUF);
 
-    // Q^T operands: qb[ks] = q[h0 + n16][32ks + 8g .. +7] (0 for padding heads)
+    // Q^T operands: qb[ks] = the query row of column n16, elements 32ks + 8g ..
+    // +7 (0 for padding columns)
     u32x4 qb[NKS];
     {
-      const bool real = n16 < GT;
+      const bool real = qrow_lane >= 0;
       // the elements of block ks that lane group g holds in the K operand:
       // 32 ks + 8 g (bf16), or after the 8-bit lane swap 32 ks + (0, 16, 8, 24)[g]
       const int goff = (ESZ == 1) ? 16 * (g & 1) + 8 * (g >> 1) : 8 * g;
-      const uint16_t* qrow = a.q + ((int64_t)b * a.n_q_heads + h0 + (real ? n16 : 0)) * D + goff;
+      // a padding column reads the tile's first row (it exists: tiles with
+      // no row are skipped above) and zeroes it
+      const int64_t row0 = EXT ? query_row(a, b, kvh, hg * GT, G)
+                               : (int64_t)b * a.n_q_heads + kvh * G + hg * GT;
+      const uint16_t* qrow = a.q + (real ? qrow_lane : row0) * D + goff;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
@@ -324,11 +348,17 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
         }
       }
       const int tok0 = (wave + st * kW) * kPageSize + 4 * g;  // token of r = 0 in the item
-      const int lim = pid >= 0 ? nt : 0;  // a select, not a branch around the page's work
+      // ok: the token exists (its V rows are used, masked to zero otherwise);
+      // the score is kept only below this lane's column end as well.  A
+      // lane's V registers hold rows of other columns' products, so the V
+      // mask must not depend on the column.  (Selects, not branches around
+      // the page's work.)
+      const int lim = pid >= 0 ? nt : 0;
+      const int slim = pid >= 0 ? col_lim : 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         ok[r] = tok0 + r < lim;
-        s[r] = ok[r] ? s[r] * p.scale_log2 : -INFINITY;
+        s[r] = (tok0 + r < slim) ? s[r] * p.scale_log2 : -INFINITY;
       }
     };
 
@@ -475,9 +505,12 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
       for (int w = 0; w < kW; ++w) v += exp2_rel(s_ml[w][h][0], M) * s_red[(w * kN + h) * D + d];
       if (nc == 1) {
         const float Ls = s_hm[h][1];
-        const int64_t orow = (int64_t)b * a.n_q_heads + h0 + h;
-        a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
-        if (d == 0 && a.lse) a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
+        const int64_t orow = EXT ? query_row(a, b, kvh, hg * GT + h, G)
+                                 : (int64_t)b * a.n_q_heads + kvh * G + hg * GT + h;
+        if (orow >= 0) {
+          a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
+          if (d == 0 && a.lse) a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
+        }
       } else {
         store_agent(&p.part_acc[((int64_t)item * GT + h) * D + d], v);
         if (d == 0) {
@@ -536,9 +569,13 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
               if (c0 + j < nc) v += s_red[(c0 + j) * GT + h] * x[j];
           }
           const float M = s_hm[h][0], Ls = s_hm[h][1];
-          const int64_t orow = (int64_t)b * a.n_q_heads + h0 + h;
-          a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
-          if (d == 0 && a.lse) a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
+          const int64_t orow = EXT ? query_row(a, b, kvh, hg * GT + h, G)
+                                   : (int64_t)b * a.n_q_heads + kvh * G + hg * GT + h;
+          if (orow >= 0) {
+            a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
+            if (d == 0 && a.lse)
+              a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
+          }
         }
         if (tid == 0)
           __hip_atomic_store(&p.count[(int64_t)b * units + u], 0, __ATOMIC_RELAXED,
@@ -551,7 +588,10 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
 template <int QT, int D>
 hipError_t launch_d(const MfParams& mp, int grid, hipStream_t s) {
   const size_t dyn = (size_t)(mp.a.batch + 1) * sizeof(int);
-  gqa_mfma_kernel<QT, D><<<grid, kT, dyn, s>>>(mp);
+  if (mp.a.q_start)
+    gqa_mfma_kernel<QT, D, true><<<grid, kT, dyn, s>>>(mp);
+  else
+    gqa_mfma_kernel<QT, D, false><<<grid, kT, dyn, s>>>(mp);
   return hipGetLastError();
 }
 

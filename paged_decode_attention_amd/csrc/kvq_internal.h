@@ -122,12 +122,21 @@ struct DecodeArgs {
   uint16_t* out;
   float* lse;
   void* workspace;
+  // Extend attention (null for the decode): the new tokens' query rows of
+  // sequence b are q_start[b] .. q_start[b+1]-1 of q and out ([rows][Hq][D]),
+  // at most max_new of them per sequence.
+  const int32_t* q_start = nullptr;
+  int max_new = 0;
 };
 
+constexpr int kExtendMaxNew = 65536;  // new tokens per sequence, extend attention
+
 // Host-only planning: returns false (with a message) for unsupported shapes.
+// ext_new > 0 plans extend attention with at most ext_new new tokens per
+// sequence (the matrix-core kernel, ext_new x G query rows per kv head).
 bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_dim_qk,
                  int head_dim_v, int page_size, int max_pages, DecodePlan* plan,
-                 const char** why);
+                 const char** why, int ext_new = 0);
 
 hipError_t launch_gqa_decode(const DecodeArgs& a, const DecodePlan& p, int num_cus,
                              hipStream_t s);

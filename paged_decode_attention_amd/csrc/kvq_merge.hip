@@ -54,7 +54,8 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_kernel(MergeParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int G = a.n_q_heads / a.n_kv_heads;
   const int kvh = u / p.n_hg, hg = u - kvh * p.n_hg;
-  const int64_t orow = (int64_t)b * a.n_q_heads + kvh * G + hg * p.gt + h;
+  const int64_t orow = query_row(a, b, kvh, hg * p.gt + h, G);
+  if (orow < 0) return;  // a padding column of extend attention
   const int grp = tid / kLanesPerRow, j = tid % kLanesPerRow;
   const float* src = p.part_acc + ((int64_t)first * p.gt + h) * p.D + dchunk * kCols + 4 * j;
   const int64_t cstride = (int64_t)p.units * p.gt * p.D;

@@ -61,6 +61,11 @@ def _load() -> ctypes.CDLL:
     lib.kvq_sparse_mla_decode.argtypes = [I, P, P, P, P, I64, P, P, I64, I, I, I, I, I, I64,
                                           c.c_float, P, P, P, c.c_size_t, P]
     lib.kvq_sparse_mla_decode.restype = I
+    lib.kvq_extend_attention_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.kvq_extend_attention_workspace_bytes.restype = c.c_size_t
+    lib.kvq_extend_attention.argtypes = [I, P, P, I, P, P, P, P, P, I64, P, I, I, I, I, I, I, I64,
+                                         c.c_float, P, P, P, c.c_size_t, P]
+    lib.kvq_extend_attention.restype = I
     lib.kvq_last_error.argtypes = []
     lib.kvq_last_error.restype = c.c_char_p
     return lib
@@ -71,7 +76,7 @@ LIB = _load()
 # every symbol the public header declares
 EXPORTS = ("kvq_pool_bytes", "kvq_store", "kvq_dequant", "kvq_paged_decode_workspace_bytes",
            "kvq_paged_decode", "kvq_sparse_mla_decode_workspace_bytes", "kvq_sparse_mla_decode",
-           "kvq_last_error")
+           "kvq_extend_attention_workspace_bytes", "kvq_extend_attention", "kvq_last_error")
 
 
 def last_error() -> str:
@@ -246,6 +251,74 @@ def sparse_mla_decode(dtype, q, slab, scales, page_table, seq_lens, topk_idx, sm
                                    _stream(q.device, stream))
     _check(rc)
     return out, lse
+
+
+def extend_workspace_bytes(dtype, batch, n_q_heads, n_kv_heads, head_dim, page_size, max_pages,
+                           max_new_tokens) -> int:
+    n = LIB.kvq_extend_attention_workspace_bytes(_dt(dtype), batch, n_q_heads, n_kv_heads,
+                                                 head_dim, page_size, max_pages, max_new_tokens)
+    if n == 0:
+        raise NotImplementedError(last_error())
+    return n
+
+
+def extend_attention(dtype, q, q_start, max_new_tokens, k_pool, k_scales, v_pool, v_scales,
+                     page_table, seq_lens, sm_scale, out=None, lse=None, workspace=None,
+                     stream=None):
+    """Causal extend (prefill) attention: q bf16 [T, Hq, D] holds the new
+    tokens of every sequence back to back (q_start int32 [batch + 1]); each
+    attends to its sequence's pool up to its own position.  Returns (out, lse)."""
+    T, n_q_heads, head_dim = q.shape
+    num_pages, n_kv_heads, page_size, _ = k_pool.shape
+    batch = seq_lens.numel()
+    max_pages = page_table.shape[1]
+    if page_table.stride(1) != 1:
+        raise ValueError("page_table rows must be contiguous")
+    pt_stride = page_table.stride(0) if batch > 1 else max_pages
+    if out is None:
+        out = torch.empty((T, n_q_heads, head_dim), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, n_q_heads), dtype=torch.float32, device=q.device)
+    need = extend_workspace_bytes(dtype, batch, n_q_heads, n_kv_heads, head_dim, page_size,
+                                  max_pages, max_new_tokens)
+    if workspace is None:  # zero-filled once; each call leaves it zeroed
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    rc = LIB.kvq_extend_attention(_dt(dtype), _ptr(q), _ptr(q_start), max_new_tokens,
+                                  _ptr(k_pool), _ptr(k_scales), _ptr(v_pool), _ptr(v_scales),
+                                  _ptr(page_table), pt_stride, _ptr(seq_lens), batch, n_q_heads,
+                                  n_kv_heads, head_dim, page_size, max_pages, num_pages,
+                                  float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(),
+                                  _stream(q.device, stream))
+    _check(rc)
+    return out, lse
+
+
+class PreparedExtend:
+    """kvq_extend_attention with every argument resolved once."""
+
+    def __init__(self, dtype, q, q_start, max_new_tokens, k_pool, k_scales, v_pool, v_scales,
+                 page_table, seq_lens, sm_scale, workspace=None, stream=None):
+        T, n_q_heads, head_dim = q.shape
+        num_pages, n_kv_heads, page_size, _ = k_pool.shape
+        batch = seq_lens.numel()
+        max_pages = page_table.shape[1]
+        self.out = torch.empty((T, n_q_heads, head_dim), dtype=torch.bfloat16, device=q.device)
+        self.lse = torch.empty((T, n_q_heads), dtype=torch.float32, device=q.device)
+        need = extend_workspace_bytes(dtype, batch, n_q_heads, n_kv_heads, head_dim, page_size,
+                                      max_pages, max_new_tokens)
+        self.workspace = workspace if workspace is not None else torch.zeros(
+            need, dtype=torch.uint8, device=q.device)
+        pt_stride = page_table.stride(0) if batch > 1 else max_pages
+        self._keep = (q, q_start, k_pool, k_scales, v_pool, v_scales, page_table, seq_lens)
+        self.args = (_dt(dtype), _ptr(q), _ptr(q_start), max_new_tokens, _ptr(k_pool),
+                     _ptr(k_scales), _ptr(v_pool), _ptr(v_scales), _ptr(page_table), pt_stride,
+                     _ptr(seq_lens), batch, n_q_heads, n_kv_heads, head_dim, page_size, max_pages,
+                     num_pages, float(sm_scale), _ptr(self.out), _ptr(self.lse),
+                     _ptr(self.workspace), self.workspace.numel(), _stream(q.device, stream))
+
+    def __call__(self):
+        _check(LIB.kvq_extend_attention(*self.args))
 
 
 class PreparedDecode:

@@ -223,6 +223,24 @@ def single256(seed: int = 3, ctx: int = 262144) -> Workload:
                     np.array([ctx], np.int32), pt, seed)
 
 
+def extend(seed: int = 6, batch: int = 8, ctx: int = 16384, new: int = 64) -> Workload:
+    """The qwen3 decode shape with the last `new` positions of every sequence
+    new: their K/V in the pool, their queries (`extend_queries`) attending
+    causally.  new_tokens["q_start"]: int32 [batch + 1]."""
+    wl = qwen3(seed=seed, batch=batch, ctx=ctx, replicas=1)
+    wl.name = "extend_b%d_ctx%d_new%d_h16x8_d128" % (batch, ctx, new)
+    wl.new_tokens = {"q_start": (np.arange(batch + 1) * new).astype(np.int32)}
+    return wl
+
+
+def extend_queries(wl: Workload, n_tokens: int) -> np.ndarray:
+    """bf16 bits uint16 [n_tokens, n_q_heads, head_dim_qk]: the new tokens'
+    queries, N(0,1), from their own sub-stream."""
+    rng = np.random.Generator(np.random.PCG64([wl.seed, 7]))
+    return to_bf16_bits(rng.standard_normal((n_tokens, wl.n_q_heads, wl.head_dim_qk),
+                                            dtype=np.float32))
+
+
 def mla(seed: int = 4, ctx: int = 163840, n_q_heads: int = 128) -> Workload:
     rng = np.random.Generator(np.random.PCG64([seed, 100]))
     n_pages = (ctx + PAGE - 1) // PAGE
@@ -265,4 +283,4 @@ def mixed(seed: int = 5, batch: int = 64, pool_pages: int = 65536, lo: int = 102
 
 
 BY_NAME = {"tiny": tiny, "qwen3": qwen3, "ragged256": ragged256, "single256": single256,
-           "mla": mla, "mixed": mixed}
+           "mla": mla, "mixed": mixed, "extend": extend}

@@ -133,3 +133,32 @@ def test_only_block_scaled_types_carry_scales():
         rc = kvq.LIB.kvq_store(kvq.DTYPES[dtype], 16, None, 128, 16, 4, 1, 128, 16, 4, 16, None,
                                None, None, None)
         assert rc == kvq.ERR_ARG and "k_scales" in kvq.last_error()
+
+
+def test_extend_validation():
+    """kvq_extend_attention rejects bad shapes and arguments before any launch."""
+    L = kvq.LIB
+    args = dict(q=256, qs=256, kp=256, ks=256, vp=512, vs=512, pt=256, sl=256, out=256, lse=None,
+                wsp=256)
+
+    def call(dtype=1, mn=64, B=2, Hq=16, Hkv=8, D=128, ps=16, mp=8, pts=8, npg=64, ws=1 << 30,
+             sm=0.1, **kw):
+        a = dict(args, **kw)
+        return L.kvq_extend_attention(dtype, a["q"], a["qs"], mn, a["kp"], a["ks"], a["vp"],
+                                      a["vs"], a["pt"], pts, a["sl"], B, Hq, Hkv, D, ps, mp, npg,
+                                      sm, a["out"], a["lse"], a["wsp"], ws, None)
+
+    assert call(mn=0) == kvq.ERR_ARG
+    assert call(mn=70000) == kvq.ERR_UNSUPPORTED and "max_new_tokens" in kvq.last_error()
+    assert call(qs=None) == kvq.ERR_ARG
+    assert call(Hq=12) == kvq.ERR_ARG
+    assert call(D=96) == kvq.ERR_UNSUPPORTED                  # only 64, 128, 256
+    assert call(D=48, dtype=0) == kvq.ERR_UNSUPPORTED
+    assert call(vp=256, vs=256) == kvq.ERR_UNSUPPORTED        # shared slab: decode only
+    assert call(ps=32) == kvq.ERR_UNSUPPORTED
+    assert call(pts=4) == kvq.ERR_ARG
+    assert call(sm=float("inf")) == kvq.ERR_ARG
+    need = kvq.extend_workspace_bytes("fp8_e4m3", 2, 16, 8, 128, 16, 8, 64)
+    assert need > kvq.workspace_bytes("fp8_e4m3", 2, 16, 8, 128, 128, 16, 8)  # 8 tiles per kv head
+    assert call(ws=need - 1) == kvq.ERR_WORKSPACE
+    assert L.kvq_extend_attention_workspace_bytes(1, 1, 128, 1, 576, 16, 8, 4) == 0

@@ -1,0 +1,138 @@
+"""GPU parity of kvq_extend_attention (causal extend / prefill attention over
+the quantized pool) against the oracle's double-precision attention over the
+same pool (filled by the GPU store and the oracle's store from the same rows).
+
+Cases: prefill (every token new), extends after a prefix, a sequence with
+more new tokens than its pool holds (the first ones see nothing), an empty
+sequence, masked pages, query-row tiles that are full, partial or spread over
+several tokens, head_dim 64 / 128 / 256, every storage type, and at the full
+extend shape sampled rows against the oracle's decode of the same query over
+the positions it may see.  Tolerance as the decode: max |o - r| / max |r| <=
+2e-2, lse within 1e-2.
+
+Page keys: [PR103] "feat(kvcache): 8-bit KV cache (q8_0 / fp8_e4m3) behind
+--kv-cache-dtype" (§What: the quantized pool feeds the prefill / extend
+attention kernels); [PR113] "feat(kvcache): 8-bit DSV4 window/compressed KV
+behind --kv-cache-dtype" (§Testing: prefill, masked (-1) columns).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_decode_attention_amd import workloads as W
+from tests.gpu_util import (bf16_to_f64, dev_bf16, dev_i32, fill_both, host_u16, kvq, rel_err,
+                            requires_gpu, say)
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+TOL = 2e-2
+
+
+def ext_workload(Hq, Hkv, D, lens, width, seed, mask_frac=0.0, extra_pages=3):
+    rng = np.random.default_rng(seed)
+    lens = np.array(lens, np.int32)
+    need = sum((int(x) + W.PAGE - 1) // W.PAGE for x in lens)
+    n_pages = need + extra_pages
+    perm = rng.permutation(n_pages).astype(np.int32)
+    pt = np.full((len(lens), width), -1, np.int32)
+    o = 0
+    for b, L in enumerate(lens):
+        n = (int(L) + W.PAGE - 1) // W.PAGE
+        pt[b, :n] = perm[o:o + n]
+        o += n
+        if mask_frac:
+            pt[b, :n][rng.random(n) < mask_frac] = -1
+    return W.Workload("ext_h%dx%d_d%d" % (Hq, Hkv, D), len(lens), Hq, Hkv, D, D, n_pages, lens,
+                      pt, seed)
+
+
+def run(wl, qtype, news, max_new=None, pools=None):
+    k = kvq()
+    pools = pools or fill_both(wl, qtype)
+    q_start = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    T = int(q_start[-1])
+    q = W.extend_queries(wl, T)
+    max_new = max_new or max(1, int(max(news)))
+    say("extend", wl.name, qtype, "news", list(news), "max_new", max_new)
+    out, lse = k.extend_attention(qtype, dev_bf16(q), dev_i32(q_start), max_new, pools["kp"],
+                                  pools["ks"], pools["vp"], pools["vs"], dev_i32(wl.page_table),
+                                  dev_i32(wl.seq_lens), wl.sm_scale)
+    torch.cuda.synchronize()
+    g = bf16_to_f64(host_u16(out)).reshape(-1, wl.head_dim_v)
+    g_lse = lse.cpu().numpy().astype(np.float64).reshape(-1)
+    o, o_lse = oracle.extend_attention(qtype, q, q_start, pools["okp"], pools["oks"], pools["ovp"],
+                                       pools["ovs"], wl.page_table, wl.seq_lens, wl.n_kv_heads,
+                                       wl.head_dim_qk, W.PAGE, wl.num_pages, wl.sm_scale)
+    err = rel_err(g, o)
+    say("  rel err %.3e" % err)
+    assert err <= TOL, err
+    fin = np.isfinite(o_lse)
+    assert np.array_equal(np.isfinite(g_lse), fin)
+    if fin.any():
+        assert np.abs(g_lse[fin] - o_lse[fin]).max() < 1e-2
+    return g, g_lse, o, q_start
+
+
+@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0", "bf16", "fp8_e4m3_cast", "fp8_e5m2_cast"])
+def test_extend_matches_oracle(qtype):
+    """16 q / 8 kv heads, head_dim 128: a 64-token extend after a prefix, a
+    prefill (every token new), a short extend, an empty sequence and more new
+    tokens than the pool holds; masked pages."""
+    wl = ext_workload(16, 8, 128, [700, 130, 64, 0, 5], 48, seed=11, mask_frac=0.1)
+    g, g_lse, o, q_start = run(wl, qtype, [64, 9, 64, 0, 8])
+    Hq = wl.n_q_heads
+    s0 = int(q_start[4])  # sequence 4: 8 new tokens, 5 in the pool -> the first 3 see nothing
+    assert np.all(g[s0 * Hq:(s0 + 3) * Hq] == 0) and np.all(np.isneginf(g_lse[s0 * Hq:(s0 + 3) * Hq]))
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,news", [(8, 2, 64, [3, 1, 2]), (16, 2, 256, [2, 1, 1]),
+                                           (32, 4, 128, [1, 5, 3]), (4, 4, 128, [33, 17, 40])])
+def test_extend_head_groups(Hq, Hkv, D, news):
+    """Tiles of G heads x a few tokens, a partial last tile, one head per kv
+    head (G = 1, 16 tokens per tile)."""
+    wl = ext_workload(Hq, Hkv, D, [400, 77, 1000], 70, seed=Hq + D, mask_frac=0.05)
+    run(wl, "fp8_e4m3", news)
+
+
+def test_extend_max_new_above_every_sequence():
+    wl = ext_workload(16, 8, 128, [300, 90], 30, seed=5)
+    run(wl, "fp8_e4m3", [7, 12], max_new=40)
+
+
+def test_extend_split_sequences_merge():
+    """Long prefixes: a sequence splits into many items per query tile, merged
+    by the last workgroup or the merge kernel."""
+    wl = ext_workload(16, 8, 128, [20000, 9000], 1300, seed=21)
+    run(wl, "fp8_e4m3", [16, 4])
+
+
+def test_extend_full_shape_sampled_rows():
+    """8 sequences x 16384 tokens, the last 64 of each new (the bench shape):
+    sampled new tokens against the oracle's decode of that query over the
+    positions it may see."""
+    wl = W.extend()
+    k = kvq()
+    pools = fill_both(wl, "fp8_e4m3")
+    q_start = wl.new_tokens["q_start"]
+    T = int(q_start[-1])
+    q = W.extend_queries(wl, T)
+    say("extend full shape", wl.name)
+    out, lse = k.extend_attention("fp8_e4m3", dev_bf16(q), dev_i32(q_start), 64, pools["kp"],
+                                  pools["ks"], pools["vp"], pools["vs"], dev_i32(wl.page_table),
+                                  dev_i32(wl.seq_lens), wl.sm_scale)
+    torch.cuda.synchronize()
+    g = bf16_to_f64(host_u16(out)).reshape(T, wl.n_q_heads, -1)
+    g_lse = lse.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(3)
+    for j in sorted(rng.choice(T, 6, replace=False).tolist()) + [0, T - 1]:
+        b = int(np.searchsorted(q_start, j, side="right") - 1)
+        E = int(q_start[b + 1] - q_start[b])
+        pos = int(wl.seq_lens[b]) - E + (j - int(q_start[b]))
+        o, o_lse = oracle.paged_decode("fp8_e4m3", q[j:j + 1], pools["okp"], pools["oks"],
+                                       pools["ovp"], pools["ovs"], wl.page_table[b:b + 1],
+                                       np.array([pos + 1], np.int32), wl.n_kv_heads, 128, 128,
+                                       W.PAGE, wl.num_pages, wl.sm_scale)
+        err = rel_err(g[j], o)
+        assert err <= TOL, (j, err)
+        assert np.abs(g_lse[j] - o_lse).max() < 1e-2
