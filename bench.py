@@ -25,7 +25,9 @@ timed on this host.
 
 Other modes: `--workload ragged256|single256|mla|mixed` times kvq_paged_decode
 alone on that workload and prints its own line; `--workload mla_sparse` times
-kvq_sparse_mla_decode (256 listed positions per query over the mla slab); `--only decode|copy` and
+kvq_sparse_mla_decode (256 listed positions per query over the mla slab);
+`--workload extend` times kvq_extend_attention (the last 64 of 8 x 16384
+tokens new, causal); `--only decode|copy` and
 `--traffic-from DIR` serve the rocprofv3 counter passes (see profiles/).
 """
 from __future__ import annotations
@@ -249,6 +251,19 @@ def decode_only(args, wl, qtype, dev, sparse_k=0) -> int:
             ws = d.workspace
             calls.append(d)
         return sparse_timing(args, wl, qtype, calls, topk_np, strm)
+    if "q_start" in wl.new_tokens:
+        q_start_np = wl.new_tokens["q_start"]
+        T = int(q_start_np[-1])
+        qx = dev_bf16(W.extend_queries(wl, T))
+        qs = torch.from_numpy(q_start_np).to(dev)
+        max_new = int(np.diff(q_start_np).max())
+        strm = torch.cuda.Stream(device=dev)
+        for kp, ks, vp, vs in pools:
+            d = kvq.PreparedExtend(qtype, qx, qs, max_new, kp, ks, vp, vs, pt, sl, wl.sm_scale,
+                                   workspace=ws, stream=strm)
+            ws = d.workspace
+            calls.append(d)
+        return extend_timing(args, wl, qtype, calls, q_start_np, strm)
     for kp, ks, vp, vs in pools:
         d = kvq.PreparedDecode(qtype, q, kp, ks, vp, vs, pt, sl, wl.sm_scale, head_dim_v=Dv,
                                workspace=ws)
@@ -297,6 +312,76 @@ def decode_only(args, wl, qtype, dev, sparse_k=0) -> int:
         res["tflops"] = round(tf, 1)
         res["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
         res["t_roof_us"] = round(max(nbytes / PEAK_GBPS / 1e3, flops / MFMA_BF16_PEAK_TFLOPS / 1e6), 3)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def replay_us(args, calls, strm) -> float:
+    """Microseconds per call: every call (bound to stream strm) captured back
+    to back in one graph, replayed args.steps times between two HIP events."""
+    import torch
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=strm):
+        for c in calls:
+            c()
+    for _ in range(args.warmup):
+        graph.replay()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / (args.steps * len(calls))
+
+
+def extend_timing(args, wl, qtype, calls, q_start, strm) -> int:
+    """Causal extend attention of every sequence's new tokens over the pool."""
+    from paged_decode_attention_amd import kvq
+    from paged_decode_attention_amd import workloads as W
+    us = replay_us(args, calls, strm)
+    H, D, Hq = wl.n_kv_heads, wl.head_dim_qk, wl.n_q_heads
+    E = np.diff(q_start).astype(np.int64)
+    T = int(q_start[-1])
+    # algorithmic bytes: every sequence's K and V rows once, its page-table
+    # entries, the new tokens' Q and O, seq_lens and q_start
+    per_tok = kvq.pool_bytes(qtype, 1, W.PAGE, H, D)[0] / W.PAGE * 2
+    tokens = int(wl.seq_lens.astype(np.int64).sum())
+    nbytes = (tokens * per_tok + 4 * sum((int(L) + W.PAGE - 1) // W.PAGE for L in wl.seq_lens)
+              + T * Hq * D * 2 * 2 + 4 * wl.batch + 4 * (wl.batch + 1))
+    # flops: each new token attends to its position + 1 rows, 2 D flops per
+    # row for q.k and 2 D for p.v, per query head
+    vis = sum(int(np.sum(int(L) - e + np.arange(e) + 1)) for L, e in zip(wl.seq_lens, E))
+    flops = 4.0 * D * Hq * vis
+    t_roof = max(nbytes / 8e12, flops / 2.5e15) * 1e6
+    res = {
+        "metric": "extend attention call time, 1 GPU",
+        "value": round(us, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "higher_is_better": False,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "%s: %d sequences x %d tokens, the last %d of each new (causal), "
+                               "%d q / %d kv heads, head_dim %d" % (
+                                   wl.name, wl.batch, int(wl.seq_lens.max()), int(E.max()), Hq,
+                                   H, D),
+                   "kv_storage": qtype, "replicas": len(calls)},
+        "call_us": round(us, 3),
+        "gbps": round(nbytes / (us * 1e-6) / 1e9, 2),
+        "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+        "t_roof_us": round(t_roof, 3),
+        "roof_frac": round(t_roof / us, 4),
+        "algorithmic_bytes_per_call": int(nbytes),
+        "flops_per_call": flops,
+    }
     print(json.dumps(res), flush=True)
     return 0
 
@@ -364,9 +449,12 @@ def main() -> int:
     ap.add_argument("--qtype", default="fp8_e4m3",
                     choices=["fp8_e4m3", "q8_0", "bf16", "fp8_e4m3_cast", "fp8_e5m2_cast"])
     ap.add_argument("--layers", type=int, default=28)
+    ap.add_argument("--extend-new", type=int, default=64,
+                    help="--workload extend: new tokens per sequence")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="qwen3",
-                    choices=["qwen3", "ragged256", "single256", "mla", "mixed", "mla_sparse"],
+                    choices=["qwen3", "ragged256", "single256", "mla", "mixed", "mla_sparse",
+                             "extend"],
                     help="qwen3 (default) is the decode step this benchmark reports; the others "
                          "time kvq_paged_decode alone on that workload and print their own line")
     ap.add_argument("--replicas", type=int, default=0,
@@ -404,6 +492,8 @@ def main() -> int:
         return 0
     if args.workload == "mla_sparse":
         return decode_only(args, W.mla(), qtype, dev, sparse_k=SPARSE_K)
+    if args.workload == "extend":
+        return decode_only(args, W.extend(new=args.extend_new), qtype, dev)
     if args.workload != "qwen3":
         return decode_only(args, W.BY_NAME[args.workload](), qtype, dev)
     wl = W.qwen3(replicas=args.layers)

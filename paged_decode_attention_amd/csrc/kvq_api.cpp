@@ -197,7 +197,10 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
     if (chunks > (max_pages + min_pages - 1) / min_pages) chunks = (max_pages + min_pages - 1) / min_pages;
     // the last workgroup merges a sequence's partials itself while they are
     // small; beyond that a merge kernel spreads the reads over the GPU
-    p.fused_merge = head_dim_v < 64 ||
+    // (extend attention: many tiles per sequence, so items rarely split; a
+    // merge kernel would launch a block per output row only to find one
+    // chunk)
+    p.fused_merge = ext_new > 0 || head_dim_v < 64 ||
                     chunks * p.gt * head_dim_v * (int64_t)sizeof(float) <= kFusedMergeMaxBytes;
   } else {
     return no("head_dim %d/%d is not supported (separate K/V: 32, 64, 128 or 256 with equal "

@@ -200,7 +200,12 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     const int b = lo;
     const int rem = item - s_prefix[b];
     const int chunk = rem / units, u = rem - chunk * units;
-    const int kvh = u / p.n_hg, hg = u - kvh * p.n_hg;
+    // Units are (kv head, tile of query rows).  Extend attention numbers them
+    // tile-major, so the tiles of one kv head sit n_kv_heads items apart: with
+    // 8 kv heads on the same XCD (blockIdx % 8), where they read the same
+    // pages at about the same time through one L2.
+    const int kvh = EXT ? u % a.n_kv_heads : u / p.n_hg;
+    const int hg = EXT ? u / a.n_kv_heads : u - kvh * p.n_hg;
     const int L = clamped_len(a, b);
     const int nc = (L + item_tokens - 1) / item_tokens;
     const int t0 = chunk * item_tokens;

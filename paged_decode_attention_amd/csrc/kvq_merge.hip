@@ -53,7 +53,9 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_kernel(MergeParams p) {
   __shared__ float s_part[kThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int G = a.n_q_heads / a.n_kv_heads;
-  const int kvh = u / p.n_hg, hg = u - kvh * p.n_hg;
+  // (extend attention numbers its units tile-major)
+  const int kvh = a.q_start ? u % a.n_kv_heads : u / p.n_hg;
+  const int hg = a.q_start ? u / a.n_kv_heads : u - kvh * p.n_hg;
   const int64_t orow = query_row(a, b, kvh, hg * p.gt + h, G);
   if (orow < 0) return;  // a padding column of extend attention
   const int grp = tid / kLanesPerRow, j = tid % kLanesPerRow;
