@@ -157,7 +157,10 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
       const int64_t rows = (int64_t)ext_new * G;
       p.mfma = true;
       p.gt = rows <= 16 ? (int)rows : 16;
-      p.n_hg = (int)((rows + p.gt - 1) / p.gt);
+      // two full tiles per unit up to head_dim 128: every wave computes both
+      // over its pages, so each page is loaded once for 32 query rows
+      p.tn = (rows > 16 && head_dim_qk <= 128) ? 2 : 1;
+      p.n_hg = (int)((rows + p.gt * p.tn - 1) / (p.gt * p.tn));
     } else {
       p.mfma = G >= 8 && head_dim_qk >= 64 && (G <= 16 || G % 16 == 0);
       if (p.mfma)
@@ -175,7 +178,8 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
     const int step = kDecodeWaves * (p.mfma ? 1 : gqa_pages_per_step(qtype, head_dim_qk) * kGqaDepth);
     const int64_t target = (p.mfma ? 2 : 1) * (int64_t)kPlanCUs;
     const int cap = kMaxItemPages / step * step;
-    const int64_t for_merge = ((int64_t)max_pages * p.gt + kMergeMaxWeights - 1) / kMergeMaxWeights;
+    const int64_t for_merge =
+        ((int64_t)max_pages * p.gt * p.tn + kMergeMaxWeights - 1) / kMergeMaxWeights;
     const int64_t min_pages = ((for_merge > step ? for_merge : step) + step - 1) / step * step;
     if (min_pages > cap) return no("max_pages %d is too large for the split-K merge", max_pages);
     p.step = step;
@@ -211,10 +215,10 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
   p.off_prefix = 0;
   p.off_count = align256((size_t)(batch + 1) * sizeof(int));
   p.off_ml = p.off_count + align256((size_t)batch * n_kv_heads * p.n_hg * sizeof(int));
-  p.off_acc = p.off_ml + align256((size_t)p.max_items * p.gt * 2 * sizeof(float));
+  p.off_acc = p.off_ml + align256((size_t)p.max_items * p.gt * p.tn * 2 * sizeof(float));
   // split-K partial outputs: fp32 accumulators (GQA) or bf16 normalized rows (MLA)
   const size_t acc_elem = (p.kind == DK_MLA) ? sizeof(uint16_t) : sizeof(float);
-  p.bytes = p.off_acc + align256((size_t)p.max_items * p.gt * head_dim_v * acc_elem);
+  p.bytes = p.off_acc + align256((size_t)p.max_items * p.gt * p.tn * head_dim_v * acc_elem);
   *plan = p;
   return true;
 }

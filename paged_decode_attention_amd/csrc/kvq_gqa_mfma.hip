@@ -69,13 +69,14 @@ __device__ __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
 struct MfParams {
   DecodeArgs a;
   int gt, n_hg;
+  int tn;            // column tiles per unit (every wave computes each over its pages)
   ItemRule rule;     // work item size (see plan_items)
   int fused;         // merge split-K partials in the last workgroup (else a merge kernel)
   float scale_log2;  // sm_scale * log2(e)
   int* prefix;       // [batch + 1]
   int* count;        // [batch * units] arrival counters, zero between calls
-  float* part_ml;    // [items][gt][2]
-  float* part_acc;   // [items][gt][D]
+  float* part_ml;    // [items][tn * gt][2]
+  float* part_acc;   // [items][tn * gt][D]
 };
 
 template <int QT, int D>
@@ -135,7 +136,10 @@ __device__ __forceinline__ void transpose4x4(const uint32_t* in, uint32_t* out) 
 
 // EXT: extend attention (query rows are new tokens x heads, each with its own
 // causal end); false: the decode, whose item end is uniform over the wave.
-template <int QT, int D, bool EXT>
+// TN: 16-column tiles per unit.  With TN = 2 every wave computes both tiles
+// over its pages, so a page's loads and V dequantization serve 32 query rows
+// (used with full tiles only: gt = 16, so a unit's column h is LDS column h).
+template <int QT, int D, bool EXT, int TN>
 __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   using Gm = MfGeo<QT, D>;
   constexpr int ESZ = Gm::ESZ, NKS = Gm::NKS, NT = Gm::NT, VDW = Gm::VDW, KLD = Gm::KLD;
@@ -147,10 +151,11 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   extern __shared__ int s_prefix[];  // [batch + 1]
   // per-wave (m, l) and O^T accumulators at the end of an item, or the merge's
   // chunk weights
-  constexpr int kRed = (kW * kN * D > kMergeMaxWeights) ? kW * kN * D : kMergeMaxWeights;
+  constexpr int kC = kN * TN;  // columns of a unit
+  constexpr int kRed = (kW * kC * D > kMergeMaxWeights) ? kW * kC * D : kMergeMaxWeights;
   __shared__ float s_red[kRed];
-  __shared__ float s_ml[kW][kN][2];
-  __shared__ float s_hm[kN][2];
+  __shared__ float s_ml[kW][kC][2];
+  __shared__ float s_hm[kC][2];
   __shared__ int s_wave[kW];
   __shared__ int s_last;
 
@@ -159,6 +164,7 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;
   const int GT = p.gt;
+  const int GTU = GT * TN;  // columns of a unit
   const int units = a.n_kv_heads * p.n_hg;
   const int G = a.n_q_heads / a.n_kv_heads;
 
@@ -214,15 +220,22 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     // extend attention: a tile of query rows past the sequence's new tokens
     // has nothing to compute or write (uniform over the block; every chunk
     // of the tile skips, so its split-K counter stays untouched)
-    if (EXT && hg * GT / G >= min(a.q_start[b + 1] - a.q_start[b], a.max_new)) continue;
-    // this lane's query row and the item tokens it may attend to (the
-    // decode's: the item's own tokens, a wave-uniform bound)
-    const int64_t qrow_lane = (n16 < GT) ? (EXT ? query_row(a, b, kvh, hg * GT + n16, G)
-                                                : (int64_t)b * a.n_q_heads + kvh * G + hg * GT + n16)
-                                         : -1;
-    int col_lim = nt;
-    if constexpr (EXT)
-      col_lim = (n16 < GT) ? max(min(nt, query_end(a, b, L, hg * GT + n16, G) - t0), 0) : 0;
+    const int col0 = hg * GTU;  // the unit's first column of the kv head's query rows
+    if (EXT && col0 / G >= min(a.q_start[b + 1] - a.q_start[b], a.max_new)) continue;
+    // this lane's query rows (one per tile) and the item tokens each may attend
+    // to (the decode's: the item's own tokens, a wave-uniform bound)
+    int64_t qrow_lane[TN];
+    int col_lim[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const int col = col0 + t * GT + n16;
+      qrow_lane[t] = (n16 < GT) ? (EXT ? query_row(a, b, kvh, col, G)
+                                       : (int64_t)b * a.n_q_heads + kvh * G + col)
+                                : -1;
+      col_lim[t] = nt;
+      if constexpr (EXT)
+        col_lim[t] = (n16 < GT) ? max(min(nt, query_end(a, b, L, col, G) - t0), 0) : 0;
+    }
     const int nsteps = (np > wave) ? (np - wave + kW - 1) / kW : 0;  // pages of this wave
 
     // page ids of this wave's steps: lane k holds the id of step k (page
@@ -242,24 +255,27 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     // every path through it issues the same loads
     const int nst = max((nsteps + NBUF - 1) / NBUF * NBUF, NBUF);
 
-    // Q^T operands: qb[ks] = the query row of column n16, elements 32ks + 8g ..
-    // +7 (0 for padding columns)
-    u32x4 qb[NKS];
+    // Q^T operands: qb[t][ks] = the query row of column n16 of tile t,
+    // elements 32ks + 8g .. +7 (0 for padding columns)
+    u32x4 qb[TN][NKS];
     {
-      const bool real = qrow_lane >= 0;
       // the elements of block ks that lane group g holds in the K operand:
       // 32 ks + 8 g (bf16), or after the 8-bit lane swap 32 ks + (0, 16, 8, 24)[g]
       const int goff = (ESZ == 1) ? 16 * (g & 1) + 8 * (g >> 1) : 8 * g;
-      // a padding column reads the tile's first row (it exists: tiles with
-      // no row are skipped above) and zeroes it
-      const int64_t row0 = EXT ? query_row(a, b, kvh, hg * GT, G)
-                               : (int64_t)b * a.n_q_heads + kvh * G + hg * GT;
-      const uint16_t* qrow = a.q + (real ? qrow_lane : row0) * D + goff;
+      // a padding column reads the unit's first row (it exists: units with no
+      // row are skipped above) and zeroes it
+      const int64_t row0 = EXT ? query_row(a, b, kvh, col0, G)
+                               : (int64_t)b * a.n_q_heads + kvh * G + col0;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
-        if (!real) v = u32x4{0, 0, 0, 0};
-        qb[ks] = v;
+      for (int t = 0; t < TN; ++t) {
+        const bool real = qrow_lane[t] >= 0;
+        const uint16_t* qrow = a.q + (real ? qrow_lane[t] : row0) * D + goff;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
+          if (!real) v = u32x4{0, 0, 0, 0};
+          qb[t][ks] = v;
+        }
       }
     }
 
@@ -290,19 +306,28 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     };
 
     // ---- S^T = K Q^T of one page: log2-domain scores of tokens 4g .. 4g+3 of
-    // the page for head n16, -inf past the item end or on a masked page ----------
-    auto scores = [&](int st, int pid, const Raw& R, float* s, bool* ok) {
+    // the page for column n16 of each tile, -inf past the column's end or on
+    // a masked page; ok: the token exists ---------------------------------------
+    auto scores = [&](int st, int pid, const Raw& R, float (*s)[4], bool* ok) {
       if constexpr (QT == QT_BF16) {
-        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+        f32x4 S[TN];
+#pragma unroll
+        for (int t = 0; t < TN; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-          S = mfma_k32(u32x4{R.k[ks][0], R.k[ks][1], R.k[ks][2], R.k[ks][3]}, qb[ks], S);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] = S[r];
+          for (int t = 0; t < TN; ++t)
+            S[t] = mfma_k32(u32x4{R.k[ks][0], R.k[ks][1], R.k[ks][2], R.k[ks][3]}, qb[t][ks], S[t]);
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[t][r] = S[t][r];
       } else if constexpr (!qt_scaled(QT)) {
         // cast codes (no scales): one product chain over the k-steps, the
         // codes handed to the lane groups as below
-        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+        f32x4 S[TN];
+#pragma unroll
+        for (int t = 0; t < TN; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           const int m = ks >> 1;
@@ -312,18 +337,24 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
           uint32_t kb[4];
           decode_dword_bf16x2<QT>(c0, kb);
           decode_dword_bf16x2<QT>(c1, kb + 2);
-          S = mfma_k32(u32x4{kb[0], kb[1], kb[2], kb[3]}, qb[ks], S);
+#pragma unroll
+          for (int t = 0; t < TN; ++t)
+            S[t] = mfma_k32(u32x4{kb[0], kb[1], kb[2], kb[3]}, qb[t][ks], S[t]);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] = S[r];
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[t][r] = S[t][r];
       } else {
         // one product tile per scale block, in groups of four live tiles
         constexpr int GS = NKS < 4 ? NKS : 4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] = 0.0f;
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[t][r] = 0.0f;
 #pragma unroll
         for (int k0 = 0; k0 < NKS; k0 += GS) {
-          f32x4 Sk[GS];
+          f32x4 Sk[TN][GS];
 #pragma unroll
           for (int k = 0; k < GS; ++k) {
             // block ks = 2m + j: lanes 0-31 hold 16 codes of block 2m, lanes
@@ -337,7 +368,10 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
             uint32_t kb[4];
             decode_dword_bf16x2<QT>(c0, kb);
             decode_dword_bf16x2<QT>(c1, kb + 2);
-            Sk[k] = mfma_k32(u32x4{kb[0], kb[1], kb[2], kb[3]}, qb[k0 + k], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+              Sk[t][k] = mfma_k32(u32x4{kb[0], kb[1], kb[2], kb[3]}, qb[t][k0 + k],
+                                  f32x4{0.f, 0.f, 0.f, 0.f});
           }
 #pragma unroll
           for (int k = 0; k < GS; ++k) {
@@ -347,38 +381,47 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
               // scale (r, ks) is fp16 number r NKS + ks of the row's run
               const int idx = r * NKS + ks;
               const uint32_t w = row_bcast(R.ks, idx >> 1);
-              s[r] = fmaf(f16_bits_to_f32((uint16_t)(w >> ((idx & 1) * 16))), Sk[k][r], s[r]);
+              const float sc = f16_bits_to_f32((uint16_t)(w >> ((idx & 1) * 16)));
+#pragma unroll
+              for (int t = 0; t < TN; ++t) s[t][r] = fmaf(sc, Sk[t][k][r], s[t][r]);
             }
           }
         }
       }
       const int tok0 = (wave + st * kW) * kPageSize + 4 * g;  // token of r = 0 in the item
       // ok: the token exists (its V rows are used, masked to zero otherwise);
-      // the score is kept only below this lane's column end as well.  A
-      // lane's V registers hold rows of other columns' products, so the V
-      // mask must not depend on the column.  (Selects, not branches around
-      // the page's work.)
+      // a score is kept only below its column's end as well.  A lane's V
+      // registers hold rows of other columns' products, so the V mask must
+      // not depend on the column.  (Selects, not branches around the page's
+      // work.)
       const int lim = pid >= 0 ? nt : 0;
-      const int slim = pid >= 0 ? col_lim : 0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        ok[r] = tok0 + r < lim;
-        s[r] = (tok0 + r < slim) ? s[r] * p.scale_log2 : -INFINITY;
+      for (int r = 0; r < 4; ++r) ok[r] = tok0 + r < lim;
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int slim = pid >= 0 ? col_lim[t] : 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s[t][r] = (tok0 + r < slim) ? s[t][r] * p.scale_log2 : -INFINITY;
       }
     };
 
     // ---- weights against the fixed reference, O^T += V^T P^T -------------------
-    float mref, lsum, smax;  // for head n16 (the same in every lane group)
-    f32x4 acc[NT];
-    auto accumulate = [&](const Raw& R, const float* s, const bool* ok) {
-      float pr[4];
+    float mref[TN], lsum[TN], smax[TN];  // for column n16 of each tile (the same in every lane group)
+    f32x4 acc[TN][NT];
+    auto accumulate = [&](const Raw& R, const float (*s)[4], const bool* ok) {
+      u32x2 pt[TN];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        smax = fmaxf(smax, s[r]);
-        pr[r] = __builtin_amdgcn_exp2f(s[r] - mref);  // 0 for a -inf score
-        lsum += pr[r];
+      for (int t = 0; t < TN; ++t) {
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          smax[t] = fmaxf(smax[t], s[t][r]);
+          pr[r] = __builtin_amdgcn_exp2f(s[t][r] - mref[t]);  // 0 for a -inf score
+          lsum[t] += pr[r];
+        }
+        pt[t] = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
       }
-      const u32x2 pt = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
       // tokens past the item end or on a masked page: codes and scale zeroed
       // (their probability is 0, but the slot may hold NaN codes)
       // (masks, not branches, so the page's work stays one scheduling region)
@@ -397,8 +440,11 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
                                  __builtin_amdgcn_perm(w[3][k], w[2][k], 0x05040100u)};
           const u32x2 e1 = u32x2{__builtin_amdgcn_perm(w[1][k], w[0][k], 0x07060302u),
                                  __builtin_amdgcn_perm(w[3][k], w[2][k], 0x07060302u)};
-          acc[2 * k] = mfma_k16(e0, pt, acc[2 * k]);
-          acc[2 * k + 1] = mfma_k16(e1, pt, acc[2 * k + 1]);
+#pragma unroll
+          for (int t = 0; t < TN; ++t) {
+            acc[t][2 * k] = mfma_k16(e0, pt[t], acc[t][2 * k]);
+            acc[t][2 * k + 1] = mfma_k16(e1, pt[t], acc[t][2 * k + 1]);
+          }
         }
       } else {
         float sv[4];
@@ -427,71 +473,88 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
               decode_dword_bf16x2<QT>(col[c], pr2);
               e = u32x2{pr2[0], pr2[1]};
             }
-            acc[4 * k + c] = mfma_k16(e, pt, acc[4 * k + c]);
+#pragma unroll
+            for (int t = 0; t < TN; ++t) acc[t][4 * k + c] = mfma_k16(e, pt[t], acc[t][4 * k + c]);
           }
         }
       }
     };
 
     // ---- stream this wave's pages, NBUF pages' loads in flight ---------------------
-    // The softmax reference of head n16 stays fixed over the pass: the largest
+    // The softmax reference of a column stays fixed over the pass: the largest
     // score of the wave's first page (0 when it has none).  Weights 2^(s -
     // mref) then need no running-max update, no cross-lane reduction and no
     // rescaling of the accumulators.  A pass whose largest score ends up more
     // than 2^64 away from the reference (the weights could overflow, or every
     // weight underflow) is streamed again with that score as the reference.
     Raw R[NBUF];
-    float M;  // largest score of head n16 over the wave's pages
+    float M[TN];  // largest score of column n16 of each tile over the wave's pages
     for (int pass = 0;; ++pass) {
 #pragma unroll
       for (int k = 0; k < NBUF; ++k) load_page(pid_of(k), R[k]);
       if (pass == 0) {
-        float s0[4];
+        float s0[TN][4];
         bool ok0[4];
         scores(0, pid_of(0), R[0], s0, ok0);
-        float t = fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3]));
-        t = max_xor32(max_xor16(t));
-        mref = (t == -INFINITY) ? 0.0f : t;
-      }
-      lsum = 0.0f;
-      smax = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < TN; ++t) {
+          float x = fmaxf(fmaxf(s0[t][0], s0[t][1]), fmaxf(s0[t][2], s0[t][3]));
+          x = max_xor32(max_xor16(x));
+          mref[t] = (x == -INFINITY) ? 0.0f : x;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        lsum[t] = 0.0f;
+        smax[t] = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
       for (int st = 0; st < nst; st += NBUF) {
 #pragma unroll
         for (int k = 0; k < NBUF; ++k) {
-          float s[4];
+          float s[TN][4];
           bool ok[4];
           scores(st + k, pid_of(st + k), R[k], s, ok);
           accumulate(R[k], s, ok);
           load_page(pid_of(st + k + NBUF), R[k]);
         }
       }
-      M = max_xor32(max_xor16(smax));
-      const bool redo = M != -INFINITY && (M > mref + 64.0f || M < mref - 64.0f);
+      bool redo = false;
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        M[t] = max_xor32(max_xor16(smax[t]));
+        redo |= M[t] != -INFINITY && (M[t] > mref[t] + 64.0f || M[t] < mref[t] - 64.0f);
+      }
       if (!__builtin_amdgcn_ballot_w64(redo)) break;
-      mref = (M == -INFINITY) ? 0.0f : M;
+#pragma unroll
+      for (int t = 0; t < TN; ++t) mref[t] = (M[t] == -INFINITY) ? 0.0f : M[t];
     }
-    // a head with no valid token here contributes nothing to the merges
-    const float m = (M == -INFINITY) ? -INFINITY : mref;
+    // a column with no valid token here contributes nothing to the merges
+    float m[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) m[t] = (M[t] == -INFINITY) ? -INFINITY : mref[t];
 
     // ---- merge the four waves ---------------------------------------------------------
-    lsum = sum_xor32(sum_xor16(lsum));
+#pragma unroll
+    for (int t = 0; t < TN; ++t) lsum[t] = sum_xor32(sum_xor16(lsum[t]));
     __syncthreads();  // s_red / s_ml of the previous item are free
-    // O^T tile i, lane (head n16, group g), row 4g + r is dv (D/16)(4g + r) + i
-    {
-      float* dst = s_red + (wave * kN + n16) * D;
+    // O^T tile i, lane (column n16, group g), row 4g + r is dv (D/16)(4g + r) + i;
+    // LDS column t kN + n16 (= the unit's column: gt = 16 whenever TN > 1)
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      float* dst = s_red + (wave * kC + t * kN + n16) * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int i = 0; i < NT; ++i) dst[(D / 16) * (4 * g + r) + i] = acc[i][r];
+        for (int i = 0; i < NT; ++i) dst[(D / 16) * (4 * g + r) + i] = acc[t][i][r];
       if (g == 0) {
-        s_ml[wave][n16][0] = m;
-        s_ml[wave][n16][1] = lsum;
+        s_ml[wave][t * kN + n16][0] = m[t];
+        s_ml[wave][t * kN + n16][1] = lsum[t];
       }
     }
     __syncthreads();
-    if (tid < kN) {
+    if (tid < kC) {
       float M = s_ml[0][tid][0];
 #pragma unroll
       for (int w = 1; w < kW; ++w) M = fmaxf(M, s_ml[w][tid][0]);
@@ -502,25 +565,25 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
       s_hm[tid][1] = Ls;
     }
     __syncthreads();
-    for (int idx = tid; idx < GT * D; idx += kT) {
+    for (int idx = tid; idx < GTU * D; idx += kT) {
       const int h = idx / D, d = idx - h * D;
       const float M = s_hm[h][0];
       float v = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kW; ++w) v += exp2_rel(s_ml[w][h][0], M) * s_red[(w * kN + h) * D + d];
+      for (int w = 0; w < kW; ++w) v += exp2_rel(s_ml[w][h][0], M) * s_red[(w * kC + h) * D + d];
       if (nc == 1) {
         const float Ls = s_hm[h][1];
-        const int64_t orow = EXT ? query_row(a, b, kvh, hg * GT + h, G)
-                                 : (int64_t)b * a.n_q_heads + kvh * G + hg * GT + h;
+        const int64_t orow = EXT ? query_row(a, b, kvh, col0 + h, G)
+                                 : (int64_t)b * a.n_q_heads + kvh * G + col0 + h;
         if (orow >= 0) {
           a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
           if (d == 0 && a.lse) a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
         }
       } else {
-        store_agent(&p.part_acc[((int64_t)item * GT + h) * D + d], v);
+        store_agent(&p.part_acc[((int64_t)item * GTU + h) * D + d], v);
         if (d == 0) {
-          store_agent(&p.part_ml[((int64_t)item * GT + h) * 2 + 0], M);
-          store_agent(&p.part_ml[((int64_t)item * GT + h) * 2 + 1], s_hm[h][1]);
+          store_agent(&p.part_ml[((int64_t)item * GTU + h) * 2 + 0], M);
+          store_agent(&p.part_ml[((int64_t)item * GTU + h) * 2 + 1], s_hm[h][1]);
         }
       }
     }
@@ -538,20 +601,20 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
       __syncthreads();
       if (s_last) {
         const int first = s_prefix[b] + u;  // item of chunk c: first + c * units
-        for (int idx = tid; idx < nc * GT; idx += kT) {
-          const int c = idx / GT, h = idx - c * GT;
-          s_red[idx] = load_agent(&p.part_ml[((int64_t)(first + c * units) * GT + h) * 2]);
+        for (int idx = tid; idx < nc * GTU; idx += kT) {
+          const int c = idx / GTU, h = idx - c * GTU;
+          s_red[idx] = load_agent(&p.part_ml[((int64_t)(first + c * units) * GTU + h) * 2]);
         }
         __syncthreads();
-        for (int h = wave; h < GT; h += kW) {
+        for (int h = wave; h < GTU; h += kW) {
           float M = -INFINITY;
-          for (int c = lane; c < nc; c += 64) M = fmaxf(M, s_red[c * GT + h]);
+          for (int c = lane; c < nc; c += 64) M = fmaxf(M, s_red[c * GTU + h]);
           M = stride_max<1>(M);
           float Ls = 0.0f;
           for (int c = lane; c < nc; c += 64) {
-            const float w = exp2_rel(s_red[c * GT + h], M);
-            Ls += w * load_agent(&p.part_ml[((int64_t)(first + c * units) * GT + h) * 2 + 1]);
-            s_red[c * GT + h] = w;
+            const float w = exp2_rel(s_red[c * GTU + h], M);
+            Ls += w * load_agent(&p.part_ml[((int64_t)(first + c * units) * GTU + h) * 2 + 1]);
+            s_red[c * GTU + h] = w;
           }
           Ls = stride_sum<1>(Ls);
           if (lane == 0) {
@@ -560,10 +623,10 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
           }
         }
         __syncthreads();
-        for (int idx = tid; idx < GT * D; idx += kT) {
+        for (int idx = tid; idx < GTU * D; idx += kT) {
           const int h = idx / D, d = idx - h * D;
-          const float* src = p.part_acc + ((int64_t)first * GT + h) * D + d;
-          const int64_t cstride = (int64_t)units * GT * D;
+          const float* src = p.part_acc + ((int64_t)first * GTU + h) * D + d;
+          const int64_t cstride = (int64_t)units * GTU * D;
           float v = 0.0f;
           for (int c0 = 0; c0 < nc; c0 += 16) {
             float x[16];
@@ -571,11 +634,11 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
             for (int j = 0; j < 16; ++j) x[j] = (c0 + j < nc) ? load_agent(src + (c0 + j) * cstride) : 0.0f;
 #pragma unroll
             for (int j = 0; j < 16; ++j)
-              if (c0 + j < nc) v += s_red[(c0 + j) * GT + h] * x[j];
+              if (c0 + j < nc) v += s_red[(c0 + j) * GTU + h] * x[j];
           }
           const float M = s_hm[h][0], Ls = s_hm[h][1];
-          const int64_t orow = EXT ? query_row(a, b, kvh, hg * GT + h, G)
-                                   : (int64_t)b * a.n_q_heads + kvh * G + hg * GT + h;
+          const int64_t orow = EXT ? query_row(a, b, kvh, col0 + h, G)
+                                   : (int64_t)b * a.n_q_heads + kvh * G + col0 + h;
           if (orow >= 0) {
             a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
             if (d == 0 && a.lse)
@@ -593,10 +656,14 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
 template <int QT, int D>
 hipError_t launch_d(const MfParams& mp, int grid, hipStream_t s) {
   const size_t dyn = (size_t)(mp.a.batch + 1) * sizeof(int);
-  if (mp.a.q_start)
-    gqa_mfma_kernel<QT, D, true><<<grid, kT, dyn, s>>>(mp);
-  else
-    gqa_mfma_kernel<QT, D, false><<<grid, kT, dyn, s>>>(mp);
+  if (mp.a.q_start && mp.tn == 2) {
+    if constexpr (D <= 128) gqa_mfma_kernel<QT, D, true, 2><<<grid, kT, dyn, s>>>(mp);
+    else return hipErrorInvalidValue;  // the planner uses two tiles only up to head_dim 128
+  } else if (mp.a.q_start) {
+    gqa_mfma_kernel<QT, D, true, 1><<<grid, kT, dyn, s>>>(mp);
+  } else {
+    gqa_mfma_kernel<QT, D, false, 1><<<grid, kT, dyn, s>>>(mp);
+  }
   return hipGetLastError();
 }
 
@@ -618,6 +685,7 @@ hipError_t launch_gqa_mfma_decode(const DecodeArgs& a, const DecodePlan& plan, i
   mp.a = a;
   mp.gt = plan.gt;
   mp.n_hg = plan.n_hg;
+  mp.tn = plan.tn;
   mp.rule = ItemRule{plan.step, plan.min_pages, plan.cap_pages, plan.target};
   mp.fused = plan.fused_merge ? 1 : 0;
   mp.scale_log2 = a.sm_scale * kLog2e;

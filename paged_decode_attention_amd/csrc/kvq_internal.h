@@ -93,7 +93,8 @@ enum DecodeKind { DK_GQA = 0, DK_MLA = 1 };
 
 struct DecodePlan {
   int kind;
-  int gt;             // query heads per work item
+  int gt;             // query heads (columns) per tile
+  int tn = 1;         // tiles per work item (extend attention: 2 when they fill)
   int n_hg;           // head groups per kv head (G / gt)
   int item_pages;     // pages per split-K work item (the MLA slab; GQA: the smallest)
   // GQA: the kernels size work items from the actual lengths, about `target`
