@@ -80,3 +80,59 @@ def test_captured_step_replays_match_eager():
         x = torch.randn(256, 256, device="cuda")
         (x @ x).sum().item()
         torch.cuda.synchronize()
+
+
+def test_captured_extend_and_sparse_replay_match_eager():
+    """Extend attention (split units merged by their last workgroup, whose
+    arrival counters reset themselves) and the sparse MLA decode (gather, slab
+    decode, merge) captured once and replayed: every replay reproduces the
+    eager outputs bit for bit."""
+    k = kvq()
+    torch.cuda.synchronize()
+    strm = torch.cuda.Stream()
+    # extend: 3 sequences, long enough that units split into several items
+    wl = W.qwen3(batch=3, ctx=6000, replicas=1)
+    slots = torch.arange(wl.n_slots, dtype=torch.int32, device="cuda")
+    kp, ks = k.alloc_pool("fp8_e4m3", wl.num_pages, 8, 128)
+    vp, vs = k.alloc_pool("fp8_e4m3", wl.num_pages, 8, 128)
+    k.store("fp8_e4m3", dev_bf16(wl.kv_rows(0, 0, wl.n_slots)), dev_bf16(wl.kv_rows(1, 0, wl.n_slots)),
+            slots, kp, ks, vp, vs)
+    news = np.array([20, 3, 40], np.int32)
+    q_start = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    ext = k.PreparedExtend("fp8_e4m3", dev_bf16(W.extend_queries(wl, int(q_start[-1]))),
+                           dev_i32(q_start), int(news.max()), kp, ks, vp, vs,
+                           dev_i32(wl.page_table), dev_i32(wl.seq_lens), wl.sm_scale, stream=strm)
+    # sparse: 2 queries over an MLA slab
+    ml = W.mla(ctx=3000, n_q_heads=64)
+    mslots = torch.arange(ml.n_slots, dtype=torch.int32, device="cuda")
+    sp, ss = k.alloc_pool("fp8_e4m3", ml.num_pages, 1, 576)
+    k.store("fp8_e4m3", dev_bf16(ml.kv_rows(0, 0, ml.n_slots)), None, mslots, sp, ss)
+    rng = np.random.default_rng(9)
+    topk = np.stack([rng.choice(3000, 200, replace=False) for _ in range(1)]).astype(np.int32)
+    spa = k.PreparedSparse("fp8_e4m3", dev_bf16(ml.query()), sp, ss, dev_i32(ml.page_table),
+                           dev_i32(ml.seq_lens), dev_i32(topk), ml.sm_scale, stream=strm)
+    calls = [ext, spa]
+    torch.cuda.synchronize()
+    say("graph: eager extend + sparse")
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    ref = [(c.out.clone(), c.lse.clone()) for c in calls]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=strm):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for c in calls:
+            c.out.fill_(3)
+            c.lse.zero_()
+        torch.cuda.synchronize()
+        say("graph: replay", rep)
+        graph.replay()
+        torch.cuda.synchronize()
+        for (o, l), c in zip(ref, calls):
+            assert torch.equal(c.out, o) and torch.equal(c.lse, l), rep
+        x = torch.randn(256, 256, device="cuda")
+        (x @ x).sum().item()
+        torch.cuda.synchronize()
