@@ -136,3 +136,36 @@ def test_extend_full_shape_sampled_rows():
         err = rel_err(g[j], o)
         assert err <= TOL, (j, err)
         assert np.abs(g_lse[j] - o_lse).max() < 1e-2
+
+
+def test_extend_rows_past_max_new_untouched_and_empty_pool_zeroed():
+    """A sequence with more new tokens than max_new_tokens: its first
+    max_new rows are computed (at their true positions), the rest are left
+    as they were.  A sequence whose pool is empty but lists new tokens: those
+    rows are 0 with lse -inf (no work item covers it)."""
+    k = kvq()
+    wl = ext_workload(16, 8, 128, [300, 0, 90], 20, seed=8)
+    pools = fill_both(wl, "fp8_e4m3")
+    news = [6, 3, 4]
+    q_start = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    T = int(q_start[-1])
+    q = W.extend_queries(wl, T)
+    out = torch.full((T, 16, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, 16), 5.0, dtype=torch.float32, device="cuda")
+    say("extend max_new 4 with 6 new tokens")
+    k.extend_attention("fp8_e4m3", dev_bf16(q), dev_i32(q_start), 4, pools["kp"], pools["ks"],
+                       pools["vp"], pools["vs"], dev_i32(wl.page_table), dev_i32(wl.seq_lens),
+                       wl.sm_scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    g = bf16_to_f64(host_u16(out)).reshape(T, 16, 128)
+    gl = lse.cpu().numpy().astype(np.float64)
+    o, ol = oracle.extend_attention("fp8_e4m3", q, q_start, pools["okp"], pools["oks"],
+                                    pools["ovp"], pools["ovs"], wl.page_table, wl.seq_lens, 8, 128,
+                                    W.PAGE, wl.num_pages, wl.sm_scale)
+    o = o.reshape(T, 16, 128)
+    ol = ol.reshape(T, 16)
+    written = [0, 1, 2, 3] + [9, 10, 11, 12]          # sequences 0 (first 4) and 2
+    assert rel_err(g[written], o[written]) <= TOL
+    assert np.abs(gl[written] - ol[written]).max() < 1e-2
+    assert np.all(g[4:6] == 7.0) and np.all(gl[4:6] == 5.0)   # past max_new: untouched
+    assert np.all(g[6:9] == 0) and np.all(np.isneginf(gl[6:9]))  # empty pool
