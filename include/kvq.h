@@ -282,7 +282,8 @@ size_t kvq_extend_attention_workspace_bytes(kvq_dtype dtype, int batch, int n_q_
  *                kvq_extend_attention_workspace_bytes(): zeroed once, left at
  *                zero by every call; calls sharing it must not overlap.
  * The query rows of a kv head (token-major, max_new_tokens x G of them) run on
- * the matrix cores in tiles of 16; each tile streams the sequence's K/V once.
+ * the matrix cores in tiles of 16, two tiles per work item up to head_dim 128;
+ * each work item streams the K/V of its token range once for its tiles.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP;
  * validation completes before any launch. */
 int kvq_extend_attention(kvq_dtype dtype, const void* q, const int32_t* q_start,

@@ -30,6 +30,13 @@
 // flight; the waves are merged through LDS at the end of a work item, and
 // split-K items are merged by the last workgroup of their (sequence, kv
 // head, head group), as in the VALU kernel.
+//
+// The same kernel runs causal extend (prefill) attention [PR103 §What: the
+// quantized pool feeds the prefill / extend kernels as well; PR113 §Testing:
+// prefill]: a kv head's query rows are then its sequence's new tokens x G
+// heads (token-major), 16 of them per column tile, each column with its own
+// causal end; up to head_dim 128 a work item carries two tiles, computed by
+// every wave over the same pages.
 #include "kvq_attn.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -39,7 +46,7 @@ namespace {
 
 constexpr int kW = kDecodeWaves;
 constexpr int kT = 64 * kW;
-constexpr int kN = 16;  // heads per MFMA column tile
+constexpr int kN = 16;  // query rows (heads, or new tokens x heads) per MFMA column tile
 
 // Lane j of each row of 16 lanes, to every lane of the row (DPP row_newbcast).
 // j is a constant once the callers' loops are unrolled; the switch folds.
@@ -174,7 +181,8 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     for (int b = tid; b <= a.batch; b += kT) p.prefix[b] = s_prefix[b];
   for (int b = blockIdx.x; b < a.batch; b += gridDim.x) {
     if (s_prefix[b] != s_prefix[b + 1]) continue;
-    // its query rows: one per head (decode), or per head of each new token
+    // a sequence without work items (no valid length): its query rows, one
+    // per head (decode) or per head of each new token (extend), are 0 / -inf
     int64_t r0 = (int64_t)b * a.n_q_heads, nr = a.n_q_heads;
     if (a.q_start) {
       r0 = (int64_t)a.q_start[b] * a.n_q_heads;
