@@ -280,7 +280,10 @@ size_t kvq_extend_attention_workspace_bytes(kvq_dtype dtype, int batch, int n_q_
  *                [T][n_q_heads] or NULL.
  *   workspace  : as kvq_paged_decode, sized by
  *                kvq_extend_attention_workspace_bytes(): zeroed once, left at
- *                zero by every call; calls sharing it must not overlap.
+ *                zero by every call; calls sharing it must not overlap.  It
+ *                holds split-K partials for every tile and grows linearly with
+ *                max_new_tokens (8 sequences x 1024 pages, 16/8 heads, head_dim
+ *                128: 21 MB at 64 new tokens, 1.4 GB at 4096).
  * The query rows of a kv head (token-major, max_new_tokens x G of them) run on
  * the matrix cores in tiles of 16, two tiles per work item up to head_dim 128;
  * each work item streams the K/V of its token range once for its tiles.
