@@ -22,9 +22,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "kvq_oracle.c")
 LIB = os.path.join(HERE, "libkvq_oracle.so")
 
-BF16, FP8_E4M3, Q8_0, FP8_E4M3_CAST, FP8_E5M2_CAST = 0, 1, 2, 3, 4
+BF16, FP8_E4M3, Q8_0, FP8_E4M3_CAST, FP8_E5M2_CAST, FP8_DS_MLA = 0, 1, 2, 3, 4, 5
 QTYPES = {"bf16": BF16, "fp8_e4m3": FP8_E4M3, "q8_0": Q8_0, "fp8_e4m3_cast": FP8_E4M3_CAST,
-          "fp8_e5m2_cast": FP8_E5M2_CAST}
+          "fp8_e5m2_cast": FP8_E5M2_CAST, "fp8_ds_mla": FP8_DS_MLA}
+# the 656-byte MLA row: 512 e4m3 codes, 4 fp32 scales (one per 128), 64 bf16 rope
+DS_ROW = 656
 # storage types with a scale buffer beside the pool
 SCALED = ("fp8_e4m3", "q8_0")
 

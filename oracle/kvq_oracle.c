@@ -43,6 +43,17 @@
  * with scale 1.0; §Summary: fp8_e4m3 or fp8_e5m2]. */
 #define KVO_FP8_E4M3_CAST 3
 #define KVO_FP8_E5M2_CAST 4
+/* The 656-byte MLA row [PR25 "Experimental FP8 KV Cache": a 656-byte fp8 row
+ * for the 576-wide latent, laid out as in vLLM].  The page does not give the
+ * fields; the reading taken: bytes 0..511 the e4m3fn codes of latent elements
+ * 0..511, bytes 512..527 four fp32 scales (scale j for elements 128j ..
+ * 128j+127, amax/448 rounded once to fp32), bytes 528..655 the 64 rope
+ * elements as bf16, unquantized.  One such row per token (n_heads = 1,
+ * head_dim = 576), no scale buffer. */
+#define KVO_FP8_DS_MLA 5
+#define KVO_DS_ROW 656
+#define KVO_DS_LATENT 512
+#define KVO_DS_TILE 128
 
 /* Quantization block length along head_dim, and the two format maxima:
  * 448 is the largest finite e4m3 magnitude, 127 the int8 limit [PR103 §What;
@@ -344,6 +355,28 @@ static void kvo_store_unit(void* p, int64_t n) {
         c->pool[r * c->head_dim + d] = kvo_cast_encode(c->qtype, (float)kvo_bf16_value(row[d]));
       continue;
     }
+    if (c->qtype == KVO_FP8_DS_MLA) {
+      /* per 128-element tile of the latent: s = amax / 448 in fp32, each
+       * element's fp32 quotient x / s clamped and rounded to nearest even on
+       * the e4m3fn grid; a zero tile stores s = 0 and zero codes; the rope
+       * part is copied */
+      uint8_t* rp = c->pool + r * KVO_DS_ROW;
+      for (int j = 0; j < KVO_DS_LATENT / KVO_DS_TILE; ++j) {
+        float amax = 0.0f;
+        for (int e = 0; e < KVO_DS_TILE; ++e) {
+          float a = fabsf((float)kvo_bf16_value(row[j * KVO_DS_TILE + e]));
+          if (a > amax) amax = a;
+        }
+        float sc = amax / KVO_E4M3_MAX;
+        for (int e = 0; e < KVO_DS_TILE; ++e) {
+          float x = (float)kvo_bf16_value(row[j * KVO_DS_TILE + e]);
+          rp[j * KVO_DS_TILE + e] = (sc > 0.0f) ? kvo_e4m3_encode(x / sc) : 0;
+        }
+        memcpy(rp + KVO_DS_LATENT + 4 * j, &sc, 4);
+      }
+      memcpy(rp + KVO_DS_LATENT + 16, row + KVO_DS_LATENT, (size_t)(c->head_dim - KVO_DS_LATENT) * 2);
+      continue;
+    }
     for (int j = 0; j < nb; ++j)
       kvo_quantize_block(c->qtype, row + j * KVO_BLOCK, KVO_BLOCK,
                          c->pool + r * c->head_dim + j * KVO_BLOCK, c->scales + r * nb + j);
@@ -383,6 +416,17 @@ static double kvo_pool_value(int qtype, const uint8_t* pool, const uint16_t* sca
   }
   if (qtype == KVO_FP8_E4M3_CAST || qtype == KVO_FP8_E5M2_CAST)
     return kvo_element_value(qtype, pool[row * head_dim + d], 0);
+  if (qtype == KVO_FP8_DS_MLA) { /* code x its tile's fp32 scale; the rope as stored */
+    const uint8_t* rp = pool + row * KVO_DS_ROW;
+    if (d >= KVO_DS_LATENT) {
+      uint16_t b;
+      memcpy(&b, rp + KVO_DS_LATENT + 16 + 2 * (d - KVO_DS_LATENT), 2);
+      return kvo_bf16_value(b);
+    }
+    float sc;
+    memcpy(&sc, rp + KVO_DS_LATENT + 4 * (d / KVO_DS_TILE), 4);
+    return kvo_e4m3_value(rp[d]) * (double)sc;
+  }
   int nb = head_dim / KVO_BLOCK;
   return kvo_element_value(qtype, pool[row * head_dim + d], scales[row * nb + d / KVO_BLOCK]);
 }

@@ -60,6 +60,9 @@ MUTANTS = [
      "int64_t len = kvo_clamped_len(c, b) - E + i;"),
     ("extend without the causal limit", "int64_t len = kvo_clamped_len(c, b) - E + i + 1;",
      "int64_t len = kvo_clamped_len(c, b);"),
+    ("656-byte row: tiles of 64", "#define KVO_DS_TILE 128", "#define KVO_DS_TILE 64"),
+    ("656-byte row: scale by reciprocal", "float sc = amax / KVO_E4M3_MAX;",
+     "float sc = amax * (1.0f / KVO_E4M3_MAX);"),
     ("extend token mapped to the next sequence",
      "while (b + 1 < c->batch && e->q_start[b + 1] <= j) ++b;",
      "while (b + 1 < c->batch && e->q_start[b + 1] < j) ++b;"),
@@ -84,7 +87,7 @@ def _run_mutant(case):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_pins.py", "tests/test_oracle_attention_pins.py",
                         "tests/test_oracle_cast_pins.py", "tests/test_oracle_sparse_pins.py",
-                        "tests/test_oracle_extend_pins.py"],
+                        "tests/test_oracle_extend_pins.py", "tests/test_oracle_dsmla_pins.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
     return name, r.returncode
 
