@@ -136,7 +136,7 @@ def write_traffic(src_dir):
 
 def store_bytes(n_tokens, n_heads, head_dim, qtype, tensors=2):
     per = {"bf16": 2.0, "fp8_e4m3": 1 + 1 / 16, "q8_0": 1 + 1 / 16, "fp8_e4m3_cast": 1.0,
-           "fp8_e5m2_cast": 1.0}[qtype]
+           "fp8_e5m2_cast": 1.0, "fp8_ds_mla": 656 / 576}[qtype]
     return int(tensors * n_tokens * n_heads * head_dim * (2 + per)) + 4 * n_tokens
 
 
@@ -412,7 +412,7 @@ def sparse_timing(args, wl, qtype, calls, topk_np, strm) -> int:
     # algorithmic bytes: the listed rows (codes + scales), their page-table
     # entries, the lists, seq_lens, Q and O
     per_row = {"bf16": 2 * 576, "fp8_e4m3": 612, "q8_0": 612, "fp8_e4m3_cast": 576,
-               "fp8_e5m2_cast": 576}[qtype]
+               "fp8_e5m2_cast": 576, "fp8_ds_mla": 656}[qtype]
     n = topk_np.size
     nbytes = (n * (per_row + 4 + 4) + 4 * wl.batch +
               wl.batch * wl.n_q_heads * (wl.head_dim_qk + wl.head_dim_v) * 2)
@@ -447,7 +447,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--qtype", default="fp8_e4m3",
-                    choices=["fp8_e4m3", "q8_0", "bf16", "fp8_e4m3_cast", "fp8_e5m2_cast"])
+                    choices=["fp8_e4m3", "q8_0", "bf16", "fp8_e4m3_cast", "fp8_e5m2_cast",
+                             "fp8_ds_mla"])
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--extend-new", type=int, default=64,
                     help="--workload extend: new tokens per sequence")

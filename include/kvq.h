@@ -53,13 +53,23 @@ typedef struct ihipStream_t* kvq_stream_t;
  * (the store casts with scale 1.0), §Benchmark (2.00x the token budget)].
  * The cast rounds to nearest even; a magnitude beyond the format's largest
  * finite value stores that value (448 for e4m3, 57344 for e5m2), the same
- * saturation the block-scaled store applies.  Inputs must be finite. */
+ * saturation the block-scaled store applies.  Inputs must be finite.
+ * KVQ_FP8_DS_MLA is the 656-byte row of the 576-wide MLA latent [PR25
+ * "Experimental FP8 KV Cache": a 656-byte fp8 row laid out as in vLLM; the
+ * page gives no field list, and the one taken is]: bytes 0..511 the e4m3fn
+ * codes of latent elements 0..511, bytes 512..527 four fp32 scales (scale j =
+ * max|x| / 448 over elements 128j .. 128j+127, an fp32 division; each code the
+ * RNE e4m3 of the clamped fp32 quotient x / scale; a zero tile stores scale 0
+ * and zero codes), bytes 528..655 the 64 rope elements as bf16.  One row per
+ * token (n_heads 1, head_dim 576), no scale buffer; the MLA slab decode
+ * (kvq_paged_decode with k_pool == v_pool) and kvq_sparse_mla_decode read it. */
 typedef enum {
   KVQ_BF16 = 0,          /* 2 bytes per element, no scale buffer                  */
   KVQ_FP8_E4M3 = 1,      /* e4m3fn codes, scale = max|x| / 448 per 32-block       */
   KVQ_Q8_0 = 2,          /* int8 codes in [-127, 127], scale = max|x| / 127       */
   KVQ_FP8_E4M3_CAST = 3, /* e4m3fn code of x itself, no scale buffer              */
-  KVQ_FP8_E5M2_CAST = 4  /* e5m2 code of x itself, no scale buffer                */
+  KVQ_FP8_E5M2_CAST = 4, /* e5m2 code of x itself, no scale buffer               */
+  KVQ_FP8_DS_MLA = 5     /* 656-byte MLA row: 512 e4m3 + 4 fp32 scales + 64 bf16 */
 } kvq_dtype;
 
 typedef enum {
@@ -85,6 +95,8 @@ typedef enum {
  *           cast types and KVQ_BF16 have none.
  * A token lives at slot = page * page_size + offset.  For the MLA latent slab
  * (one KV head, K and V the same row) n_heads = 1 and head_dim = 576.
+ * KVQ_FP8_DS_MLA: [num_pages][1][page_size][656] bytes, each row as described
+ * at kvq_dtype (codes, scales and rope together); no scale buffer.
  * ------------------------------------------------------------------------- */
 
 /* Bytes of one pool (codes + scales) for one of K or V.  This is the cost

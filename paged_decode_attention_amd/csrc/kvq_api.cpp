@@ -41,8 +41,10 @@ int ok() {
 
 bool known_dtype(int d) {
   return d == KVQ_BF16 || d == KVQ_FP8_E4M3 || d == KVQ_Q8_0 || d == KVQ_FP8_E4M3_CAST ||
-         d == KVQ_FP8_E5M2_CAST;
+         d == KVQ_FP8_E5M2_CAST || d == KVQ_FP8_DS_MLA;
 }
+// the 656-byte MLA row: one head of 576 elements per token
+bool dsm_shape_ok(int n_heads, int head_dim) { return n_heads == 1 && head_dim == kvq::kMlaDqk; }
 // a scale buffer beside the pool (the block-scaled types)
 bool scaled(int d) { return d == KVQ_FP8_E4M3 || d == KVQ_Q8_0; }
 
@@ -84,6 +86,8 @@ int check_rows(int dtype, int64_t n_tokens, int n_heads, int head_dim, int page_
     return fail(KVQ_ERR_ARG, "%s: head_dim %d is not a multiple of 8", fn, head_dim);
   if (page_size < 1 || page_size > 1024)
     return fail(KVQ_ERR_ARG, "%s: page_size %d outside 1..1024", fn, page_size);
+  if (dtype == KVQ_FP8_DS_MLA && !dsm_shape_ok(n_heads, head_dim))
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: the 656-byte row holds one head of 576 elements", fn);
   if (num_pages < 0) return fail(KVQ_ERR_ARG, "%s: num_pages < 0", fn);
   if (num_pages * (int64_t)page_size > INT32_MAX)
     return fail(KVQ_ERR_ARG, "%s: pool capacity exceeds 2^31-1 slots", fn);
@@ -117,6 +121,9 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
     return no("head_dim %d/%d is not a multiple of the %d-element quantization block",
               head_dim_qk, head_dim_v, KVQ_BLOCK);
   if (head_dim_v > head_dim_qk) return no("head_dim_v %d > head_dim_qk %d", head_dim_v, head_dim_qk);
+  if (qtype == KVQ_FP8_DS_MLA &&
+      !(head_dim_qk == kMlaDqk && head_dim_v == kMlaDv && n_kv_heads == 1 && ext_new == 0))
+    return no("the 656-byte row is the decode format of the 576/512 slab only");
   DecodePlan p{};
   const int G = n_q_heads / n_kv_heads;
   if (ext_new > 0 && !(head_dim_qk == head_dim_v &&
@@ -236,7 +243,7 @@ bool plan_sparse(int qtype, int batch, int n_q_heads, int k, SparseLayout* lay,
   const int gpages = L.kk / kPageSize;
   if (!plan_decode(qtype, batch, n_q_heads, 1, kMlaDqk, kMlaDv, kPageSize, gpages, &L.dense, why))
     return false;
-  L.row_bytes = kMlaDqk * (qtype == KVQ_BF16 ? 2 : 1);
+  L.row_bytes = (qtype == KVQ_FP8_DS_MLA) ? kDsmRow : kMlaDqk * (qtype == KVQ_BF16 ? 2 : 1);
   const size_t rows = (size_t)batch * L.kk;
   L.off_dense = 0;
   L.off_slab = align256(L.dense.bytes);
@@ -261,8 +268,12 @@ int64_t kvq_pool_bytes(kvq_dtype dtype, int64_t num_pages, int page_size, int n_
     return fail(-1, "kvq_pool_bytes: sizes must be positive (num_pages may be 0)");
   if (dtype != KVQ_BF16 && head_dim % KVQ_BLOCK != 0)
     return fail(-1, "kvq_pool_bytes: head_dim %d is not a multiple of %d", head_dim, KVQ_BLOCK);
+  if (dtype == KVQ_FP8_DS_MLA && !dsm_shape_ok(n_heads, head_dim))
+    return fail(-1, "kvq_pool_bytes: the 656-byte row holds one head of 576 elements");
   const int64_t elems = num_pages * page_size * (int64_t)n_heads * head_dim;
-  const int64_t codes = (dtype == KVQ_BF16) ? 2 * elems : elems;
+  const int64_t codes = (dtype == KVQ_BF16)         ? 2 * elems
+                        : (dtype == KVQ_FP8_DS_MLA) ? num_pages * page_size * (int64_t)kvq::kDsmRow
+                                                    : elems;
   const int64_t scales = scaled(dtype) ? (elems / KVQ_BLOCK) * 2 : 0;
   if (code_bytes) *code_bytes = codes;
   if (scale_bytes) *scale_bytes = scales;
@@ -281,6 +292,8 @@ int kvq_store(kvq_dtype dtype, const void* k_src, const void* v_src, int64_t src
   if (scaled(dtype) && !k_scales) return fail(KVQ_ERR_ARG, "kvq_store: null k_scales");
   if (v_src && (!v_pool || (scaled(dtype) && !v_scales)))
     return fail(KVQ_ERR_ARG, "kvq_store: v_src given without v_pool/v_scales");
+  if (v_src && dtype == KVQ_FP8_DS_MLA)
+    return fail(KVQ_ERR_ARG, "kvq_store: the 656-byte row is one slab (K and V the same row)");
   if (src_token_stride < (int64_t)n_heads * head_dim || src_token_stride % 8 != 0)
     return fail(KVQ_ERR_ARG,
                 "kvq_store: src_token_stride %lld must be >= n_heads*head_dim and a multiple of 8",

@@ -68,7 +68,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // fp32.
 template <int QT>
 __device__ __forceinline__ void decode_dword_bf16x2(uint32_t w, uint32_t* o) {
-  if constexpr (QT == QT_FP8 || QT == QT_FP8C) {
+  if constexpr (QT == QT_FP8 || QT == QT_FP8C || QT == QT_DSM) {
     o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
     o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
   } else if constexpr (QT == QT_BF8C) {
@@ -100,7 +100,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 template <int QT>
 __device__ __forceinline__ void decode_dword(uint32_t w, float* o) {
-  if constexpr (QT == QT_FP8 || QT == QT_FP8C) {
+  if constexpr (QT == QT_FP8 || QT == QT_FP8C || QT == QT_DSM) {
     fp8x4_to_f32(w, o);
   } else if constexpr (QT == QT_BF8C) {
     bf8x4_to_f32(w, o);

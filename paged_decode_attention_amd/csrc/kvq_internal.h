@@ -7,7 +7,10 @@
 
 namespace kvq {
 
-enum { QT_BF16 = 0, QT_FP8 = 1, QT_Q8 = 2, QT_FP8C = 3, QT_BF8C = 4 };
+// QT_DSM: the 656-byte MLA row (512 e4m3 codes, four fp32 scales one per 128
+// latent elements, 64 bf16 rope elements), one per token, no scale buffer.
+enum { QT_BF16 = 0, QT_FP8 = 1, QT_Q8 = 2, QT_FP8C = 3, QT_BF8C = 4, QT_DSM = 5 };
+constexpr int kDsmRow = 656, kDsmLatent = 512, kDsmTile = 128;
 // block-scaled 8-bit codes (a scale buffer beside the pool)
 __host__ __device__ constexpr bool qt_scaled(int qt) { return qt == QT_FP8 || qt == QT_Q8; }
 // 8-bit float codes (e4m3 or e5m2), block-scaled or cast

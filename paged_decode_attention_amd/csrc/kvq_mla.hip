@@ -162,11 +162,12 @@ struct MlaParams {
 template <int QT>
 struct MlaGeo {
   static constexpr int ESZ = (QT == QT_BF16) ? 2 : 1;
-  static constexpr int ROWB = kDqk * ESZ;           // code bytes per token row
+  // code bytes per token row (the 656-byte row: its codes, scales and rope)
+  static constexpr int ROWB = (QT == QT_DSM) ? kDsmRow : kDqk * ESZ;
   static constexpr int PAGEB = kPageSize * ROWB;    // code bytes per page
   static constexpr int SCLB = kPageSize * kNB * 2;  // scale bytes per page
   static constexpr int VW = 4 * ESZ;                // dwords of 16 V-part elements
-  static constexpr int RW = 2 * ESZ;                // dwords of 8 rope elements
+  static constexpr int RW = (QT == QT_DSM) ? 4 : 2 * ESZ;  // dwords of 8 rope elements
 };
 
 // One thread's share of a tile's codes and scales, loaded a tile ahead.
@@ -199,11 +200,13 @@ __device__ __forceinline__ void buf_load_dw(__amdgpu_buffer_rsrc_t rs, uint32_t 
 
 // Codes of one dword (four 8-bit codes, or two bf16) times the block scale,
 // rounded once to bf16 pairs (the product is exact in fp32).
+// (The 656-byte row's fp32 tile scales make the product inexact: it is
+// rounded to fp32, then to bf16.)
 template <int QT>
 __device__ __forceinline__ void dequant_dword(uint32_t w, float s, uint32_t* o) {
   if constexpr (QT == QT_BF16) {
     o[0] = w;
-  } else if constexpr (!qt_scaled(QT)) {  // cast codes: exact, no scale
+  } else if constexpr (!qt_scaled(QT) && QT != QT_DSM) {  // cast codes: exact, no scale
     decode_dword_bf16x2<QT>(w, o);
   } else {
     float f[4];
@@ -230,6 +233,7 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
   constexpr int ESZ = Gm::ESZ, ROWB = Gm::ROWB, PAGEB = Gm::PAGEB, SCLB = Gm::SCLB;
   constexpr int VW = Gm::VW, RW = Gm::RW;
   constexpr int EPD = (QT == QT_BF16) ? 1 : 2;  // bf16 pairs per code dword
+  constexpr int RPD = (QT == QT_BF16 || QT == QT_DSM) ? 1 : 2;  // ... per rope dword
   // two tile buffers (K rows, V^T); at the end of an item the same memory
   // stages each wave's output rows
   __shared__ __attribute__((aligned(16))) uint16_t s_tiles[2 * kTile * kKS + 2 * kVtElems];
@@ -324,13 +328,20 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
       const int rt = t >> 3, p8 = t & 7;
       const uint32_t vbase = (uint32_t)((4 * (q & 3)) * ROWB + u * 16 * ESZ);
       const uint32_t sbase = (uint32_t)((4 * (q & 3)) * kNB * 2 + (u >> 2) * 4);
-      const uint32_t roff = (uint32_t)((rt & (kPageSize - 1)) * ROWB + (kDv + 8 * p8) * ESZ);
+      const uint32_t roff = (uint32_t)((rt & (kPageSize - 1)) * ROWB +
+                                       (QT == QT_DSM ? kDsmLatent + 16 + 16 * p8 : (kDv + 8 * p8) * ESZ));
       const uint32_t rsoff = (uint32_t)((rt & (kPageSize - 1)) * kNB * 2 + (kDv / 32) * 2);
       const int P = max(__builtin_amdgcn_readfirstlane(page_of(j, wpage)), 0);
       const auto rc = page_rsrc(a.k_pool + (int64_t)P * PAGEB, PAGEB);
 #pragma unroll
       for (int i = 0; i < 4; ++i) buf_load_dw<VW>(rc, vbase + i * ROWB, R.v[i]);
       buf_load_dw<RW>(rc, roff, R.r);
+      if constexpr (QT == QT_DSM) {  // the fp32 scale of unit u's 128-element tile, per token
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          R.vs[i] = __builtin_amdgcn_raw_buffer_load_b32(
+              rc, (uint32_t)((4 * (q & 3) + i) * ROWB + kDsmLatent + 4 * (u >> 3)), 0, 0);
+      }
       if constexpr (qt_scaled(QT)) {
         const auto rs = page_rsrc(a.k_scales + (int64_t)P * (SCLB / 2), SCLB);
 #pragma unroll
@@ -369,7 +380,8 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         st.ok[i] = page_ok && (kTile * j + 4 * q + i < nt);
-        st.sv[i] = qt_scaled(QT) ? scale_half(R.vs[i], ((u >> 1) & 1) * 16) : 1.0f;
+        st.sv[i] = (QT == QT_DSM) ? __uint_as_float(R.vs[i])
+                   : qt_scaled(QT) ? scale_half(R.vs[i], ((u >> 1) & 1) * 16) : 1.0f;
       }
       st.okr = page_ok && (kTile * j + rt < nt);
     };
@@ -404,7 +416,12 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
         const float s = qt_scaled(QT) ? scale_half(R.rs, ((t & 7) >> 2) * 16) : 1.0f;
         uint32_t rw[4];
 #pragma unroll
-        for (int k = 0; k < RW; ++k) dequant_dword<QT>(R.r[k], s, &rw[k * EPD]);
+        for (int k = 0; k < RW; ++k) {
+          if constexpr (QT == QT_DSM)
+            rw[k] = R.r[k];  // the rope is stored as bf16
+          else
+            dequant_dword<QT>(R.r[k], s, &rw[k * RPD]);
+        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) rw[k] = st.okr ? rw[k] : 0u;
         ds_write16<0>(st.rb, u32x4{rw[0], rw[1], rw[2], rw[3]});
@@ -719,6 +736,7 @@ hipError_t launch_mla_decode(const DecodeArgs& a, const DecodePlan& plan, int nu
     case QT_FP8: return launch_q<QT_FP8>(mp, (int)grid, merge_grid, s);
     case QT_FP8C: return launch_q<QT_FP8C>(mp, (int)grid, merge_grid, s);
     case QT_BF8C: return launch_q<QT_BF8C>(mp, (int)grid, merge_grid, s);
+    case QT_DSM: return launch_q<QT_DSM>(mp, (int)grid, merge_grid, s);
     default: return launch_q<QT_Q8>(mp, (int)grid, merge_grid, s);
   }
 }

@@ -158,7 +158,9 @@ hipError_t launch_sparse_gather(const SparseArgs& s, const SparseLayout& lay, in
   g.g_pt = reinterpret_cast<int32_t*>(ws + lay.off_pt);
   g.g_len = reinterpret_cast<int32_t*>(ws + lay.off_len);
   const dim3 grid((unsigned)((int64_t)batch * g.slices));
-  if (lay.row_bytes == kMlaDqk * 2)
+  if (lay.row_bytes == kDsmRow)
+    sparse_gather_kernel<kDsmRow / 16><<<grid, kThreads, 0, stream>>>(g);
+  else if (lay.row_bytes == kMlaDqk * 2)
     sparse_gather_kernel<kMlaDqk * 2 / 16><<<grid, kThreads, 0, stream>>>(g);
   else
     sparse_gather_kernel<kMlaDqk / 16><<<grid, kThreads, 0, stream>>>(g);

@@ -214,9 +214,100 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, Dequan
   *reinterpret_cast<uint4*>(a.out + ((int64_t)token * a.n_heads + h) * a.head_dim + e8 * 8) = outv;
 }
 
+// ---- the 656-byte MLA row ------------------------------------------------------------
+// One wave per token: lane l quantizes latent elements 8l .. 8l+7, the 16
+// lanes of tile j = l / 16 share its maximum; the tile scale is amax / 448 as
+// an IEEE fp32 division and each element's quotient x / s too (a 24-bit scale
+// leaves no margin for a reciprocal shortcut); clamp, then the packed RNE
+// conversion.  A zero tile stores scale 0 and zero codes.  Lanes 0-15 copy
+// the 64 rope elements (8 bytes each).
+__global__ __launch_bounds__(kThreads) void store_dsm_kernel(StoreArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t token = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (token >= a.n_tokens) return;  // uniform over the wave
+  const int32_t slot = a.slots[token];
+  if (slot < 0 || (int64_t)slot >= a.num_pages * (int64_t)a.page_size) return;
+  const uint16_t* src = a.src[0] + token * a.stride;
+  const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * lane);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float x[8], m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_lo(w[i]);
+    x[2 * i + 1] = bf16_hi(w[i]);
+    m = fmaxf(m, fmaxf(fabsf(x[2 * i]), fabsf(x[2 * i + 1])));
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));  // the tile's 16 lanes
+  const float sc = m / 448.0f;
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (sc > 0.0f) ? fminf(fmaxf(x[i] / sc, -448.0f), 448.0f) : 0.0f;
+  uint32_t c[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * k + 0], v[4 * k + 1], 0, false);
+    c[k] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[4 * k + 2], v[4 * k + 3], lo, true);
+  }
+  uint8_t* row = a.pool[0] + (int64_t)slot * kDsmRow;  // n_heads = 1
+  *reinterpret_cast<uint2*>(row + 8 * lane) = make_uint2(c[0], c[1]);
+  if ((lane & 15) == 0) *reinterpret_cast<float*>(row + kDsmLatent + 4 * (lane >> 4)) = sc;
+  if (lane < 16)
+    *reinterpret_cast<uint2*>(row + kDsmLatent + 16 + 8 * lane) =
+        *reinterpret_cast<const uint2*>(src + kDsmLatent + 4 * lane);
+}
+
+// bf16 of one code x its fp32 tile scale, rounded once: the fp32 product p is
+// exact up to the fma residual r; only when p falls exactly on a bf16
+// rounding midpoint does r decide the direction.
+__device__ __forceinline__ uint32_t bf16_of_product(float x, float s) {
+  const float p = x * s;
+  const float r = fmaf(x, s, -p);
+  uint32_t b = __float_as_uint(p);
+  if ((b & 0xffffu) == 0x8000u && r != 0.0f) {
+    // exact value beyond the midpoint (away from zero) rounds up in
+    // magnitude, below it down
+    const bool away = (r > 0.0f) == (p > 0.0f);
+    return away ? (b + 0x8000u) >> 16 : (b - 0x8000u) >> 16;
+  }
+  return bf16_rne(p);
+}
+
+// One wave per token: lane l decodes latent elements 8l .. 8l+7; lanes 0-7
+// copy 8 rope elements each.
+__global__ __launch_bounds__(kThreads) void dequant_dsm_kernel(DequantArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t token = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (token >= a.n_tokens) return;  // uniform over the wave
+  const int32_t slot = a.slots[token];
+  uint16_t* out = a.out + token * kMlaDqk;
+  uint4 lat = make_uint4(0, 0, 0, 0), rope = make_uint4(0, 0, 0, 0);
+  if (slot >= 0 && (int64_t)slot < a.num_pages * (int64_t)a.page_size) {
+    const uint8_t* row = a.pool + (int64_t)slot * kDsmRow;
+    const uint2 raw = *reinterpret_cast<const uint2*>(row + 8 * lane);
+    const float s = *reinterpret_cast<const float*>(row + kDsmLatent + 4 * (lane >> 4));
+    float x[8];
+    decode_dword<QT_DSM>(raw.x, x);
+    decode_dword<QT_DSM>(raw.y, x + 4);
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = bf16_of_product(x[2 * i], s) | (bf16_of_product(x[2 * i + 1], s) << 16);
+    lat = make_uint4(o[0], o[1], o[2], o[3]);
+    if (lane < 8) rope = *reinterpret_cast<const uint4*>(row + kDsmLatent + 16 + 16 * lane);
+  }
+  *reinterpret_cast<uint4*>(out + 8 * lane) = lat;
+  if (lane < 8) *reinterpret_cast<uint4*>(out + kDsmLatent + 8 * lane) = rope;
+}
+
 }  // namespace
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t s) {
+  if (a.n_tokens > 0 && a.qtype == QT_DSM) {
+    const int64_t blocks = (a.n_tokens + kThreads / 64 - 1) / (kThreads / 64);
+    store_dsm_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+  }
   if (a.n_tokens == 0) return hipSuccess;
   const int nb = a.head_dim / 32;
   // bf16 pools are copied in 16-byte pieces with the same lane layout: one
@@ -252,6 +343,11 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t s) {
 
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {
   if (a.n_tokens == 0) return hipSuccess;
+  if (a.qtype == QT_DSM) {
+    const int64_t blocks = (a.n_tokens + kThreads / 64 - 1) / (kThreads / 64);
+    dequant_dsm_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+  }
   const uint32_t per_head = (uint32_t)(a.head_dim / 8);
   const uint32_t per_token = per_head * (uint32_t)a.n_heads;
   const int64_t max_tokens = ((int64_t)1 << 31) / per_token;

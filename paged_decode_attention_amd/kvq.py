@@ -25,7 +25,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
-DTYPES = {"bf16": 0, "fp8_e4m3": 1, "q8_0": 2, "fp8_e4m3_cast": 3, "fp8_e5m2_cast": 4}
+DTYPES = {"bf16": 0, "fp8_e4m3": 1, "q8_0": 2, "fp8_e4m3_cast": 3, "fp8_e5m2_cast": 4, "fp8_ds_mla": 5}
 SCALED = ("fp8_e4m3", "q8_0")  # storage types with a scale buffer
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 
@@ -132,6 +132,15 @@ def workspace_bytes(dtype, batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v
     return n
 
 
+DS_ROW = 656  # bytes of one row of the fp8_ds_mla slab (576 elements)
+
+
+def _row_dim(dtype, pool) -> int:
+    """Elements per head row of a pool tensor (its last dimension is bytes for
+    the 656-byte row)."""
+    return 576 if _dt(dtype) == DTYPES["fp8_ds_mla"] else pool.shape[3]
+
+
 def alloc_pool(dtype, num_pages: int, n_heads: int, head_dim: int, page_size: int = 16,
                device="cuda"):
     """Allocate (pool, scales) tensors of the layout above, sized by kvq_pool_bytes."""
@@ -139,6 +148,11 @@ def alloc_pool(dtype, num_pages: int, n_heads: int, head_dim: int, page_size: in
     if _dt(dtype) == DTYPES["bf16"]:
         pool = torch.empty((num_pages, n_heads, page_size, head_dim), dtype=torch.bfloat16,
                            device=device)
+        return pool, None
+    if _dt(dtype) == DTYPES["fp8_ds_mla"]:  # 656-byte rows: codes, scales and rope together
+        pool = torch.empty((num_pages, n_heads, page_size, DS_ROW), dtype=torch.uint8,
+                           device=device)
+        assert pool.numel() == cb
         return pool, None
     pool = torch.empty((num_pages, n_heads, page_size, head_dim), dtype=torch.uint8,
                        device=device)
@@ -157,7 +171,8 @@ def store(dtype, k, v, slot_mapping, k_pool, k_scales, v_pool=None, v_scales=Non
           stream=None) -> None:
     """Quantize-on-store of k (and v) bf16 [n_tokens, n_heads, head_dim] (or
     [n_tokens, stride] rows whose first n_heads*head_dim elements are the heads)."""
-    num_pages, n_heads, page_size, head_dim = k_pool.shape
+    num_pages, n_heads, page_size, _ = k_pool.shape
+    head_dim = _row_dim(dtype, k_pool)
     n_tokens = slot_mapping.numel()
     # a single token's leading stride is irrelevant (and may be anything)
     stride = k.stride(0) if n_tokens > 1 else n_heads * head_dim
@@ -173,7 +188,8 @@ def store(dtype, k, v, slot_mapping, k_pool, k_scales, v_pool=None, v_scales=Non
 
 def dequant(dtype, pool, scales, slot_mapping, out=None, stream=None):
     """Rows at slot_mapping, dequantized to bf16 [n_tokens, n_heads, head_dim]."""
-    num_pages, n_heads, page_size, head_dim = pool.shape
+    num_pages, n_heads, page_size, _ = pool.shape
+    head_dim = _row_dim(dtype, pool)
     n = slot_mapping.numel()
     if out is None:
         out = torch.empty((n, n_heads, head_dim), dtype=torch.bfloat16, device=pool.device)
@@ -384,7 +400,8 @@ class PreparedStore:
 
     def __init__(self, dtype, k, v, slot_mapping, k_pool, k_scales, v_pool=None, v_scales=None,
                  stream=None):
-        num_pages, n_heads, page_size, head_dim = k_pool.shape
+        num_pages, n_heads, page_size, _ = k_pool.shape
+        head_dim = _row_dim(dtype, k_pool)
         n_tokens = slot_mapping.numel()
         stride = k.stride(0) if n_tokens > 1 else n_heads * head_dim
         self._keep = (k, v, slot_mapping, k_pool, k_scales, v_pool, v_scales)

@@ -146,7 +146,7 @@ class Workload:
         entries walked and seq_lens.  Masked pages are not counted."""
         D, Dv = self.head_dim_qk, self.head_dim_v
         per = {"bf16": 2.0, "fp8_e4m3": 17 / 16, "q8_0": 17 / 16, "fp8_e4m3_cast": 1.0,
-               "fp8_e5m2_cast": 1.0}[qtype]
+               "fp8_e5m2_cast": 1.0, "fp8_ds_mla": 656 / 576}[qtype]  # 656-byte row: whole row
         n_valid = 0
         for b in range(self.batch):
             L = min(int(self.seq_lens[b]), self.max_pages * PAGE)

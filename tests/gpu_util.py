@@ -48,6 +48,8 @@ def host_u16(t: torch.Tensor) -> np.ndarray:
 def np_pool(qtype, num_pages, H, D, fill_code=0, fill_scale=0):
     if qtype == "bf16":
         return np.full((num_pages, H, W.PAGE, D), fill_scale, np.uint16), None
+    if qtype == "fp8_ds_mla":  # 656-byte rows
+        return np.full((num_pages, H, W.PAGE, oracle.DS_ROW), fill_code, np.uint8), None
     codes = np.full((num_pages, H, W.PAGE, D), fill_code, np.uint8)
     if qtype not in oracle.SCALED:  # the cast types: no scale buffer
         return codes, None

@@ -162,3 +162,23 @@ def test_extend_validation():
     assert need > kvq.workspace_bytes("fp8_e4m3", 2, 16, 8, 128, 128, 16, 8)  # 8 tiles per kv head
     assert call(ws=need - 1) == kvq.ERR_WORKSPACE
     assert L.kvq_extend_attention_workspace_bytes(1, 1, 128, 1, 576, 16, 8, 4) == 0
+
+
+def test_656_byte_row_shape_and_validation():
+    """fp8_ds_mla: 656 bytes per token row, one head of 576 elements, no scale
+    buffer; other shapes, a separate V source and the separate-K/V kernels
+    are rejected before any launch."""
+    L = kvq.LIB
+    total, codes, scales = kvq.pool_bytes("fp8_ds_mla", 10, 16, 1, 576)
+    assert total == codes == 10 * 16 * 656 and scales == 0
+    assert L.kvq_pool_bytes(5, 10, 16, 1, 512, None, None) == -1
+    assert L.kvq_pool_bytes(5, 10, 16, 2, 576, None, None) == -1
+    # store: wrong shape, and a V source (the row is K and V at once)
+    assert L.kvq_store(5, 16, None, 576, 16, 4, 1, 512, 16, 4, 16, None, None, None, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_store(5, 16, 16, 576, 16, 4, 1, 576, 16, 4, 16, None, 16, None, None) == kvq.ERR_ARG
+    # decode: the slab shape only
+    assert kvq.workspace_bytes("fp8_ds_mla", 1, 128, 1, 576, 512, 16, 64) > 0
+    assert L.kvq_paged_decode_workspace_bytes(5, 2, 16, 8, 128, 128, 16, 8) == 0
+    assert "656-byte" in kvq.last_error()
+    assert L.kvq_extend_attention_workspace_bytes(5, 2, 16, 8, 128, 16, 8, 4) == 0
+    assert kvq.sparse_workspace_bytes("fp8_ds_mla", 1, 128, 256) > 0

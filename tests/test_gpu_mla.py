@@ -58,7 +58,8 @@ def check(wl, qtype, rows=None, tol=TOL):
     return g_out, pools
 
 
-@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0", "bf16", "fp8_e4m3_cast", "fp8_e5m2_cast"])
+@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0", "bf16", "fp8_e4m3_cast", "fp8_e5m2_cast",
+                                   "fp8_ds_mla"])
 @pytest.mark.parametrize("Hq", [128, 64, 16])
 def test_mla_small_matches_oracle(qtype, Hq):
     """Ragged lengths around the page (16) and tile (32) edges, masked pages,
@@ -163,8 +164,9 @@ def test_mla_page_permutation_gives_identical_bits():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_mla_full_size_sampled_rows():
+@pytest.mark.parametrize("qtype", ["fp8_e4m3", "fp8_ds_mla"])
+def test_mla_full_size_sampled_rows(qtype):
     """The 163840-token slab with 128 heads, in the launch configuration the
     benchmark times; the oracle computes a sample of the heads."""
     wl = W.mla()
-    check(wl, "fp8_e4m3", rows=np.array([0, 1, 37, 64, 100, 127], np.int32))
+    check(wl, qtype, rows=np.array([0, 1, 37, 64, 100, 127], np.int32))

@@ -66,7 +66,8 @@ def run(wl, qtype, topk, pools=None):
     return g, g_lse, pools
 
 
-@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0", "bf16", "fp8_e4m3_cast", "fp8_e5m2_cast"])
+@pytest.mark.parametrize("qtype", ["fp8_e4m3", "q8_0", "bf16", "fp8_e4m3_cast", "fp8_e5m2_cast",
+                                   "fp8_ds_mla"])
 @pytest.mark.parametrize("K", [256, 100, 33])
 def test_sparse_matches_oracle(qtype, K):
     wl = mla_workload(128, [0, 700, 2000, 45], 140, seed=K + 5, mask_frac=0.15)
