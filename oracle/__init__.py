@@ -102,8 +102,8 @@ def _declare(L):
                                         c.c_int64, c.c_double, P, P, c.c_int]
     L.kvo_sparse_mla_decode.restype = None
     L.kvo_extend_attention.argtypes = [c.c_int, P, P, P, P, P, P, P, c.c_int64, P, c.c_int, c.c_int,
-                                       c.c_int, c.c_int, c.c_int, c.c_int, c.c_int64, c.c_double,
-                                       P, P, c.c_int]
+                                       c.c_int, c.c_int, c.c_int, c.c_int, c.c_int, c.c_int64,
+                                       c.c_double, P, P, c.c_int]
     L.kvo_extend_attention.restype = None
     L.kvo_e5m2_value.argtypes = [c.c_uint8]
     L.kvo_e5m2_value.restype = c.c_double
@@ -244,10 +244,13 @@ def paged_decode(qtype, q_bf16: np.ndarray, k_pool: np.ndarray, k_scales, v_pool
 def extend_attention(qtype, q_bf16: np.ndarray, q_start: np.ndarray, k_pool: np.ndarray,
                      k_scales, v_pool: np.ndarray, v_scales, page_table: np.ndarray,
                      seq_lens: np.ndarray, n_kv_heads: int, head_dim: int, page_size: int,
-                     num_pages: int, sm_scale: float, threads: int | None = None):
+                     num_pages: int, sm_scale: float, threads: int | None = None,
+                     head_dim_v: int | None = None):
     """Causal extend attention in double.  q_bf16: uint16 [T][Hq][D], the new
     tokens of every sequence back to back; q_start: int32 [B+1] (q_start[0] =
-    0).  Returns (out float64 [T*Hq][D], lse float64 [T*Hq])."""
+    0).  Pass ``v_pool is k_pool`` and head_dim_v for the shared MLA slab.
+    Returns (out float64 [T*Hq][Dv], lse float64 [T*Hq])."""
+    head_dim_v = head_dim_v or head_dim
     q = np.ascontiguousarray(q_bf16, dtype=np.uint16)
     T, Hq = q.shape[0], q.shape[1]
     qs = np.ascontiguousarray(q_start, dtype=np.int32)
@@ -255,11 +258,14 @@ def extend_attention(qtype, q_bf16: np.ndarray, q_start: np.ndarray, k_pool: np.
     pt = np.ascontiguousarray(page_table, dtype=np.int32)
     sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
     B = len(sl)
-    out = np.empty((T * Hq, head_dim), dtype=np.float64)
+    out = np.empty((T * Hq, head_dim_v), dtype=np.float64)
     lse = np.empty(T * Hq, dtype=np.float64)
-    lib().kvo_extend_attention(_qt(qtype), _ptr(q), _ptr(qs), _ptr(k_pool), _ptr(k_scales),
-                               _ptr(v_pool), _ptr(v_scales), _ptr(pt), pt.shape[1], _ptr(sl), B,
-                               Hq, n_kv_heads, head_dim, page_size, pt.shape[1], num_pages,
+    kp = _ptr(k_pool)
+    vp = kp if v_pool is k_pool else _ptr(v_pool)
+    lib().kvo_extend_attention(_qt(qtype), _ptr(q), _ptr(qs), kp, _ptr(k_scales),
+                               vp, _ptr(v_scales), _ptr(pt), pt.shape[1], _ptr(sl), B,
+                               Hq, n_kv_heads, head_dim, head_dim_v, page_size, pt.shape[1],
+                               num_pages,
                                float(sm_scale), _ptr(out), _ptr(lse),
                                threads or default_threads())
     return out, lse

@@ -598,16 +598,19 @@ static void kvo_ext_unit(void* p, int64_t r) {
              c->lse ? c->lse + r : NULL);
 }
 
+/* head_dim_v < head_dim with v_pool == k_pool: the shared MLA slab (V the
+ * first head_dim_v elements of each row), as in the decode. */
 void kvo_extend_attention(int qtype, const uint16_t* q, const int32_t* q_start,
                           const uint8_t* k_pool, const uint16_t* k_scales, const uint8_t* v_pool,
                           const uint16_t* v_scales, const int32_t* page_table, int64_t pt_stride,
                           const int32_t* seq_lens, int batch, int n_q_heads, int n_kv_heads,
-                          int head_dim, int page_size, int max_pages, int64_t num_pages,
-                          double sm_scale, double* out, double* lse, int threads) {
+                          int head_dim, int head_dim_v, int page_size, int max_pages,
+                          int64_t num_pages, double sm_scale, double* out, double* lse,
+                          int threads) {
   kvo_ext_ctx e;
-  kvo_dec_ctx c = {qtype,     q,          k_pool,    v_pool,    k_scales,  v_scales,
-                   page_table, pt_stride, seq_lens,  batch,     n_q_heads, n_kv_heads,
-                   head_dim,  head_dim,   page_size, max_pages, num_pages, sm_scale,
+  kvo_dec_ctx c = {qtype,     q,          k_pool,    v_pool,     k_scales,  v_scales,
+                   page_table, pt_stride, seq_lens,  batch,      n_q_heads, n_kv_heads,
+                   head_dim,  head_dim_v, page_size, max_pages,  num_pages, sm_scale,
                    NULL,      out,        lse};
   e.d = c;
   e.q_start = q_start;

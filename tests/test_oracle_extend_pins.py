@@ -141,3 +141,35 @@ def test_last_new_token_is_the_decode():
     Hq = c["Hq"]
     rows = np.concatenate([np.arange(j * Hq, (j + 1) * Hq) for j in last])
     assert np.array_equal(o[rows], od) and np.array_equal(l[rows], ld)
+
+
+def test_mla_slab_extend_brute_force():
+    """The shared 576/512 slab: each new token's causal softmax over the
+    rows it may see, K the whole row, V its first 512 elements."""
+    rng = np.random.default_rng(9)
+    lens, news = np.array([70, 40], np.int32), [5, 40]
+    n_pages = 8
+    pt = np.array([[3, 0, 6, 1, 7], [2, 5, 4, -1, -1]], np.int32)
+    rows = (rng.standard_normal((n_pages * PAGE, 1, 576), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    pool = np.zeros((n_pages, 1, PAGE, 576), np.uint8)
+    sc = np.zeros((n_pages, 1, PAGE, 18), np.uint16)
+    oracle.store("fp8_e4m3", rows, np.arange(n_pages * PAGE, dtype=np.int32), 1, 576, PAGE, n_pages, pool, sc)
+    q_start = np.array([0, 5, 45], np.int32)
+    q = (rng.standard_normal((45, 16, 576), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    sm = 0.05
+    out, lse = oracle.extend_attention("fp8_e4m3", q, q_start, pool, sc, pool, sc, pt, lens, 1, 576,
+                                       PAGE, n_pages, sm, head_dim_v=512)
+    qv = (q.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for b in range(2):
+        E = news[b]
+        for i in range(E):
+            pos = int(lens[b]) - E + i
+            slots = [int(pt[b, t // PAGE]) * PAGE + t % PAGE for t in range(pos + 1)]
+            K, _ = oracle.dequant("fp8_e4m3", pool, sc, np.array(slots, np.int32), 1, 576, PAGE, n_pages)
+            j = int(q_start[b]) + i
+            z = sm * (qv[j] @ K[:, 0, :].T)              # [16 heads, n]
+            zm = z.max(axis=1, keepdims=True)
+            w = np.exp(z - zm)
+            ref = (w @ K[:, 0, :512]) / w.sum(axis=1, keepdims=True)
+            assert np.allclose(out[j * 16:(j + 1) * 16], ref, rtol=1e-10, atol=1e-12)
+            assert np.allclose(lse[j * 16:(j + 1) * 16], zm[:, 0] + np.log(w.sum(axis=1)), rtol=1e-12)
