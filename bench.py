@@ -345,19 +345,19 @@ def extend_timing(args, wl, qtype, calls, q_start, strm) -> int:
     from paged_decode_attention_amd import kvq
     from paged_decode_attention_amd import workloads as W
     us = replay_us(args, calls, strm)
-    H, D, Hq = wl.n_kv_heads, wl.head_dim_qk, wl.n_q_heads
+    H, D, Dv, Hq = wl.n_kv_heads, wl.head_dim_qk, wl.head_dim_v, wl.n_q_heads
     E = np.diff(q_start).astype(np.int64)
     T = int(q_start[-1])
     # algorithmic bytes: every sequence's K and V rows once, its page-table
     # entries, the new tokens' Q and O, seq_lens and q_start
-    per_tok = kvq.pool_bytes(qtype, 1, W.PAGE, H, D)[0] / W.PAGE * 2
+    per_tok = kvq.pool_bytes(qtype, 1, W.PAGE, H, D)[0] / W.PAGE * (1 if wl.shared else 2)
     tokens = int(wl.seq_lens.astype(np.int64).sum())
     nbytes = (tokens * per_tok + 4 * sum((int(L) + W.PAGE - 1) // W.PAGE for L in wl.seq_lens)
-              + T * Hq * D * 2 * 2 + 4 * wl.batch + 4 * (wl.batch + 1))
+              + T * Hq * (D + Dv) * 2 + 4 * wl.batch + 4 * (wl.batch + 1))
     # flops: each new token attends to its position + 1 rows, 2 D flops per
     # row for q.k and 2 D for p.v, per query head
     vis = sum(int(np.sum(int(L) - e + np.arange(e) + 1)) for L, e in zip(wl.seq_lens, E))
-    flops = 4.0 * D * Hq * vis
+    flops = 2.0 * (D + Dv) * Hq * vis
     t_roof = max(nbytes / 8e12, flops / 2.5e15) * 1e6
     res = {
         "metric": "extend attention call time, 1 GPU",
@@ -370,9 +370,9 @@ def extend_timing(args, wl, qtype, calls, q_start, strm) -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "%s: %d sequences x %d tokens, the last %d of each new (causal), "
-                               "%d q / %d kv heads, head_dim %d" % (
+                               "%d q / %d kv heads, head_dim %d/%d" % (
                                    wl.name, wl.batch, int(wl.seq_lens.max()), int(E.max()), Hq,
-                                   H, D),
+                                   H, D, Dv),
                    "kv_storage": qtype, "replicas": len(calls)},
         "call_us": round(us, 3),
         "gbps": round(nbytes / (us * 1e-6) / 1e9, 2),
@@ -455,7 +455,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="qwen3",
                     choices=["qwen3", "ragged256", "single256", "mla", "mixed", "mla_sparse",
-                             "extend"],
+                             "extend", "mla_extend"],
                     help="qwen3 (default) is the decode step this benchmark reports; the others "
                          "time kvq_paged_decode alone on that workload and print their own line")
     ap.add_argument("--replicas", type=int, default=0,
@@ -495,6 +495,8 @@ def main() -> int:
         return decode_only(args, W.mla(), qtype, dev, sparse_k=SPARSE_K)
     if args.workload == "extend":
         return decode_only(args, W.extend(new=args.extend_new), qtype, dev)
+    if args.workload == "mla_extend":
+        return decode_only(args, W.mla_extend(new=args.extend_new), qtype, dev)
     if args.workload != "qwen3":
         return decode_only(args, W.BY_NAME[args.workload](), qtype, dev)
     wl = W.qwen3(replicas=args.layers)

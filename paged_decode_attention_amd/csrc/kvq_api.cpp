@@ -454,8 +454,16 @@ size_t kvq_extend_attention_workspace_bytes(kvq_dtype dtype, int batch, int n_q_
     fail(KVQ_ERR_ARG, "kvq_extend_attention_workspace_bytes: max_new_tokens must be >= 1");
     return 0;
   }
-  if (!kvq::plan_decode(dtype, batch, n_q_heads, n_kv_heads, head_dim, head_dim, page_size,
-                        max_pages, &p, &why, max_new_tokens)) {
+  const bool slab = head_dim == kvq::kMlaDqk && n_kv_heads == 1;
+  if (slab && (int64_t)batch * max_new_tokens > kvq::kMlaMaxBatch) {
+    fail(KVQ_ERR_UNSUPPORTED, "kvq_extend_attention_workspace_bytes: batch x max_new_tokens "
+                              "exceeds %d for the 576/512 slab", kvq::kMlaMaxBatch);
+    return 0;
+  }
+  if (!(slab ? kvq::plan_decode(dtype, batch * max_new_tokens, n_q_heads, 1, kvq::kMlaDqk,
+                                kvq::kMlaDv, page_size, max_pages, &p, &why)
+             : kvq::plan_decode(dtype, batch, n_q_heads, n_kv_heads, head_dim, head_dim,
+                                page_size, max_pages, &p, &why, max_new_tokens))) {
     fail(KVQ_ERR_UNSUPPORTED, "kvq_extend_attention_workspace_bytes: %s", why);
     return 0;
   }
@@ -492,14 +500,26 @@ int kvq_extend_attention(kvq_dtype dtype, const void* q, const int32_t* q_start,
     return fail(KVQ_ERR_ARG, "kvq_extend_attention: null pointer");
   if (scaled(dtype) && (!k_scales || !v_scales))
     return fail(KVQ_ERR_ARG, "kvq_extend_attention: null scales");
-  if (k_pool == v_pool)
-    return fail(KVQ_ERR_UNSUPPORTED, "kvq_extend_attention: needs separate K and V pools");
+  // the shared 576/512 slab: the MLA kernel with its work numbered by new token
+  const bool slab = k_pool == v_pool;
+  if (slab && !(head_dim == kvq::kMlaDqk && n_kv_heads == 1 && k_scales == v_scales))
+    return fail(KVQ_ERR_UNSUPPORTED,
+                "kvq_extend_attention: k_pool == v_pool is the 576/512 slab (one kv head, "
+                "the same scales)");
+  if (!slab && (head_dim == kvq::kMlaDqk || dtype == KVQ_FP8_DS_MLA))
+    return fail(KVQ_ERR_UNSUPPORTED, "kvq_extend_attention: the 576-wide slab needs k_pool == v_pool");
+  if (slab && (int64_t)batch * max_new_tokens > kvq::kMlaMaxBatch)
+    return fail(KVQ_ERR_UNSUPPORTED,
+                "kvq_extend_attention: batch x max_new_tokens exceeds %d for the 576/512 slab",
+                kvq::kMlaMaxBatch);
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out_bf16, 4))
     return fail(KVQ_ERR_ARG, "kvq_extend_attention: q and pools must be 16-byte aligned");
   kvq::DecodePlan plan;
   const char* why = nullptr;
-  if (!kvq::plan_decode(dtype, batch, n_q_heads, n_kv_heads, head_dim, head_dim, page_size,
-                        max_pages, &plan, &why, max_new_tokens))
+  if (!(slab ? kvq::plan_decode(dtype, batch * max_new_tokens, n_q_heads, 1, kvq::kMlaDqk,
+                                kvq::kMlaDv, page_size, max_pages, &plan, &why)
+             : kvq::plan_decode(dtype, batch, n_q_heads, n_kv_heads, head_dim, head_dim,
+                                page_size, max_pages, &plan, &why, max_new_tokens)))
     return fail(KVQ_ERR_UNSUPPORTED, "kvq_extend_attention: %s", why);
   if (!workspace || workspace_bytes < plan.bytes)
     return fail(KVQ_ERR_WORKSPACE, "kvq_extend_attention: workspace of %zu bytes needed, %zu given",
@@ -529,7 +549,12 @@ int kvq_extend_attention(kvq_dtype dtype, const void* q, const int32_t* q_start,
   a.workspace = workspace;
   a.q_start = q_start;
   a.max_new = max_new_tokens;
-  hipError_t e = kvq::launch_gqa_mfma_decode(a, plan, num_cus_current(), stream);
+  if (slab) {  // work index v = b * max_new + i over the new tokens
+    a.batch = batch * max_new_tokens;
+    a.head_dim_v = kvq::kMlaDv;
+  }
+  hipError_t e = slab ? kvq::launch_mla_decode(a, plan, num_cus_current(), stream)
+                      : kvq::launch_gqa_mfma_decode(a, plan, num_cus_current(), stream);
   if (e != hipSuccess) return hip_fail(e, "kvq_extend_attention");
   return ok();
 }

@@ -101,6 +101,36 @@ __device__ __forceinline__ int clamped_len(const DecodeArgs& a, int b) {
 // Exclusive scan of per-sequence item counts into s_prefix[0..B], by all 256
 // threads: each sums a contiguous range of sequences, the ranges are scanned
 // with wave shuffles and one LDS exchange, then written out.
+// The same over the lengths len(b) (the slab's extend attention numbers its
+// work by new token; see kvq_mla.hip).
+template <int kThreads, typename LenFn>
+__device__ void build_prefix_with(const DecodeArgs& a, int item_tokens, int units, int* s_prefix,
+                                  int* s_wave, LenFn len) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = a.batch;
+  const int per = (B + kThreads - 1) / kThreads;
+  const int b0 = tid * per, b1 = min(b0 + per, B);
+  int local = 0;
+  for (int b = b0; b < b1; ++b) local += (len(b) + item_tokens - 1) / item_tokens * units;
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += s_wave[w];
+  int run = base + incl - local;
+  for (int b = b0; b < b1; ++b) {
+    s_prefix[b] = run;
+    run += (len(b) + item_tokens - 1) / item_tokens * units;
+  }
+  if (tid == kThreads - 1) s_prefix[B] = base + incl;
+  __syncthreads();
+}
+
 template <int kThreads>
 __device__ void build_prefix(const DecodeArgs& a, int item_tokens, int units, int* s_prefix,
                              int* s_wave) {

@@ -227,6 +227,29 @@ __device__ __forceinline__ float scale_half(uint32_t w, int shift) {
   return f16_bits_to_f32((uint16_t)(w >> shift));
 }
 
+// Extend attention over the slab [PR103 §What: the quantized pool feeds the
+// prefill / extend kernels; PR113 §Testing: prefill] runs the same kernel
+// with the work numbered by new token: index v of the work list is new token
+// i = v % M of sequence s = v / M (M = max_new); it attends to its
+// sequence's first L_s - E_s + i + 1 positions (its causal end) through page
+// row s, and reads / writes q and out row q_start[s] + i.  Indexes past a
+// sequence's new tokens have no positions and no row.  Without q_start, v is
+// the sequence itself.
+__device__ __forceinline__ int mla_len(const DecodeArgs& a, int v) {
+  if (!a.q_start) return clamped_len(a, v);
+  const int s = v / a.max_new, i = v - s * a.max_new;
+  const int E = a.q_start[s + 1] - a.q_start[s];
+  return i < E ? max(clamped_len(a, s) - E + i + 1, 0) : 0;
+}
+__device__ __forceinline__ int mla_pt_row(const DecodeArgs& a, int v) {
+  return a.q_start ? v / a.max_new : v;
+}
+__device__ __forceinline__ int64_t mla_row(const DecodeArgs& a, int v) {
+  if (!a.q_start) return v;
+  const int s = v / a.max_new, i = v - s * a.max_new;
+  return i < a.q_start[s + 1] - a.q_start[s] ? (int64_t)a.q_start[s] + i : -1;
+}
+
 template <int QT>
 __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
   using Gm = MlaGeo<QT>;
@@ -249,16 +272,19 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
   const int n16 = lane & 15, g = lane >> 4;
   const int Hq = a.n_q_heads;
 
-  build_prefix<kT>(a, p.item_tokens, 1, s_prefix, s_wave);
+  build_prefix_with<kT>(a, p.item_tokens, 1, s_prefix, s_wave,
+                        [&](int v) { return mla_len(a, v); });
   const int total = s_prefix[a.batch];
   if (blockIdx.x == 0)
     for (int b = tid; b <= a.batch; b += kT) p.prefix[b] = s_prefix[b];
   // a sequence with no valid length has no items: its output is 0, lse -inf
   for (int b = blockIdx.x; b < a.batch; b += gridDim.x) {
     if (s_prefix[b] != s_prefix[b + 1]) continue;
-    for (int i = tid; i < Hq * kDv; i += kT) a.out[(int64_t)b * Hq * kDv + i] = 0;
+    const int64_t row = mla_row(a, b);
+    if (row < 0) continue;  // no such new token
+    for (int i = tid; i < Hq * kDv; i += kT) a.out[row * Hq * kDv + i] = 0;
     if (a.lse)
-      for (int h = tid; h < Hq; h += kT) a.lse[(int64_t)b * Hq + h] = -INFINITY;
+      for (int h = tid; h < Hq; h += kT) a.lse[row * Hq + h] = -INFINITY;
   }
 
   // ---- tile geometry ----------------------------------------------------------------
@@ -288,7 +314,8 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
     }
     const int b = lo;
     const int chunk = item - s_prefix[b];
-    const int L = clamped_len(a, b);
+    const int L = mla_len(a, b);
+    const int64_t orow = mla_row(a, b);  // valid: b has work
     const int nc = (L + p.item_tokens - 1) / p.item_tokens;
     const int t0 = chunk * p.item_tokens;
     const int nt = min(p.item_tokens, L - t0);
@@ -298,7 +325,7 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
     // page ids of the item: lane k holds page column t0/16 + k; masked -> -1
     int pid = -1;
     if (lane < npages) {
-      const int v = a.page_table[(int64_t)b * a.pt_stride + t0 / kPageSize + lane];
+      const int v = a.page_table[(int64_t)mla_pt_row(a, b) * a.pt_stride + t0 / kPageSize + lane];
       pid = (v >= 0 && (int64_t)v < a.num_pages) ? v : -1;
     }
     // page id of tile j's page k (k = 0, 1); -1 past the item
@@ -313,7 +340,7 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
       const int h = 32 * wave + 16 * ht + n16;
-      const uint16_t* qrow = a.q + ((int64_t)b * Hq + (h < Hq ? h : 0)) * kDqk + 8 * g;
+      const uint16_t* qrow = a.q + (orow * Hq + (h < Hq ? h : 0)) * kDqk + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < kNB; ++ks) {
         u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
@@ -599,7 +626,7 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
         if (gg == 0 && h < Hq) {
           if (nc == 1) {
             if (a.lse)
-              a.lse[(int64_t)b * Hq + h] =
+              a.lse[orow * Hq + h] =
                   (mref[ht] == -INFINITY) ? -INFINITY : (mref[ht] + log2f(Lh[ht])) * kLn2;
           } else {
             *reinterpret_cast<float2*>(p.part_ml + ((int64_t)item * Hq + h) * 2) =
@@ -613,7 +640,7 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
       // below Hq (stores past it are dropped), so no store waits on another.
       const int rows = __builtin_amdgcn_readfirstlane(min(32, max(Hq - 32 * wave, 0)));
       const uint64_t da = reinterpret_cast<uint64_t>(
-          ((nc == 1) ? a.out + (int64_t)b * Hq * kDv : p.part_out + (int64_t)item * Hq * kDv) +
+          ((nc == 1) ? a.out + orow * Hq * kDv : p.part_out + (int64_t)item * Hq * kDv) +
           (int64_t)32 * wave * kDv);
       const uint64_t dsa = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(da >> 32)) << 32) |
                            (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)da);
@@ -665,7 +692,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaParams p) {
     if (lane == 0) {
       s_L = Ls;
       if (a.lse && half == 0)
-        a.lse[(int64_t)b * Hq + h] = (Ls > 0.0f) ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+        a.lse[mla_row(a, b) * Hq + h] = (Ls > 0.0f) ? (M + log2f(Ls)) * kLn2 : -INFINITY;
     }
   }
   __syncthreads();
@@ -699,7 +726,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaParams p) {
 #pragma unroll
     for (int k = 0; k < kMergeGroups; ++k) t += s_red[k][tid];
     const float Ls = s_L;
-    a.out[((int64_t)b * Hq + h) * kDv + half * kMergeCols + tid] =
+    a.out[(mla_row(a, b) * Hq + h) * kDv + half * kMergeCols + tid] =
         (uint16_t)bf16_rne(Ls > 0.0f ? t / Ls : 0.0f);
   }
 }

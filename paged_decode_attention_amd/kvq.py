@@ -283,8 +283,10 @@ def extend_attention(dtype, q, q_start, max_new_tokens, k_pool, k_scales, v_pool
                      stream=None):
     """Causal extend (prefill) attention: q bf16 [T, Hq, D] holds the new
     tokens of every sequence back to back (q_start int32 [batch + 1]); each
-    attends to its sequence's pool up to its own position.  Returns (out, lse)."""
+    attends to its sequence's pool up to its own position.  Pass v_pool=k_pool
+    for the shared 576/512 slab (out [T, Hq, 512]).  Returns (out, lse)."""
     T, n_q_heads, head_dim = q.shape
+    head_dim_v = 512 if v_pool is k_pool else head_dim
     num_pages, n_kv_heads, page_size, _ = k_pool.shape
     batch = seq_lens.numel()
     max_pages = page_table.shape[1]
@@ -292,7 +294,7 @@ def extend_attention(dtype, q, q_start, max_new_tokens, k_pool, k_scales, v_pool
         raise ValueError("page_table rows must be contiguous")
     pt_stride = page_table.stride(0) if batch > 1 else max_pages
     if out is None:
-        out = torch.empty((T, n_q_heads, head_dim), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((T, n_q_heads, head_dim_v), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((T, n_q_heads), dtype=torch.float32, device=q.device)
     need = extend_workspace_bytes(dtype, batch, n_q_heads, n_kv_heads, head_dim, page_size,
@@ -319,7 +321,8 @@ class PreparedExtend:
         num_pages, n_kv_heads, page_size, _ = k_pool.shape
         batch = seq_lens.numel()
         max_pages = page_table.shape[1]
-        self.out = torch.empty((T, n_q_heads, head_dim), dtype=torch.bfloat16, device=q.device)
+        head_dim_v = 512 if v_pool is k_pool else head_dim
+        self.out = torch.empty((T, n_q_heads, head_dim_v), dtype=torch.bfloat16, device=q.device)
         self.lse = torch.empty((T, n_q_heads), dtype=torch.float32, device=q.device)
         need = extend_workspace_bytes(dtype, batch, n_q_heads, n_kv_heads, head_dim, page_size,
                                       max_pages, max_new_tokens)

@@ -233,6 +233,14 @@ def extend(seed: int = 6, batch: int = 8, ctx: int = 16384, new: int = 64) -> Wo
     return wl
 
 
+def mla_extend(seed: int = 4, ctx: int = 163840, new: int = 4) -> Workload:
+    """The mla slab with its last `new` positions new (extend over the slab)."""
+    wl = mla(seed=seed, ctx=ctx)
+    wl.name = "mla_extend_b1_ctx%d_new%d_h128x1_d576_dv512" % (ctx, new)
+    wl.new_tokens = {"q_start": np.array([0, new], np.int32)}
+    return wl
+
+
 def extend_queries(wl: Workload, n_tokens: int) -> np.ndarray:
     """bf16 bits uint16 [n_tokens, n_q_heads, head_dim_qk]: the new tokens'
     queries, N(0,1), from their own sub-stream."""

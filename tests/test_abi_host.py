@@ -161,7 +161,11 @@ def test_extend_validation():
     need = kvq.extend_workspace_bytes("fp8_e4m3", 2, 16, 8, 128, 16, 8, 64)
     assert need > kvq.workspace_bytes("fp8_e4m3", 2, 16, 8, 128, 128, 16, 8)  # 8 tiles per kv head
     assert call(ws=need - 1) == kvq.ERR_WORKSPACE
-    assert L.kvq_extend_attention_workspace_bytes(1, 1, 128, 1, 576, 16, 8, 4) == 0
+    # the shared 576/512 slab: work numbered by new token, at most 1024 of them
+    assert L.kvq_extend_attention_workspace_bytes(1, 1, 128, 1, 576, 16, 8, 4) > 0
+    assert L.kvq_extend_attention_workspace_bytes(1, 8, 128, 1, 576, 16, 8, 200) == 0
+    assert call(Hq=128, Hkv=1, D=576, vp=256, vs=256, mn=200, B=8) == kvq.ERR_UNSUPPORTED
+    assert call(Hq=128, Hkv=1, D=576) == kvq.ERR_UNSUPPORTED  # separate pools at 576
 
 
 def test_656_byte_row_shape_and_validation():

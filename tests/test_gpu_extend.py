@@ -169,3 +169,34 @@ def test_extend_rows_past_max_new_untouched_and_empty_pool_zeroed():
     assert np.abs(gl[written] - ol[written]).max() < 1e-2
     assert np.all(g[4:6] == 7.0) and np.all(gl[4:6] == 5.0)   # past max_new: untouched
     assert np.all(g[6:9] == 0) and np.all(np.isneginf(gl[6:9]))  # empty pool
+
+
+@pytest.mark.parametrize("qtype", ["fp8_e4m3", "bf16", "fp8_ds_mla"])
+def test_extend_over_the_mla_slab(qtype):
+    """The shared 576/512 slab, 64 query heads: extends after a prefix, a
+    prefill, more new tokens than the pool holds, an empty sequence, masked
+    pages, sequences long enough to split into several items."""
+    from tests.test_gpu_mla import mla_workload
+    k = kvq()
+    wl = mla_workload(64, [900, 40, 3, 0, 3000], 200, seed=13, mask_frac=0.1)
+    pools = fill_both(wl, qtype)
+    news = [9, 40, 5, 0, 2]
+    q_start = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    T = int(q_start[-1])
+    q = W.extend_queries(wl, T)
+    say("extend over the slab", qtype)
+    out, lse = k.extend_attention(qtype, dev_bf16(q), dev_i32(q_start), max(news), pools["kp"],
+                                  pools["ks"], pools["kp"], pools["ks"], dev_i32(wl.page_table),
+                                  dev_i32(wl.seq_lens), wl.sm_scale)
+    torch.cuda.synchronize()
+    g = bf16_to_f64(host_u16(out)).reshape(-1, 512)
+    gl = lse.cpu().numpy().astype(np.float64).reshape(-1)
+    o, ol = oracle.extend_attention(qtype, q, q_start, pools["okp"], pools["oks"], pools["okp"],
+                                    pools["oks"], wl.page_table, wl.seq_lens, 1, 576, W.PAGE,
+                                    wl.num_pages, wl.sm_scale, head_dim_v=512)
+    assert rel_err(g, o) <= TOL
+    fin = np.isfinite(ol)
+    assert np.array_equal(np.isfinite(gl), fin)
+    assert np.abs(gl[fin] - ol[fin]).max() < 1e-2
+    s2 = int(q_start[2])  # 5 new tokens, 3 in the pool: the first 2 see nothing
+    assert np.all(g[s2 * 64:(s2 + 2) * 64] == 0)
