@@ -286,17 +286,23 @@ size_t kvq_extend_attention_workspace_bytes(kvq_dtype dtype, int batch, int n_q_
  *   q_start    : device int32 [batch + 1]: q_start[0] = 0, nondecreasing, each
  *                difference at most max_new_tokens (rows past max_new_tokens of
  *                a sequence are not written).
- *   k_pool, v_pool, scales, page_table, seq_lens, num_pages: as kvq_paged_decode
- *                (separate K and V pools, head_dim 64, 128 or 256).
- *   out_bf16   : device bf16 [T][n_q_heads][head_dim]; lse: device fp32
- *                [T][n_q_heads] or NULL.
+ *   k_pool, v_pool, scales, page_table, seq_lens, num_pages: as kvq_paged_decode:
+ *                separate K and V pools with head_dim 64, 128 or 256, or the
+ *                shared 576/512 slab (k_pool == v_pool, k_scales == v_scales,
+ *                n_kv_heads 1, head_dim 576; batch x max_new_tokens at most
+ *                1024), whose V is the first 512 elements of each row.
+ *   out_bf16   : device bf16 [T][n_q_heads][head_dim] (the slab: [T][n_q_heads]
+ *                [512]); lse: device fp32 [T][n_q_heads] or NULL.
  *   workspace  : as kvq_paged_decode, sized by
  *                kvq_extend_attention_workspace_bytes(): zeroed once, left at
  *                zero by every call; calls sharing it must not overlap.  It
  *                holds split-K partials for every tile and grows linearly with
  *                max_new_tokens (8 sequences x 1024 pages, 16/8 heads, head_dim
  *                128: 21 MB at 64 new tokens, 1.4 GB at 4096).
- * The query rows of a kv head (token-major, max_new_tokens x G of them) run on
+ * Over the slab each new token runs as one query of the slab decode (its 128
+ * or fewer heads are one matrix-core tile set), over its own causal length.
+ * With separate pools the query rows of a kv head (token-major, max_new_tokens
+ * x G of them) run on
  * the matrix cores in tiles of 16, two tiles per work item up to head_dim 128;
  * each work item streams the K/V of its token range once for its tiles.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP;
