@@ -183,7 +183,8 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
     // the bounds: whole steps of pages per wave, at most kMaxItemPages, and
     // few enough chunks per sequence for the merge's weights to fit in LDS.
     const int step = kDecodeWaves * (p.mfma ? 1 : gqa_pages_per_step(qtype, head_dim_qk) * kGqaDepth);
-    const int64_t target = (p.mfma ? 2 : 1) * (int64_t)kPlanCUs;
+    // one item per CU; extend attention (many more query rows) two
+    const int64_t target = (p.mfma && ext_new > 0 ? 2 : 1) * (int64_t)kPlanCUs;
     const int cap = kMaxItemPages / step * step;
     const int64_t for_merge =
         ((int64_t)max_pages * p.gt * p.tn + kMergeMaxWeights - 1) / kMergeMaxWeights;
