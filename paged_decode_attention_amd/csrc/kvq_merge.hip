@@ -9,8 +9,9 @@
 // (log2-domain running max and sum) and acc_c[h][d] (fp32, unnormalized).
 // With M = max_c m_c and w_c = 2^(m_c - M):
 //   out[h][d] = sum_c w_c acc_c[h][d] / sum_c w_c l_c,  lse = (M + log2 sum_c w_c l_c) ln 2.
-// Block = (b, u, head, 16 columns); 64 groups of 4 threads take every 64th
-// chunk, a thread 4 columns; the first chunk rows and every chunk's (m, l)
+// Block = (b, u, head, 32 columns); 32 groups of 8 threads take every 32nd
+// chunk, a thread 4 columns (16 columns per block left half the groups idle
+// at 32 chunks: 7% slower at head_dim 256); the first chunk rows and every chunk's (m, l)
 // are loaded at once, before the weights are formed.  The decode kernels
 // merge in their last workgroup instead when the partials of a sequence are
 // few (see plan_decode).
@@ -21,7 +22,7 @@
 namespace kvq {
 namespace {
 
-constexpr int kCols = 16;                // columns per block
+constexpr int kCols = 32;                // columns per block
 constexpr int kLanesPerRow = kCols / 4;  // a thread takes 4 columns
 constexpr int kThreads = 256;
 constexpr int kGroups = kThreads / kLanesPerRow;  // chunk rows in flight per block
