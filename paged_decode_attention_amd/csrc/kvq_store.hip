@@ -43,8 +43,8 @@ namespace {
 constexpr int kThreads = 256;
 
 struct StoreGrid {
-  FastDiv per_token;  // lanes per token = n_heads * nb * 4
-  FastDiv per_head;   // lanes per head row = nb * 4
+  FastDiv per_token;  // lanes per token = n_heads * lanes per head row
+  FastDiv per_head;   // lanes per head row = nb * 2 (8-bit) or head_dim / 8 (bf16)
   uint32_t n_lanes;
 };
 
@@ -86,89 +86,102 @@ __device__ __forceinline__ void quantize8(const float* x, float s, uint32_t* out
   }
 }
 
+// Workgroups are dealt to the 8 XCDs in turn (block b runs on XCD b % 8).
+// Give each XCD one contiguous run of logical blocks instead, so that the
+// consecutive tokens of a page -- whose 128-byte scale rows and code rows
+// share cache lines -- are written through one L2 and leave it as whole
+// lines.  A bijection on [0, n): XCD x holds n / 8 blocks, plus one if
+// x < n % 8.
+__device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t n) {
+  const uint32_t q = n >> 3, r = n & 7u, x = b & 7u;
+  return x * q + (x < r ? x : r) + (b >> 3);
+}
+
 template <int QT>
 __global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs a, StoreGrid g) {
-  const uint32_t lane = blockIdx.x * kThreads + threadIdx.x;
-  // The quad of a block must stay together for the DPP max, so no early return
+  // 8-bit formats: 16 elements per lane, a 32-element block on a lane pair;
+  // bf16: 8 elements (one 16-byte piece) per lane
+  constexpr int E = (QT == QT_BF16) ? 8 : 16;
+  const uint32_t lane = xcd_block(blockIdx.x, gridDim.x) * kThreads + threadIdx.x;
+  // A lane pair must stay together for the DPP max, so no early return
   // before it; out-of-range lanes only skip their memory accesses.
   const bool in_range = lane < g.n_lanes;
   const uint32_t l = in_range ? lane : 0u;
   const uint32_t token = g.per_token.div(l);
   const uint32_t r0 = l - token * g.per_token.d;
   const uint32_t h = g.per_head.div(r0);
-  const uint32_t r1 = r0 - h * g.per_head.d;  // (block, quarter) within the row
-  const uint32_t blk = r1 >> 2, quarter = r1 & 3u;
+  const uint32_t r1 = r0 - h * g.per_head.d;  // piece of E elements within the row
   const int nb = a.head_dim >> 5;
 
   const int32_t slot = in_range ? a.slots[token] : -1;
   const int64_t cap = a.num_pages * (int64_t)a.page_size;
   const bool valid = slot >= 0 && (int64_t)slot < cap;
 
-  const int64_t src_off = (int64_t)token * a.stride + (int64_t)h * a.head_dim + blk * 32 + quarter * 8;
+  const int64_t col = (int64_t)r1 * E;
+  const int64_t src_off = (int64_t)token * a.stride + (int64_t)h * a.head_dim + col;
   const int64_t page = valid ? slot / a.page_size : 0;
   const int64_t off = valid ? slot - page * a.page_size : 0;
   const int64_t row = (page * a.n_heads + h) * a.page_size + off;
 
-  // the source rows exist for every token: both loads are issued at once,
+  // the source rows exist for every token: all loads are issued at once,
   // without waiting for the slot
-  uint4 raws[2];
+  constexpr int NP = E / 8;  // 16-byte source pieces per lane
+  uint4 raws[2][NP];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
-    raws[t] = a.src[t] ? *reinterpret_cast<const uint4*>(a.src[t] + src_off) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      raws[t][p] = a.src[t] ? *reinterpret_cast<const uint4*>(a.src[t] + src_off + 8 * p)
+                            : make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     if (a.src[t] == nullptr) continue;  // uniform: V absent
-    const uint4 raw = raws[t];
     if constexpr (QT == QT_BF16) {
-      if (valid)
-        *reinterpret_cast<uint4*>(a.pool[t] + (row * a.head_dim + blk * 32 + quarter * 8) * 2) = raw;
-    } else if constexpr (!qt_scaled(QT)) {
-      constexpr float M = (QT == QT_BF8C) ? 57344.0f : 448.0f;
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-      uint32_t codes[2];
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          v[2 * i] = fminf(fmaxf(bf16_lo(w[2 * d + i]), -M), M);
-          v[2 * i + 1] = fminf(fmaxf(bf16_hi(w[2 * d + i]), -M), M);
-        }
-        if constexpr (QT == QT_BF8C) {
-          const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(v[0], v[1], 0, false);
-          codes[d] = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(v[2], v[3], lo, true);
-        } else {
-          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-          codes[d] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
-        }
-      }
-      if (valid)
-        *reinterpret_cast<uint2*>(a.pool[t] + row * a.head_dim + blk * 32 + quarter * 8) =
-            make_uint2(codes[0], codes[1]);
+      if (valid) *reinterpret_cast<uint4*>(a.pool[t] + (row * a.head_dim + col) * 2) = raws[t][0];
     } else {
-      float x[8];
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-      float amax = 0.0f;
+      float x[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf16_lo(w[i]);
-        x[2 * i + 1] = bf16_hi(w[i]);
-        amax = fmaxf(amax, fmaxf(fabsf(x[2 * i]), fabsf(x[2 * i + 1])));
+      for (int p = 0; p < 2; ++p) {
+        const uint32_t w[4] = {raws[t][p].x, raws[t][p].y, raws[t][p].z, raws[t][p].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[8 * p + 2 * i] = bf16_lo(w[i]);
+          x[8 * p + 2 * i + 1] = bf16_hi(w[i]);
+        }
       }
-      amax = fmaxf(amax, dpp_xor1(amax));
-      amax = fmaxf(amax, dpp_xor2(amax));
-      constexpr float M = (QT == QT_Q8) ? 127.0f : 448.0f;
-      float sq = amax / M;  // IEEE fp32 division
-      sq = fminf(sq, 65504.0f);  // a quotient past the fp16 range saturates
-      const _Float16 sh = (_Float16)sq;  // round to nearest even
-      const float s = (float)sh;
-      uint32_t codes[2];
-      quantize8<QT>(x, s, codes);
-      if (valid) {
-        *reinterpret_cast<uint2*>(a.pool[t] + row * a.head_dim + blk * 32 + quarter * 8) =
-            make_uint2(codes[0], codes[1]);
-        if (quarter == 0) a.scales[t][row * nb + blk] = __builtin_bit_cast(uint16_t, sh);
+      uint32_t codes[4];
+      if constexpr (!qt_scaled(QT)) {
+        constexpr float M = (QT == QT_BF8C) ? 57344.0f : 448.0f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = fminf(fmaxf(x[4 * d + i], -M), M);
+          if constexpr (QT == QT_BF8C) {
+            const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(v[0], v[1], 0, false);
+            codes[d] = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(v[2], v[3], lo, true);
+          } else {
+            const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+            codes[d] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
+          }
+        }
+      } else {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+        amax = fmaxf(amax, dpp_xor1(amax));  // the other half of the block
+        constexpr float M = (QT == QT_Q8) ? 127.0f : 448.0f;
+        float sq = amax / M;  // IEEE fp32 division
+        sq = fminf(sq, 65504.0f);  // a quotient past the fp16 range saturates
+        const _Float16 sh = (_Float16)sq;  // round to nearest even
+        const float s = (float)sh;
+        quantize8<QT>(x, s, codes);
+        quantize8<QT>(x + 8, s, codes + 2);
+        if (valid && (r1 & 1u) == 0) a.scales[t][row * nb + (r1 >> 1)] = __builtin_bit_cast(uint16_t, sh);
       }
+      if (valid)
+        *reinterpret_cast<uint4*>(a.pool[t] + row * a.head_dim + col) =
+            make_uint4(codes[0], codes[1], codes[2], codes[3]);
     }
   }
 }
@@ -310,9 +323,9 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t s) {
   }
   if (a.n_tokens == 0) return hipSuccess;
   const int nb = a.head_dim / 32;
-  // bf16 pools are copied in 16-byte pieces with the same lane layout: one
-  // "block" of 32 elements = 4 lanes of 8 elements.
-  const uint32_t per_head = (uint32_t)(a.qtype == QT_BF16 ? a.head_dim / 8 : nb * 4);
+  // 8-bit formats: a 32-element block = 2 lanes of 16 elements; bf16 pools
+  // are copied in 16-byte pieces of 8 elements.
+  const uint32_t per_head = (uint32_t)(a.qtype == QT_BF16 ? a.head_dim / 8 : nb * 2);
   const uint32_t per_token = per_head * (uint32_t)a.n_heads;
   // keep every launch below 2^31 lanes
   const int64_t max_tokens = ((int64_t)1 << 31) / per_token;
