@@ -178,6 +178,7 @@ def cpu_baseline(wl, qtype, k_rows, v_rows, q_bits):
         "value": round(dec_bytes / (t2 - t1) / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": ("%d layer decodes (of the step's 28) of all %d sequences x %d heads over "
                    "%d tokens each: %.2f s, %.1f MB algorithmic; the oracle's fill of that "
@@ -188,6 +189,49 @@ def cpu_baseline(wl, qtype, k_rows, v_rows, q_bits):
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def arith_dtype(qtype: str) -> str:
+    """What the path computes in: the stored codes meet bf16 queries as bf16
+    operands (dot2 / MFMA) with fp32 accumulation and an fp32 softmax."""
+    return "bf16 operands, fp32 accumulation (%s storage)" % qtype
+
+
+def median_of_means(elapsed_ms, counts):
+    """Median over groups of (milliseconds, calls) of the per-call mean."""
+    means = sorted(t / n for t, n in zip(elapsed_ms, counts))
+    return means[len(means) // 2]
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def timed_replays(graph, n_replays, groups=5):
+    """Replay `graph` n_replays times split into `groups` runs, each between
+    two HIP events on the current stream; returns (median per-replay ms,
+    list of the group means)."""
+    import torch
+    groups = max(1, min(groups, n_replays))
+    sizes = [n_replays // groups + (1 if i < n_replays % groups else 0) for i in range(groups)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in sizes]
+    torch.cuda.synchronize()
+    for (e0, e1), n in zip(ev, sizes):
+        e0.record()
+        for _ in range(n):
+            graph.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    return median_of_means(ms, sizes), [round(t / n, 5) for t, n in zip(ms, sizes)]
 
 
 SPARSE_K = 256  # tokens listed per query by the sparse MLA workload
@@ -281,14 +325,18 @@ def decode_only(args, wl, qtype, dev, sparse_k=0) -> int:
         log("ran %d decode calls" % (args.steps * R))
         return 0
     K = args.steps
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(K):
-        for c in calls:
-            c()
-    t1.record()
+    # 5 runs of K sweeps over the replicas, an event pair around each run:
+    # the median run's mean per call
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(5)]
+    for e0, e1 in ev:
+        e0.record()
+        for _ in range(K):
+            for c in calls:
+                c()
+        e1.record()
     torch.cuda.synchronize()
-    us = t0.elapsed_time(t1) * 1e3 / (K * R)
+    us = median_of_means([e0.elapsed_time(e1) for e0, e1 in ev], [K * R] * 5) * 1e3
     nbytes = wl.algorithmic_bytes(qtype)
     n_tok = int(np.minimum(wl.seq_lens, wl.max_pages * W.PAGE).sum())
     res = {
@@ -299,7 +347,7 @@ def decode_only(args, wl, qtype, dev, sparse_k=0) -> int:
         "steps": K,
         "warmup": args.warmup,
         "higher_is_better": True,
-        "dtype": "f32",
+        "dtype": arith_dtype(qtype),
         "data": "synthetic",
         "config": {"workload": wl.name, "kv_storage": qtype, "replicas": R},
         "decode_call_us": round(us, 3),
@@ -330,14 +378,8 @@ def replay_us(args, calls, strm) -> float:
             c()
     for _ in range(args.warmup):
         graph.replay()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
-        graph.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) * 1e3 / (args.steps * len(calls))
+    ms, _ = timed_replays(graph, 5 * args.steps)
+    return ms * 1e3 / len(calls)
 
 
 def extend_timing(args, wl, qtype, calls, q_start, strm) -> int:
@@ -367,7 +409,7 @@ def extend_timing(args, wl, qtype, calls, q_start, strm) -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "higher_is_better": False,
-        "dtype": "f32",
+        "dtype": arith_dtype(qtype),
         "data": "synthetic",
         "config": {"workload": "%s: %d sequences x %d tokens, the last %d of each new (causal), "
                                "%d q / %d kv heads, head_dim %d/%d" % (
@@ -401,14 +443,8 @@ def sparse_timing(args, wl, qtype, calls, topk_np, strm) -> int:
     for _ in range(args.warmup):
         graph.replay()
     K, R = args.steps, len(calls)
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(K):
-        graph.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    us = t0.elapsed_time(t1) * 1e3 / (K * R)
+    ms, _ = timed_replays(graph, 5 * K)
+    us = ms * 1e3 / R
     # algorithmic bytes: the listed rows (codes + scales), their page-table
     # entries, the lists, seq_lens, Q and O
     per_row = {"bf16": 2 * 576, "fp8_e4m3": 612, "q8_0": 612, "fp8_e4m3_cast": 576,
@@ -425,7 +461,7 @@ def sparse_timing(args, wl, qtype, calls, topk_np, strm) -> int:
         "steps": K,
         "warmup": args.warmup,
         "higher_is_better": False,
-        "dtype": "f32",
+        "dtype": arith_dtype(qtype),
         "data": "synthetic",
         "config": {"workload": "sparse top-%d decode over the %s slab (%d queries x %d heads, "
                                "%d distinct random positions each)" % (
@@ -592,14 +628,8 @@ def main() -> int:
         step()
     for _ in range(args.warmup):
         graph.replay()
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for _ in range(K):
-        graph.replay()
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / K
+    # exactly K steps, in 5 groups (one event pair each): the median group mean
+    ms_step, step_means = timed_replays(graph, K)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     # (2b) the decode launches alone: the L layers' decodes captured back to
     # back into one graph, replayed K times between two events on their
@@ -611,14 +641,9 @@ def main() -> int:
             decodes[layer]()
     for _ in range(args.warmup):
         dgraph.replay()
-    d_start, d_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    d_start.record()
-    for _ in range(K):
-        dgraph.replay()
-    d_end.record()
-    torch.cuda.synchronize()
-    dec_graph = d_start.elapsed_time(d_end) / (K * L)  # ms per decode launch
+    # 5 runs of K replays: the median run's mean
+    dg_ms, dec_means = timed_replays(dgraph, 5 * K)
+    dec_graph = dg_ms / L  # ms per decode launch
     # (3) the store at the mixed workload's size: 8192 new tokens (the last 128
     # of 64 sequences) x 8 kv heads x 128, K and V in one fused kvq_store into
     # a 2^20-slot pool, timed alone: 8 calls captured back to back in one
@@ -639,14 +664,8 @@ def main() -> int:
             big()
     for _ in range(args.warmup):
         sgraph.replay()
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    s0.record()
-    for _ in range(K):
-        sgraph.replay()
-    s1.record()
-    torch.cuda.synchronize()
-    big_us = s0.elapsed_time(s1) * 1e3 / (K * 8)
+    sg_ms, _ = timed_replays(sgraph, 5 * K)
+    big_us = sg_ms * 1e3 / 8
     big_bytes = store_bytes(int(mslots.numel()), H, D, qtype)
     achieved = dec_bytes / (dec_graph * 1e-3) / 1e9
     log("step %.3f ms (graph), decode launch %.2f us (decode-only graph; %.2f us with an event "
@@ -664,7 +683,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": arith_dtype(qtype),
         "data": "synthetic",
         "config": {
             "workload": "decode step (replayed as one HIP graph), %d layers x (store 1 new token "
@@ -681,6 +700,10 @@ def main() -> int:
         },
         "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "timing": "median of 5 group means (HIP events on the stream around graph replays): "
+                  "the step over exactly %d steps; the decode launch and the store over 5 x %d "
+                  "replays" % (K, K),
+        "step_ms_group_means": step_means,
         "decode_call_us": round(dec_graph * 1e3, 3),
         "decode_call_us_eager_events": round(dec_avg * 1e3, 3),
         "store_call_us": round(st_avg * 1e3, 3),

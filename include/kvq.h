@@ -103,14 +103,14 @@ typedef enum {
  * model: the caller should size allocations and token budgets with this same
  * function, so that the budget and the pool cannot disagree [PR113 §One
  * ordering trap worth knowing about; PR103 §What: unit_bytes()/kv_cost() on
- * effective bytes].  Host-only, pure.  *code_bytes and *scale_bytes (each
- * nullable) receive the two parts; scale bytes are 0 for KVQ_BF16 and the
- * cast types.
+ * effective bytes].  Host-only, pure.  *scale_bytes (nullable) receives the
+ * bytes of the scale buffer (0 for KVQ_BF16, the cast types and the 656-byte
+ * row); the code buffer is the return value minus that.
  * Returns -1 (and sets the error message) on invalid arguments:
  * num_pages < 0, page_size < 1, n_heads < 1, head_dim < 1, head_dim not a
  * multiple of 32 for an 8-bit type, or an unknown dtype. */
 int64_t kvq_pool_bytes(kvq_dtype dtype, int64_t num_pages, int page_size, int n_heads,
-                       int head_dim, int64_t* code_bytes, int64_t* scale_bytes);
+                       int head_dim, int64_t* scale_bytes);
 
 /* Quantize-on-store [PR103 §What: store kernel, per-block max-abs -> codes +
  * scales; review §"A bug on sm_89": clamp, then round to nearest even for
@@ -123,7 +123,10 @@ int64_t kvq_pool_bytes(kvq_dtype dtype, int64_t num_pages, int page_size, int n_
  *     code_i = round(clamp(fp32(x_i / s), -M, M)), e4m3: nearest even,
  *         q8_0: half away from zero; s == 0 gives all-zero codes.
  * Both quotients are IEEE fp32 divisions; the result is bit-exact and
- * deterministic.  KVQ_BF16 copies the row unchanged.  The cast types store
+ * deterministic.  An infinite element makes max|x| / M infinite, so its
+ * block's scale is held at 65504: the element stores +-M and the others
+ * their quotient by 65504.  NaN elements are not supported (their codes and
+ * their block's scale are unspecified).  KVQ_BF16 copies the row unchanged.  The cast types store
  *     code_i = round(clamp(x_i, -M, M)), nearest even, M = 448 (e4m3) or
  *         57344 (e5m2), and write no scale.
  *
@@ -160,10 +163,12 @@ int kvq_dequant(kvq_dtype dtype, const void* pool, const uint16_t* scales,
                 int page_size, int64_t num_pages, void* out_bf16, kvq_stream_t stream);
 
 /* Workspace bytes kvq_paged_decode needs for these shapes (split-K partial
- * results).  0 if the shapes are invalid (see kvq_paged_decode). Host-only. */
-size_t kvq_paged_decode_workspace_bytes(kvq_dtype dtype, int batch, int n_q_heads,
-                                        int n_kv_heads, int head_dim_qk, int head_dim_v,
-                                        int page_size, int max_pages);
+ * results and arrival counters), for any storage type.  The shapes name the
+ * kernel: n_kv_heads == 1 with head_dim_v == 512 is the shared 576/512 slab,
+ * any other shape has head_dim_qk == head_dim_v.  0 if no storage type
+ * supports the shapes (see kvq_paged_decode).  Host-only, pure. */
+size_t kvq_paged_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads,
+                                        int head_dim_v, int max_pages, int page_size);
 
 /* Paged decode attention: one bf16 query token per sequence against the
  * quantized pool [PR103 §What: dequant inside the attention kernels behind a
@@ -190,6 +195,12 @@ size_t kvq_paged_decode_workspace_bytes(kvq_dtype dtype, int batch, int n_q_head
  *   page_table : device int32 [batch][pt_stride]; columns >= max_pages are
  *                never read.
  *   seq_lens   : device int32 [batch]; negative counts as 0.
+ *   seq_lens_host : host int32 [batch] holding the same values, or NULL.
+ *                The kernels plan the split from seq_lens on the device
+ *                either way (the device values decide the result); given
+ *                the host copy, the launch is sized to the exact number of
+ *                work items instead of an upper bound.  Read before the
+ *                call returns.
  *   out_bf16   : device bf16 [batch][n_q_heads][head_dim_v].
  *   lse        : device fp32 [batch][n_q_heads], or NULL.
  *   workspace  : device, at least kvq_paged_decode_workspace_bytes() bytes,
@@ -208,10 +219,10 @@ size_t kvq_paged_decode_workspace_bytes(kvq_dtype dtype, int batch, int n_q_head
 int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
                      const uint16_t* k_scales, const void* v_pool, const uint16_t* v_scales,
                      const int32_t* page_table, int64_t pt_stride, const int32_t* seq_lens,
-                     int batch, int n_q_heads, int n_kv_heads, int head_dim_qk, int head_dim_v,
-                     int page_size, int max_pages, int64_t num_pages, float sm_scale,
-                     void* out_bf16, float* lse, void* workspace, size_t workspace_bytes,
-                     kvq_stream_t stream);
+                     const int32_t* seq_lens_host, int batch, int n_q_heads, int n_kv_heads,
+                     int head_dim_qk, int head_dim_v, int page_size, int max_pages,
+                     int64_t num_pages, float sm_scale, void* out_bf16, float* lse,
+                     void* workspace, size_t workspace_bytes, kvq_stream_t stream);
 
 /* Workspace bytes kvq_sparse_mla_decode needs: the gathered rows of every
  * list (codes and scales), their page table and lengths, and the split-K

@@ -95,6 +95,8 @@ def _declare(L):
     L.kvo_paged_decode.restype = None
     L.kvo_e4m3_encode_array.argtypes = [P, c.c_int64, P]
     L.kvo_e4m3_encode_array.restype = None
+    L.kvo_e4m3_encode_bits.argtypes = [c.c_uint32, c.c_int64, P]
+    L.kvo_e4m3_encode_bits.restype = None
     L.kvo_q8_encode_array.argtypes = [P, c.c_int64, P]
     L.kvo_q8_encode_array.restype = None
     L.kvo_sparse_mla_decode.argtypes = [c.c_int, P, P, P, P, c.c_int64, P, P, c.c_int64, c.c_int,
@@ -139,6 +141,21 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
     v = np.ascontiguousarray(v, dtype=np.float32)
     out = np.empty(v.shape, dtype=np.uint8)
     lib().kvo_e4m3_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e4m3_encode_bits(first: int, count: int, threads: int | None = None) -> np.ndarray:
+    """e4m3 codes of the fp32 values whose bit patterns are first .. first +
+    count - 1 (the encoder over a range, split across threads)."""
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty(count, dtype=np.uint8)
+    threads = threads or default_threads()
+    per = -(-count // threads) if count else 0
+    L = lib()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda k: L.kvo_e4m3_encode_bits(first + k * per, min(per, count - k * per),
+                                                       out.ctypes.data + k * per),
+                    [k for k in range(threads) if k * per < count]))
     return out
 
 

@@ -715,6 +715,15 @@ void kvo_sparse_mla_decode(int qtype, const uint16_t* q, const uint8_t* slab,
 void kvo_e4m3_encode_array(const float* v, int64_t n, uint8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = kvo_e4m3_encode(v[i]);
 }
+/* The fp32 values with bit patterns first, first + 1, ..., first + n - 1. */
+void kvo_e4m3_encode_bits(uint32_t first, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) {
+    uint32_t b = first + (uint32_t)i;
+    float v;
+    memcpy(&v, &b, sizeof v);
+    out[i] = kvo_e4m3_encode(v);
+  }
+}
 void kvo_q8_encode_array(const float* v, int64_t n, int8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = kvo_q8_encode(v[i]);
 }

@@ -18,6 +18,8 @@
 #include <string>
 
 #include "kvq.h"
+#include "kvq_debug.h"
+#include "kvq_attn.h"
 #include "kvq_internal.h"
 
 namespace {
@@ -70,6 +72,30 @@ int num_cus_current() {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Work items of a decode call from host copies of the lengths, by the rule
+// the kernels apply to the device copies (at least 1, so that one workgroup
+// still writes the outputs of empty sequences).
+int64_t host_items(const kvq::DecodePlan& p, const kvq::DecodeArgs& a, const int32_t* lens) {
+  const int64_t cap = (int64_t)a.max_pages * kvq::kPageSize;
+  auto clamp_len = [&](int b) {
+    int64_t L = lens[b];
+    return L < 0 ? (int64_t)0 : (L > cap ? cap : L);
+  };
+  int64_t item_tokens, units = 1;
+  if (p.kind == kvq::DK_MLA) {
+    item_tokens = (int64_t)p.item_pages * kvq::kPageSize;
+  } else {
+    units = (int64_t)a.n_kv_heads * p.n_hg;
+    int64_t pages = 0;
+    for (int b = 0; b < a.batch; ++b) pages += (clamp_len(b) + kvq::kPageSize - 1) / kvq::kPageSize;
+    item_tokens = kvq::rule_item_tokens(
+        kvq::ItemRule{p.step, p.min_pages, p.cap_pages, p.target}, pages, (int)units);
+  }
+  int64_t items = 0;
+  for (int b = 0; b < a.batch; ++b) items += (clamp_len(b) + item_tokens - 1) / item_tokens * units;
+  return items < 1 ? 1 : items;
+}
+
 // Shared by kvq_store and kvq_dequant.
 int check_rows(int dtype, int64_t n_tokens, int n_heads, int head_dim, int page_size,
                int64_t num_pages, const char* fn) {
@@ -92,6 +118,89 @@ int check_rows(int dtype, int64_t n_tokens, int n_heads, int head_dim, int page_
   if (num_pages * (int64_t)page_size > INT32_MAX)
     return fail(KVQ_ERR_ARG, "%s: pool capacity exceeds 2^31-1 slots", fn);
   return KVQ_OK;
+}
+
+// The validation and launches of kvq_paged_decode.
+int decode_call(const char* fn, kvq_dtype dtype, const void* q, const void* k_pool,
+                     const uint16_t* k_scales, const void* v_pool, const uint16_t* v_scales,
+                     const int32_t* page_table, int64_t pt_stride, const int32_t* seq_lens,
+                     const int32_t* seq_lens_host, int batch, int n_q_heads, int n_kv_heads,
+                     int head_dim_qk, int head_dim_v, int page_size, int max_pages,
+                     int64_t num_pages, float sm_scale, void* out_bf16, float* lse,
+                     void* workspace, size_t workspace_bytes, kvq_stream_t stream) {
+  if (!known_dtype(dtype)) return fail(KVQ_ERR_ARG, "%s: unknown dtype %d", fn, dtype);
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || max_pages < 1 || head_dim_qk < 1 ||
+      head_dim_v < 1 || page_size < 1)
+    return fail(KVQ_ERR_ARG, "%s: sizes must be >= 1", fn);
+  if (n_q_heads % n_kv_heads != 0)
+    return fail(KVQ_ERR_ARG, "%s: n_q_heads %d is not a multiple of n_kv_heads %d", fn,
+                n_q_heads, n_kv_heads);
+  if (dtype != KVQ_BF16 && (head_dim_qk % KVQ_BLOCK || head_dim_v % KVQ_BLOCK))
+    return fail(KVQ_ERR_ARG,
+                "%s: head_dim %d/%d is not a multiple of the %d-element block", fn,
+                head_dim_qk, head_dim_v, KVQ_BLOCK);
+  if (head_dim_v > head_dim_qk)
+    return fail(KVQ_ERR_ARG, "%s: head_dim_v %d > head_dim_qk %d", fn, head_dim_v,
+                head_dim_qk);
+  if (pt_stride < max_pages)
+    return fail(KVQ_ERR_ARG, "%s: pt_stride %lld < max_pages %d", fn,
+                (long long)pt_stride, max_pages);
+  if (num_pages < 1 || num_pages * (int64_t)page_size > INT32_MAX)
+    return fail(KVQ_ERR_ARG, "%s: num_pages must be in 1..2^31/page_size", fn);
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
+    return fail(KVQ_ERR_ARG, "%s: sm_scale is not finite", fn);
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out_bf16)
+    return fail(KVQ_ERR_ARG, "%s: null pointer", fn);
+  if (scaled(dtype) && (!k_scales || !v_scales))
+    return fail(KVQ_ERR_ARG, "%s: null scales", fn);
+  const bool shared = (k_pool == v_pool);
+  if (shared != (k_scales == v_scales) && scaled(dtype))
+    return fail(KVQ_ERR_ARG, "%s: k_pool == v_pool requires k_scales == v_scales", fn);
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out_bf16, 4))
+    return fail(KVQ_ERR_ARG, "%s: q and pools must be 16-byte aligned", fn);
+  kvq::DecodePlan plan;
+  const char* why = nullptr;
+  if (!kvq::plan_decode(dtype, batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, page_size,
+                        max_pages, &plan, &why))
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: %s", fn, why);
+  if (shared && plan.kind != kvq::DK_MLA)
+    return fail(KVQ_ERR_UNSUPPORTED,
+                "%s: k_pool == v_pool is only supported for the 576/512 slab", fn);
+  if (!shared && plan.kind == kvq::DK_MLA)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: the 576/512 shape needs the shared slab", fn);
+  if (!workspace || workspace_bytes < plan.bytes)
+    return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn,
+                plan.bytes, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256))
+    return fail(KVQ_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  kvq::DecodeArgs a;
+  a.qtype = dtype;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = static_cast<const uint8_t*>(k_pool);
+  a.k_scales = k_scales;
+  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.v_scales = v_scales;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.head_dim_qk = head_dim_qk;
+  a.head_dim_v = head_dim_v;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.sm_scale = sm_scale;
+  a.out = static_cast<uint16_t*>(out_bf16);
+  a.lse = lse;
+  a.workspace = workspace;
+  if (seq_lens_host) a.items_hint = host_items(plan, a, seq_lens_host);
+  const int cus = num_cus_current();
+  hipError_t e = (plan.kind == kvq::DK_MLA) ? kvq::launch_mla_decode(a, plan, cus, stream)
+                 : plan.mfma                 ? kvq::launch_gqa_mfma_decode(a, plan, cus, stream)
+                                             : kvq::launch_gqa_decode(a, plan, cus, stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
 }
 
 }  // namespace
@@ -188,7 +297,14 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
     const int cap = kMaxItemPages / step * step;
     const int64_t for_merge =
         ((int64_t)max_pages * p.gt * p.tn + kMergeMaxWeights - 1) / kMergeMaxWeights;
-    const int64_t min_pages = ((for_merge > step ? for_merge : step) + step - 1) / step * step;
+    int64_t min_pages = ((for_merge > step ? for_merge : step) + step - 1) / step * step;
+    // the in-kernel merge holds chunks x columns weights in LDS, and a
+    // sequence splits into ceil(max_pages / item pages) chunks: rounding up
+    // can add one chunk past max_pages * columns / kMergeMaxWeights when the
+    // column count does not divide kMergeMaxWeights (12 columns: 342 x 12)
+    while (min_pages <= cap &&
+           (max_pages + min_pages - 1) / min_pages * p.gt * p.tn > kMergeMaxWeights)
+      min_pages += step;
     if (min_pages > cap) return no("max_pages %d is too large for the split-K merge", max_pages);
     p.step = step;
     p.min_pages = (int)min_pages;
@@ -263,7 +379,7 @@ extern "C" {
 const char* kvq_last_error(void) { return g_err.c_str(); }
 
 int64_t kvq_pool_bytes(kvq_dtype dtype, int64_t num_pages, int page_size, int n_heads,
-                       int head_dim, int64_t* code_bytes, int64_t* scale_bytes) {
+                       int head_dim, int64_t* scale_bytes) {
   if (!known_dtype(dtype)) return fail(-1, "kvq_pool_bytes: unknown dtype %d", (int)dtype);
   if (num_pages < 0 || page_size < 1 || n_heads < 1 || head_dim < 1)
     return fail(-1, "kvq_pool_bytes: sizes must be positive (num_pages may be 0)");
@@ -276,7 +392,6 @@ int64_t kvq_pool_bytes(kvq_dtype dtype, int64_t num_pages, int page_size, int n_
                         : (dtype == KVQ_FP8_DS_MLA) ? num_pages * page_size * (int64_t)kvq::kDsmRow
                                                     : elems;
   const int64_t scales = scaled(dtype) ? (elems / KVQ_BLOCK) * 2 : 0;
-  if (code_bytes) *code_bytes = codes;
   if (scale_bytes) *scale_bytes = scales;
   g_err.clear();
   return codes + scales;
@@ -351,99 +466,45 @@ int kvq_dequant(kvq_dtype dtype, const void* pool, const uint16_t* scales,
   return ok();
 }
 
-size_t kvq_paged_decode_workspace_bytes(kvq_dtype dtype, int batch, int n_q_heads,
-                                        int n_kv_heads, int head_dim_qk, int head_dim_v,
-                                        int page_size, int max_pages) {
-  kvq::DecodePlan p;
+size_t kvq_paged_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads,
+                                        int head_dim_v, int max_pages, int page_size) {
+  // The shapes fix the kernel: one kv head with a 512-wide V is the 576/512
+  // slab, anything else has K as wide as V.  The storage type only changes
+  // how finely items may split, so the answer covers every type.
+  const int head_dim_qk =
+      (n_kv_heads == 1 && head_dim_v == kvq::kMlaDv) ? kvq::kMlaDqk : head_dim_v;
+  size_t need = 0;
   const char* why = nullptr;
-  if (!kvq::plan_decode(dtype, batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, page_size,
-                        max_pages, &p, &why)) {
+  for (int dtype : {KVQ_BF16, KVQ_FP8_E4M3, KVQ_Q8_0, KVQ_FP8_E4M3_CAST, KVQ_FP8_E5M2_CAST,
+                    KVQ_FP8_DS_MLA}) {
+    kvq::DecodePlan p;
+    const char* w = nullptr;
+    if (kvq::plan_decode(dtype, batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, page_size,
+                         max_pages, &p, &w)) {
+      if (p.bytes > need) need = p.bytes;
+    } else if (!why) {
+      why = w;
+    }
+  }
+  if (need == 0) {
     fail(KVQ_ERR_UNSUPPORTED, "kvq_paged_decode_workspace_bytes: %s", why);
     return 0;
   }
   g_err.clear();
-  return p.bytes;
+  return need;
 }
 
 int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
                      const uint16_t* k_scales, const void* v_pool, const uint16_t* v_scales,
                      const int32_t* page_table, int64_t pt_stride, const int32_t* seq_lens,
-                     int batch, int n_q_heads, int n_kv_heads, int head_dim_qk, int head_dim_v,
-                     int page_size, int max_pages, int64_t num_pages, float sm_scale,
-                     void* out_bf16, float* lse, void* workspace, size_t workspace_bytes,
-                     kvq_stream_t stream) {
-  if (!known_dtype(dtype)) return fail(KVQ_ERR_ARG, "kvq_paged_decode: unknown dtype %d", dtype);
-  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || max_pages < 1 || head_dim_qk < 1 ||
-      head_dim_v < 1 || page_size < 1)
-    return fail(KVQ_ERR_ARG, "kvq_paged_decode: sizes must be >= 1");
-  if (n_q_heads % n_kv_heads != 0)
-    return fail(KVQ_ERR_ARG, "kvq_paged_decode: n_q_heads %d is not a multiple of n_kv_heads %d",
-                n_q_heads, n_kv_heads);
-  if (dtype != KVQ_BF16 && (head_dim_qk % KVQ_BLOCK || head_dim_v % KVQ_BLOCK))
-    return fail(KVQ_ERR_ARG,
-                "kvq_paged_decode: head_dim %d/%d is not a multiple of the %d-element block",
-                head_dim_qk, head_dim_v, KVQ_BLOCK);
-  if (head_dim_v > head_dim_qk)
-    return fail(KVQ_ERR_ARG, "kvq_paged_decode: head_dim_v %d > head_dim_qk %d", head_dim_v,
-                head_dim_qk);
-  if (pt_stride < max_pages)
-    return fail(KVQ_ERR_ARG, "kvq_paged_decode: pt_stride %lld < max_pages %d",
-                (long long)pt_stride, max_pages);
-  if (num_pages < 1 || num_pages * (int64_t)page_size > INT32_MAX)
-    return fail(KVQ_ERR_ARG, "kvq_paged_decode: num_pages must be in 1..2^31/page_size");
-  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
-    return fail(KVQ_ERR_ARG, "kvq_paged_decode: sm_scale is not finite");
-  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out_bf16)
-    return fail(KVQ_ERR_ARG, "kvq_paged_decode: null pointer");
-  if (scaled(dtype) && (!k_scales || !v_scales))
-    return fail(KVQ_ERR_ARG, "kvq_paged_decode: null scales");
-  const bool shared = (k_pool == v_pool);
-  if (shared != (k_scales == v_scales) && scaled(dtype))
-    return fail(KVQ_ERR_ARG, "kvq_paged_decode: k_pool == v_pool requires k_scales == v_scales");
-  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out_bf16, 4))
-    return fail(KVQ_ERR_ARG, "kvq_paged_decode: q and pools must be 16-byte aligned");
-  kvq::DecodePlan plan;
-  const char* why = nullptr;
-  if (!kvq::plan_decode(dtype, batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, page_size,
-                        max_pages, &plan, &why))
-    return fail(KVQ_ERR_UNSUPPORTED, "kvq_paged_decode: %s", why);
-  if (shared && plan.kind != kvq::DK_MLA)
-    return fail(KVQ_ERR_UNSUPPORTED,
-                "kvq_paged_decode: k_pool == v_pool is only supported for the 576/512 slab");
-  if (!shared && plan.kind == kvq::DK_MLA)
-    return fail(KVQ_ERR_UNSUPPORTED, "kvq_paged_decode: the 576/512 shape needs the shared slab");
-  if (!workspace || workspace_bytes < plan.bytes)
-    return fail(KVQ_ERR_WORKSPACE, "kvq_paged_decode: workspace of %zu bytes needed, %zu given",
-                plan.bytes, workspace ? workspace_bytes : (size_t)0);
-  if (!aligned(workspace, 256))
-    return fail(KVQ_ERR_WORKSPACE, "kvq_paged_decode: workspace must be 256-byte aligned");
-  kvq::DecodeArgs a;
-  a.qtype = dtype;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k_pool = static_cast<const uint8_t*>(k_pool);
-  a.k_scales = k_scales;
-  a.v_pool = static_cast<const uint8_t*>(v_pool);
-  a.v_scales = v_scales;
-  a.page_table = page_table;
-  a.pt_stride = pt_stride;
-  a.seq_lens = seq_lens;
-  a.batch = batch;
-  a.n_q_heads = n_q_heads;
-  a.n_kv_heads = n_kv_heads;
-  a.head_dim_qk = head_dim_qk;
-  a.head_dim_v = head_dim_v;
-  a.max_pages = max_pages;
-  a.num_pages = num_pages;
-  a.sm_scale = sm_scale;
-  a.out = static_cast<uint16_t*>(out_bf16);
-  a.lse = lse;
-  a.workspace = workspace;
-  const int cus = num_cus_current();
-  hipError_t e = (plan.kind == kvq::DK_MLA) ? kvq::launch_mla_decode(a, plan, cus, stream)
-                 : plan.mfma                 ? kvq::launch_gqa_mfma_decode(a, plan, cus, stream)
-                                             : kvq::launch_gqa_decode(a, plan, cus, stream);
-  if (e != hipSuccess) return hip_fail(e, "kvq_paged_decode");
-  return ok();
+                     const int32_t* seq_lens_host, int batch, int n_q_heads, int n_kv_heads,
+                     int head_dim_qk, int head_dim_v, int page_size, int max_pages,
+                     int64_t num_pages, float sm_scale, void* out_bf16, float* lse,
+                     void* workspace, size_t workspace_bytes, kvq_stream_t stream) {
+  return decode_call("kvq_paged_decode", dtype, q, k_pool, k_scales, v_pool, v_scales, page_table,
+                     pt_stride, seq_lens, seq_lens_host, batch, n_q_heads, n_kv_heads,
+                     head_dim_qk, head_dim_v, page_size, max_pages, num_pages, sm_scale, out_bf16,
+                     lse, workspace, workspace_bytes, stream);
 }
 
 size_t kvq_extend_attention_workspace_bytes(kvq_dtype dtype, int batch, int n_q_heads,
@@ -650,6 +711,37 @@ int kvq_sparse_mla_decode(kvq_dtype dtype, const void* q, const void* slab,
   e = kvq::launch_mla_decode(a, lay.dense, num_cus_current(), stream);
   if (e != hipSuccess) return hip_fail(e, "kvq_sparse_mla_decode");
   return ok();
+}
+
+int kvq_debug_e4m3_encode_range(uint32_t first_bits, int64_t count, uint8_t* out_codes,
+                                kvq_stream_t stream) {
+  if (count < 0 || count % 4 != 0 || (int64_t)first_bits + count > ((int64_t)1 << 32))
+    return fail(KVQ_ERR_ARG, "kvq_debug_e4m3_encode_range: count %lld must be a multiple of 4 "
+                             "within the 2^32 bit patterns", (long long)count);
+  if (count == 0) return ok();
+  if (!out_codes || !aligned(out_codes, 4))
+    return fail(KVQ_ERR_ARG, "kvq_debug_e4m3_encode_range: out_codes null or not 4-byte aligned");
+  hipError_t e = kvq::launch_debug_e4m3(first_bits, count, out_codes, stream);
+  if (e != hipSuccess) return hip_fail(e, "kvq_debug_e4m3_encode_range");
+  return ok();
+}
+
+int kvq_debug_decode_plan(kvq_dtype dtype, int batch, int n_q_heads, int n_kv_heads,
+                          int head_dim_qk, int head_dim_v, int max_pages, int max_new_tokens,
+                          int64_t* out, int n_out) {
+  kvq::DecodePlan p;
+  const char* why = nullptr;
+  if (!kvq::plan_decode(dtype, batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v,
+                        kvq::kPageSize, max_pages, &p, &why, max_new_tokens > 0 ? max_new_tokens : 0))
+    return fail(KVQ_ERR_UNSUPPORTED, "kvq_debug_decode_plan: %s", why);
+  const int64_t v[] = {p.kind, p.gt, p.tn, p.n_hg, p.step, p.min_pages, p.cap_pages, p.target,
+                       p.max_items, (int64_t)p.bytes, p.item_pages, p.fused_merge ? 1 : 0,
+                       p.mfma ? 1 : 0};
+  const int n = (int)(sizeof v / sizeof v[0]);
+  int k = 0;
+  for (; out && k < n_out && k < n; ++k) out[k] = v[k];
+  g_err.clear();
+  return k;
 }
 
 }  // extern "C"

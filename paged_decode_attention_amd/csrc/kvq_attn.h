@@ -166,7 +166,7 @@ struct ItemRule {
 
 // Tokens per work item under rule r for a batch holding `pages` pages in
 // all, `units` items per chunk of a sequence.
-__device__ __forceinline__ int rule_item_tokens(const ItemRule& r, int64_t pages, int units) {
+__host__ __device__ inline int rule_item_tokens(const ItemRule& r, int64_t pages, int units) {
   const int64_t work = pages * units;
   int64_t ip = (work + r.target - 1) / r.target;
   ip = (ip + r.step - 1) / r.step * r.step;

@@ -610,15 +610,13 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
 
     if (nc > 1 && p.fused) {
       // ---- the last item of this (sequence, kv head, head group) merges -------------
-      // every thread's partial stores are complete (agent-coherent) before
-      // the counter moves; the merging workgroup reads them with agent-scope
-      // loads
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_s_waitcnt(0);
+      // The workgroup's partial stores happen before thread 0's release
+      // increment (barrier); the workgroup that sees the final count
+      // acquires them and hands them on with the next barrier.
       __syncthreads();
       if (tid == 0) {
         const int old = __hip_atomic_fetch_add(&p.count[(int64_t)b * units + u], 1,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                               __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == nc - 1);
       }
       __syncthreads();
@@ -763,6 +761,7 @@ hipError_t launch_gqa_decode(const DecodeArgs& a, const DecodePlan& plan, int nu
   // items.
   int64_t grid = 2 * (int64_t)num_cus;
   if (grid > plan.max_items) grid = plan.max_items;
+  if (a.items_hint > 0 && grid > a.items_hint) grid = a.items_hint;  // exact from host lengths
   if (grid < 1) grid = 1;
   hipError_t e;
   switch (a.qtype) {

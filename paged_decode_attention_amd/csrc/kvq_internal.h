@@ -89,6 +89,8 @@ struct DequantArgs {
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
+// Test export: e4m3 codes of the fp32 bit patterns first .. first + count - 1.
+hipError_t launch_debug_e4m3(uint32_t first, int64_t count, uint8_t* out, hipStream_t s);
 
 // ---- paged decode --------------------------------------------------------------
 
@@ -131,6 +133,10 @@ struct DecodeArgs {
   // at most max_new of them per sequence.
   const int32_t* q_start = nullptr;
   int max_new = 0;
+  // Host-side only: the exact number of work items when the caller passed
+  // the lengths on the host too (0: unknown); the launch then holds no
+  // workgroup beyond it.  The kernels themselves plan from seq_lens.
+  int64_t items_hint = 0;
 };
 
 constexpr int kExtendMaxNew = 65536;  // new tokens per sequence, extend attention

@@ -755,6 +755,7 @@ hipError_t launch_mla_decode(const DecodeArgs& a, const DecodePlan& plan, int nu
   mp.part_out = reinterpret_cast<uint16_t*>(ws + plan.off_acc);
   int64_t grid = num_cus;  // one workgroup per CU fits the tiles' LDS
   if (grid > plan.max_items) grid = plan.max_items;
+  if (a.items_hint > 0 && grid > a.items_hint) grid = a.items_hint;  // exact from host lengths
   if (grid < 1) grid = 1;
   const int64_t max_chunks = (a.max_pages + plan.item_pages - 1) / plan.item_pages;
   const int merge_grid = (max_chunks > 1) ? a.batch * a.n_q_heads * 2 : 0;

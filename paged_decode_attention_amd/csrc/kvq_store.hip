@@ -5,12 +5,18 @@
 // "feat(kvcache): 8-bit DSV4 window/compressed KV behind --kv-cache-dtype"
 // (§What this adds).
 //
-// Mapping: four lanes own one 32-element block (8 bf16 = one 16-byte load
-// each).  The block max-abs is a 2-step DPP max inside the lane quad; every
-// lane then derives the same fp16 scale, quantizes its 8 elements and writes
-// 8 code bytes; lane 0 of the quad writes the 2-byte scale.  K and V of the
-// same (token, head, block) are handled by the same lane, so a thread keeps
-// two independent 16-byte loads in flight.
+// Mapping: a lane pair owns one 32-element block, 16 elements per lane (two
+// 16-byte loads of bf16 per tensor).  The block max-abs is one DPP xor-1 max
+// across the pair; both lanes derive the same fp16 scale, quantize their 16
+// elements and write 16 code bytes in one store; the even lane writes the
+// 2-byte scale.  K and V of the same (token, head, block) are handled by the
+// same lane, so a thread keeps four independent 16-byte loads in flight.
+// Workgroups are remapped so that each XCD takes one contiguous run of
+// tokens (xcd_block).
+//
+// Infinite elements saturate: the block max is then infinite, its scale is
+// held at 65504, the infinite element stores +-M and the others their
+// quotient by 65504.  NaN elements are not supported.
 //
 // The cast types (a per-tensor scale of 1.0, [PR126] "Add fp8 KV-cache
 // quantization (--kv-dtype)" §How it works) take the same lanes without the
@@ -62,16 +68,17 @@ __device__ __forceinline__ void quantize8(const float* x, float s, uint32_t* out
   for (int i = 0; i < 8; ++i) {
     const float q0 = x[i] * r;
     // x / s (see the header); the sign is x's (s > 0), also for a -0 element,
-    // which the correction step alone would turn into +0
-    const float q = copysignf(fmaf(fmaf(-s, q0, x[i]), r, q0), x[i]);
+    // which the correction step alone would turn into +0.  Past +-M the
+    // clamp decides and the estimate is kept: for an infinite element the
+    // residual would be inf - inf (NaN), which the clamp turns into -M.
+    const float qc = fmaf(fmaf(-s, q0, x[i]), r, q0);
+    const float q = copysignf(fabsf(q0) > M ? q0 : qc, x[i]);
     v[i] = fminf(fmaxf(q, -M), M);
   }
   if constexpr (QT == QT_FP8) {
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w + 0], v[4 * w + 1], 0, false);
-      out2[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w + 2], v[4 * w + 3], lo, true);
-    }
+    for (int w = 0; w < 2; ++w)
+      out2[w] = e4m3x4_clamped(v[4 * w + 0], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3]);
   } else {
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
@@ -161,8 +168,7 @@ __global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs a, StoreGrid 
             const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(v[0], v[1], 0, false);
             codes[d] = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(v[2], v[3], lo, true);
           } else {
-            const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-            codes[d] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], lo, true);
+            codes[d] = e4m3x4_clamped(v[0], v[1], v[2], v[3]);
           }
         }
       } else {
@@ -255,13 +261,10 @@ __global__ __launch_bounds__(kThreads) void store_dsm_kernel(StoreArgs a) {
   const float sc = m / 448.0f;
   float v[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = (sc > 0.0f) ? fminf(fmaxf(x[i] / sc, -448.0f), 448.0f) : 0.0f;
+  for (int i = 0; i < 8; ++i) v[i] = (sc > 0.0f) ? x[i] / sc : 0.0f;
   uint32_t c[2];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * k + 0], v[4 * k + 1], 0, false);
-    c[k] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[4 * k + 2], v[4 * k + 3], lo, true);
-  }
+  for (int k = 0; k < 2; ++k) c[k] = e4m3x4_clamped(v[4 * k + 0], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
   uint8_t* row = a.pool[0] + (int64_t)slot * kDsmRow;  // n_heads = 1
   *reinterpret_cast<uint2*>(row + 8 * lane) = make_uint2(c[0], c[1]);
   if ((lane & 15) == 0) *reinterpret_cast<float*>(row + kDsmLatent + 4 * (lane >> 4)) = sc;
@@ -350,6 +353,30 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Test export: the e4m3 encoder over a range of fp32 bit patterns, four
+// consecutive patterns per thread (count is a multiple of 4).
+__global__ __launch_bounds__(kThreads) void debug_e4m3_kernel(uint32_t first, uint32_t quads,
+                                                              uint32_t* out) {
+  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= quads) return;
+  const uint32_t b = first + 4 * i;
+  out[i] = e4m3x4_clamped(__uint_as_float(b), __uint_as_float(b + 1), __uint_as_float(b + 2),
+                          __uint_as_float(b + 3));
+}
+
+hipError_t launch_debug_e4m3(uint32_t first, int64_t count, uint8_t* out, hipStream_t s) {
+  for (int64_t done = 0; done < count;) {
+    const int64_t n = (count - done < ((int64_t)1 << 30)) ? count - done : ((int64_t)1 << 30);
+    const uint32_t quads = (uint32_t)(n / 4);
+    debug_e4m3_kernel<<<(quads + kThreads - 1) / kThreads, kThreads, 0, s>>>(
+        first + (uint32_t)done, quads, reinterpret_cast<uint32_t*>(out + done));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    done += n;
   }
   return hipSuccess;
 }

@@ -23,7 +23,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvq.so")
+# KVQ_LIB may name another build of the same sources (A/B timing of variants)
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(HERE, "libkvq.so")
 
 DTYPES = {"bf16": 0, "fp8_e4m3": 1, "q8_0": 2, "fp8_e4m3_cast": 3, "fp8_e5m2_cast": 4, "fp8_ds_mla": 5}
 SCALED = ("fp8_e4m3", "q8_0")  # storage types with a scale buffer
@@ -45,15 +46,15 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     c = ctypes
     P, I, I64 = c.c_void_p, c.c_int, c.c_int64
-    lib.kvq_pool_bytes.argtypes = [I, I64, I, I, I, c.POINTER(I64), c.POINTER(I64)]
+    lib.kvq_pool_bytes.argtypes = [I, I64, I, I, I, c.POINTER(I64)]
     lib.kvq_pool_bytes.restype = I64
     lib.kvq_store.argtypes = [I, P, P, I64, P, I64, I, I, I, I64, P, P, P, P, P]
     lib.kvq_store.restype = I
     lib.kvq_dequant.argtypes = [I, P, P, P, I64, I, I, I, I64, P, P]
     lib.kvq_dequant.restype = I
-    lib.kvq_paged_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.kvq_paged_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.kvq_paged_decode_workspace_bytes.restype = c.c_size_t
-    lib.kvq_paged_decode.argtypes = [I, P, P, P, P, P, P, I64, P, I, I, I, I, I, I, I, I64,
+    lib.kvq_paged_decode.argtypes = [I, P, P, P, P, P, P, I64, P, P, I, I, I, I, I, I, I, I64,
                                      c.c_float, P, P, P, c.c_size_t, P]
     lib.kvq_paged_decode.restype = I
     lib.kvq_sparse_mla_decode_workspace_bytes.argtypes = [I, I, I, I]
@@ -66,6 +67,10 @@ def _load() -> ctypes.CDLL:
     lib.kvq_extend_attention.argtypes = [I, P, P, I, P, P, P, P, P, I64, P, I, I, I, I, I, I, I64,
                                          c.c_float, P, P, P, c.c_size_t, P]
     lib.kvq_extend_attention.restype = I
+    lib.kvq_debug_e4m3_encode_range.argtypes = [c.c_uint32, I64, P, P]
+    lib.kvq_debug_e4m3_encode_range.restype = I
+    lib.kvq_debug_decode_plan.argtypes = [I, I, I, I, I, I, I, I, c.POINTER(I64), I]
+    lib.kvq_debug_decode_plan.restype = I
     lib.kvq_last_error.argtypes = []
     lib.kvq_last_error.restype = c.c_char_p
     return lib
@@ -77,6 +82,10 @@ LIB = _load()
 EXPORTS = ("kvq_pool_bytes", "kvq_store", "kvq_dequant", "kvq_paged_decode_workspace_bytes",
            "kvq_paged_decode", "kvq_sparse_mla_decode_workspace_bytes", "kvq_sparse_mla_decode",
            "kvq_extend_attention_workspace_bytes", "kvq_extend_attention", "kvq_last_error")
+# the test exports (kvq_debug.h)
+DEBUG_EXPORTS = ("kvq_debug_e4m3_encode_range", "kvq_debug_decode_plan")
+PLAN_FIELDS = ("kind", "gt", "tn", "n_hg", "step", "min_pages", "cap_pages", "target",
+               "max_items", "bytes", "item_pages", "fused_merge", "mfma")
 
 
 def last_error() -> str:
@@ -114,22 +123,51 @@ def _stream(device, stream) -> int | None:
 # ---- host-only -------------------------------------------------------------------
 
 def pool_bytes(dtype, num_pages: int, page_size: int, n_heads: int, head_dim: int):
-    """(total, code_bytes, scale_bytes) of one K or V pool; the cost model."""
-    cb, sb = ctypes.c_int64(0), ctypes.c_int64(0)
+    """(total, code_bytes, scale_bytes) of one K or V pool; the cost model
+    (kvq_pool_bytes returns the total and the scale part)."""
+    sb = ctypes.c_int64(0)
     total = LIB.kvq_pool_bytes(_dt(dtype), num_pages, page_size, n_heads, head_dim,
-                               ctypes.byref(cb), ctypes.byref(sb))
+                               ctypes.byref(sb))
     if total < 0:
         raise ValueError(last_error())
-    return total, cb.value, sb.value
+    return total, total - sb.value, sb.value
 
 
-def workspace_bytes(dtype, batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v,
-                    page_size, max_pages) -> int:
-    n = LIB.kvq_paged_decode_workspace_bytes(_dt(dtype), batch, n_q_heads, n_kv_heads,
-                                             head_dim_qk, head_dim_v, page_size, max_pages)
+def workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim_v, max_pages, page_size) -> int:
+    """kvq_paged_decode_workspace_bytes: enough for every storage type."""
+    n = LIB.kvq_paged_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim_v,
+                                             max_pages, page_size)
     if n == 0:
         raise NotImplementedError(last_error())
     return n
+
+
+def _host_lens(seq_lens_host):
+    """An int32 numpy copy of the lengths for the host argument (None: absent)."""
+    if seq_lens_host is None:
+        return None, None
+    import numpy as np
+    arr = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    return arr, arr.ctypes.data
+
+
+def debug_plan(dtype, batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, max_pages,
+               max_new_tokens=0):
+    """The decode planner's fields (PLAN_FIELDS) for these shapes, or None
+    when it refuses them (kvq_debug_decode_plan)."""
+    out = (ctypes.c_int64 * len(PLAN_FIELDS))()
+    n = LIB.kvq_debug_decode_plan(_dt(dtype), batch, n_q_heads, n_kv_heads, head_dim_qk,
+                                  head_dim_v, max_pages, max_new_tokens, out, len(PLAN_FIELDS))
+    if n < 0:
+        return None
+    return dict(zip(PLAN_FIELDS, list(out)[:n]))
+
+
+def debug_e4m3_encode_range(first_bits: int, count: int, out, stream=None) -> None:
+    """The device e4m3 encoder over fp32 bit patterns first_bits .. + count - 1
+    into the uint8 device tensor out (kvq_debug_e4m3_encode_range)."""
+    _check(LIB.kvq_debug_e4m3_encode_range(first_bits, count, _ptr(out),
+                                           _stream(out.device, stream)))
 
 
 DS_ROW = 656  # bytes of one row of the fp8_ds_mla slab (576 elements)
@@ -202,11 +240,12 @@ def dequant(dtype, pool, scales, slot_mapping, out=None, stream=None):
 
 def paged_decode(dtype, q, k_pool, k_scales, v_pool, v_scales, page_table, seq_lens,
                  sm_scale: float, head_dim_v: int | None = None, out=None, lse=None,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, seq_lens_host=None):
     """One-token decode attention over the paged pool; returns (out, lse).
 
     Pass v_pool=k_pool (and v_scales=k_scales) for the shared MLA slab, with
-    head_dim_v the V width taken from the front of each row."""
+    head_dim_v the V width taken from the front of each row.  seq_lens_host
+    (optional, the same lengths on the host) sizes the launch exactly."""
     batch, n_q_heads, head_dim_qk = q.shape
     num_pages, n_kv_heads, page_size, _ = k_pool.shape
     if head_dim_v is None:
@@ -220,14 +259,14 @@ def paged_decode(dtype, q, k_pool, k_scales, v_pool, v_scales, page_table, seq_l
         out = torch.empty((batch, n_q_heads, head_dim_v), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((batch, n_q_heads), dtype=torch.float32, device=q.device)
-    need = workspace_bytes(dtype, batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v,
-                           page_size, max_pages)
+    need = workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim_v, max_pages, page_size)
     if workspace is None:  # zero-filled once; each call leaves it zeroed
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
+    _lens, lens_ptr = _host_lens(seq_lens_host)
     rc = LIB.kvq_paged_decode(_dt(dtype), _ptr(q), _ptr(k_pool), _ptr(k_scales), _ptr(v_pool),
                               _ptr(v_scales), _ptr(page_table), pt_stride,
-                              _ptr(seq_lens), batch, n_q_heads, n_kv_heads, head_dim_qk,
+                              _ptr(seq_lens), lens_ptr, batch, n_q_heads, n_kv_heads, head_dim_qk,
                               head_dim_v, page_size, max_pages, num_pages, float(sm_scale),
                               _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                               _stream(q.device, stream))
@@ -345,7 +384,8 @@ class PreparedDecode:
     graph capture): calling it only crosses into the library."""
 
     def __init__(self, dtype, q, k_pool, k_scales, v_pool, v_scales, page_table, seq_lens,
-                 sm_scale, head_dim_v=None, out=None, lse=None, workspace=None, stream=None):
+                 sm_scale, head_dim_v=None, out=None, lse=None, workspace=None, stream=None,
+                 seq_lens_host=None):
         batch, n_q_heads, head_dim_qk = q.shape
         num_pages, n_kv_heads, page_size, _ = k_pool.shape
         head_dim_v = head_dim_v or v_pool.shape[3]
@@ -354,14 +394,14 @@ class PreparedDecode:
             (batch, n_q_heads, head_dim_v), dtype=torch.bfloat16, device=q.device)
         self.lse = lse if lse is not None else torch.empty(
             (batch, n_q_heads), dtype=torch.float32, device=q.device)
-        need = workspace_bytes(dtype, batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v,
-                               page_size, max_pages)
+        need = workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim_v, max_pages, page_size)
         self.workspace = workspace if workspace is not None else torch.zeros(
             need, dtype=torch.uint8, device=q.device)
         pt_stride = page_table.stride(0) if batch > 1 else max_pages
-        self._keep = (q, k_pool, k_scales, v_pool, v_scales, page_table, seq_lens)
+        lens, lens_ptr = _host_lens(seq_lens_host)
+        self._keep = (q, k_pool, k_scales, v_pool, v_scales, page_table, seq_lens, lens)
         self.args = (_dt(dtype), _ptr(q), _ptr(k_pool), _ptr(k_scales), _ptr(v_pool),
-                     _ptr(v_scales), _ptr(page_table), pt_stride, _ptr(seq_lens), batch,
+                     _ptr(v_scales), _ptr(page_table), pt_stride, _ptr(seq_lens), lens_ptr, batch,
                      n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, page_size, max_pages,
                      num_pages, float(sm_scale), _ptr(self.out), _ptr(self.lse),
                      _ptr(self.workspace), self.workspace.numel(), _stream(q.device, stream))

@@ -30,6 +30,7 @@ Workloads (all with page size 16):
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -110,12 +111,17 @@ class Workload:
         of `pages`, each page drawn from its own sub-stream (N(0,1)).  The mixed
         workload's pool background is defined this way, so that any subset of
         its 65536 pages can be generated on its own."""
+        from concurrent.futures import ThreadPoolExecutor
         H, D = self.n_kv_heads, self.head_dim_qk
         pages = np.asarray(pages, dtype=np.int64)
         out = np.empty((len(pages), PAGE, H, D), np.float32)
-        for i, pg in enumerate(pages):
-            rng = np.random.Generator(np.random.PCG64([self.seed, tensor, 1 << 24, int(pg)]))
+
+        def fill(i):  # numpy draws without holding the GIL
+            rng = np.random.Generator(np.random.PCG64([self.seed, tensor, 1 << 24, int(pages[i])]))
             out[i] = rng.standard_normal((PAGE, H, D), dtype=np.float32)
+
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, range(len(pages))))
         return to_bf16_bits(out.reshape(-1, H, D))
 
     def query(self) -> np.ndarray:

@@ -22,17 +22,21 @@ from tests.test_oracle_pins import FACTS
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def header_functions():
-    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+def header_functions(name="kvq.h"):
+    src = open(os.path.join(ROOT, "include", name)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_symbol():
-    names = header_functions()
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert "kvq.h" in headers and "kvq_debug.h" in headers
+    names = header_functions("kvq.h")
     assert set(names) == set(kvq.EXPORTS)
-    for n in names:
-        assert ctypes.cast(getattr(kvq.LIB, n), ctypes.c_void_p).value
+    assert set(header_functions("kvq_debug.h")) == set(kvq.DEBUG_EXPORTS)
+    for h in headers:
+        for n in header_functions(h):
+            assert ctypes.cast(getattr(kvq.LIB, n), ctypes.c_void_p).value, n
 
 
 def test_pool_bytes_is_17_16_per_element_and_32_17_vs_bf16():
@@ -58,7 +62,7 @@ def test_head_dim_not_multiple_of_32_is_rejected_up_front(dtype):
     rc = kvq.LIB.kvq_store(kvq.DTYPES[dtype], 16, 16, 48, 16, 1, 1, 48, 16, 4, 16, 16, 16, 16,
                            None)
     assert rc == kvq.ERR_ARG and "multiple of the 32-element" in kvq.last_error()
-    assert kvq.LIB.kvq_paged_decode_workspace_bytes(kvq.DTYPES[dtype], 1, 2, 1, 48, 48, 16, 4) == 0
+    assert kvq.LIB.kvq_paged_decode_workspace_bytes(1, 2, 1, 48, 4, 16) == 0
 
 
 def test_validation_errors_before_any_launch():
@@ -83,15 +87,15 @@ def test_validation_errors_before_any_launch():
 
 def test_decode_validation():
     L = kvq.LIB
-    args = dict(q=256, kp=256, ks=256, vp=512, vs=512, pt=256, sl=256, out=256, lse=None,
-                wsp=256)
+    args = dict(q=256, kp=256, ks=256, vp=512, vs=512, pt=256, sl=256, sl_host=None, out=256,
+                lse=None, wsp=256)
 
     def call(dtype=1, B=2, Hq=16, Hkv=8, D=128, Dv=128, ps=16, mp=8, pts=8, npg=64, ws=1 << 30,
              sm=0.1, **kw):
         a = dict(args, **kw)
         return L.kvq_paged_decode(dtype, a["q"], a["kp"], a["ks"], a["vp"], a["vs"], a["pt"], pts,
-                                  a["sl"], B, Hq, Hkv, D, Dv, ps, mp, npg, sm, a["out"], a["lse"],
-                                  a["wsp"], ws, None)
+                                  a["sl"], a["sl_host"], B, Hq, Hkv, D, Dv, ps, mp, npg, sm,
+                                  a["out"], a["lse"], a["wsp"], ws, None)
 
     assert call(Hq=12, Hkv=8) == kvq.ERR_ARG                 # not a multiple
     assert call(ps=32) == kvq.ERR_UNSUPPORTED and "page_size" in kvq.last_error()
@@ -106,8 +110,24 @@ def test_decode_validation():
     assert call(B=5000) == kvq.ERR_UNSUPPORTED
     # k_pool == v_pool is the shared-slab form, only for 576/512
     assert call(vp=256, vs=256) == kvq.ERR_UNSUPPORTED
-    need = kvq.workspace_bytes("fp8_e4m3", 2, 16, 8, 128, 128, 16, 8)
+    need = kvq.workspace_bytes(2, 16, 8, 128, 8, 16)
     assert call(ws=need - 1) == kvq.ERR_WORKSPACE
+    # the 656-byte row is the slab's format only
+    assert call(dtype=5) == kvq.ERR_UNSUPPORTED and "656-byte" in kvq.last_error()
+
+
+def test_workspace_query_covers_every_storage_type():
+    """kvq_paged_decode_workspace_bytes takes no storage type: its answer is
+    the largest workspace any type's plan needs for the shapes (the plans
+    read through the library's test export)."""
+    for B, Hq, Hkv, Dv, mp in [(8, 16, 8, 128, 1024), (3, 16, 2, 256, 2048), (64, 16, 8, 128, 8192),
+                               (1, 128, 1, 512, 10240), (2, 32, 1, 64, 3), (5, 8, 8, 32, 100)]:
+        need = kvq.workspace_bytes(B, Hq, Hkv, Dv, mp, 16)
+        assert need > 0 and need % 256 == 0
+        Dqk = 576 if (Hkv == 1 and Dv == 512) else Dv
+        plans = [kvq.debug_plan(dt, B, Hq, Hkv, Dqk, Dv, mp) for dt in kvq.DTYPES]
+        sizes = [p["bytes"] for p in plans if p is not None]
+        assert sizes and need == max(sizes)
 
 
 def test_python_errors_are_typed():
@@ -116,7 +136,7 @@ def test_python_errors_are_typed():
     with pytest.raises(ValueError):
         kvq.pool_bytes("int4", 1, 16, 1, 32)
     with pytest.raises(NotImplementedError):
-        kvq.workspace_bytes("fp8_e4m3", 1, 8, 1, 64, 64, 8, 4)
+        kvq.workspace_bytes(1, 8, 1, 64, 4, 8)
 
 
 def test_only_block_scaled_types_carry_scales():
@@ -159,7 +179,7 @@ def test_extend_validation():
     assert call(pts=4) == kvq.ERR_ARG
     assert call(sm=float("inf")) == kvq.ERR_ARG
     need = kvq.extend_workspace_bytes("fp8_e4m3", 2, 16, 8, 128, 16, 8, 64)
-    assert need > kvq.workspace_bytes("fp8_e4m3", 2, 16, 8, 128, 128, 16, 8)  # 8 tiles per kv head
+    assert need > kvq.workspace_bytes(2, 16, 8, 128, 8, 16)  # 8 tiles per kv head
     assert call(ws=need - 1) == kvq.ERR_WORKSPACE
     # the shared 576/512 slab: work numbered by new token, at most 1024 of them
     assert L.kvq_extend_attention_workspace_bytes(1, 1, 128, 1, 576, 16, 8, 4) > 0
@@ -175,14 +195,43 @@ def test_656_byte_row_shape_and_validation():
     L = kvq.LIB
     total, codes, scales = kvq.pool_bytes("fp8_ds_mla", 10, 16, 1, 576)
     assert total == codes == 10 * 16 * 656 and scales == 0
-    assert L.kvq_pool_bytes(5, 10, 16, 1, 512, None, None) == -1
-    assert L.kvq_pool_bytes(5, 10, 16, 2, 576, None, None) == -1
+    assert L.kvq_pool_bytes(5, 10, 16, 1, 512, None) == -1
+    assert L.kvq_pool_bytes(5, 10, 16, 2, 576, None) == -1
     # store: wrong shape, and a V source (the row is K and V at once)
     assert L.kvq_store(5, 16, None, 576, 16, 4, 1, 512, 16, 4, 16, None, None, None, None) == kvq.ERR_UNSUPPORTED
     assert L.kvq_store(5, 16, 16, 576, 16, 4, 1, 576, 16, 4, 16, None, 16, None, None) == kvq.ERR_ARG
     # decode: the slab shape only
-    assert kvq.workspace_bytes("fp8_ds_mla", 1, 128, 1, 576, 512, 16, 64) > 0
-    assert L.kvq_paged_decode_workspace_bytes(5, 2, 16, 8, 128, 128, 16, 8) == 0
+    assert kvq.workspace_bytes(1, 128, 1, 512, 64, 16) > 0
+    assert L.kvq_paged_decode(5, 256, 256, None, 512, None, 256, 8, 256, None, 2, 16, 8, 128, 128,
+                              16, 8, 64, 0.1, 256, None, 256, 1 << 30, None) == kvq.ERR_UNSUPPORTED
     assert "656-byte" in kvq.last_error()
     assert L.kvq_extend_attention_workspace_bytes(5, 2, 16, 8, 128, 16, 8, 4) == 0
     assert kvq.sparse_workspace_bytes("fp8_ds_mla", 1, 128, 256) > 0
+
+
+def test_in_kernel_merge_weights_fit_in_lds():
+    """The last workgroup of a split sequence merges its chunks with one LDS
+    weight per (chunk, query column), 4096 at most.  A sequence splits into at
+    most ceil(max_pages / item pages) chunks, and the kernels never size items
+    below the plan's fewest pages (their rule clamps to it), so the plan must
+    keep ceil(max_pages / min_pages) x columns within 4096 whenever the merge
+    runs inside the decode kernel: every G, new-token count, head_dim and
+    table width."""
+    checked = 0
+    for D in (32, 64, 128, 256):
+        for G in (1, 2, 3, 4, 5, 6, 8, 12, 16, 32):
+            for ext in (0, 1, 2, 3, 5, 7, 11, 64):
+                if ext and D == 32:
+                    continue
+                for mp in (1, 7, 100, 1000, 1365, 2048, 4095, 16384, 32768):
+                    for dt in ("fp8_e4m3", "bf16"):
+                        p = kvq.debug_plan(dt, 2, 2 * G, 2, D, D, mp, ext)
+                        if p is None or not p["fused_merge"]:
+                            continue
+                        checked += 1
+                        chunks = -(-mp // p["min_pages"])
+                        assert chunks * p["gt"] * p["tn"] <= 4096, (D, G, ext, mp, dt, p)
+                        assert p["min_pages"] % p["step"] == 0
+                        assert p["min_pages"] <= p["cap_pages"]
+    assert checked > 1000
+

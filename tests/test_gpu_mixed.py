@@ -4,12 +4,10 @@ pool, then paged decode of 64 sequences with log-uniform contexts in
 [1024, 131072], -1 masked page-table columns and pages shared between
 sequences.
 
-The background rows of the pages that the checked sequences read are drawn
-per page (Workload.page_rows) and stored on both sides; the new tokens' codes
-and scales must match the oracle's bit for bit, and the decode of three
-sequences (the shortest, the median and the longest context) within the
-attention tolerance.  Other sequences read partly unfilled (zero) pages and
-are not checked.
+The background rows of every page the batch reads are drawn per page
+(Workload.page_rows) and stored on both sides; the new tokens' codes and
+scales must match the oracle's bit for bit, and the decode of all 64
+sequences within the attention tolerance.
 
 Page keys: [PR103] "feat(kvcache): 8-bit KV cache (q8_0 / fp8_e4m3) behind
 --kv-cache-dtype" §What (store kernel, QUANT switch) and the review comment
@@ -36,28 +34,29 @@ def test_mixed_store_then_decode(qtype):
     wl = W.mixed()
     H, D = wl.n_kv_heads, wl.head_dim_qk
     k = kvq()
-    order = np.argsort(wl.seq_lens, kind="stable")
-    seqs = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+    # background: every page any sequence reads, in chunks of pages
     pages = set()
-    for b in seqs:
+    for b in range(wl.batch):
         n = (int(wl.seq_lens[b]) + W.PAGE - 1) // W.PAGE
         cols = wl.page_table[b, :n]
         pages.update(int(x) for x in cols[cols >= 0])
     pages = np.array(sorted(pages), np.int64)
-    say("mixed", qtype, "checked sequences", seqs, "background pages", len(pages))
-
-    # background: the pages the checked sequences read
-    bg_slots = (pages[:, None] * W.PAGE + np.arange(W.PAGE)[None]).reshape(-1).astype(np.int32)
-    bg_k, bg_v = wl.page_rows(0, pages), wl.page_rows(1, pages)
+    say("mixed", qtype, "background pages", len(pages))
     kp, ks = k.alloc_pool(qtype, wl.num_pages, H, D)
     vp, vs = k.alloc_pool(qtype, wl.num_pages, H, D)
     for t in (kp, ks, vp, vs):
         t.zero_()
-    k.store(qtype, dev_bf16(bg_k), dev_bf16(bg_v), dev_i32(bg_slots), kp, ks, vp, vs)
     okp, oks = np_pool(qtype, wl.num_pages, H, D)
     ovp, ovs = np_pool(qtype, wl.num_pages, H, D)
-    oracle.store(qtype, bg_k, bg_slots, H, D, W.PAGE, wl.num_pages, okp, oks)
-    oracle.store(qtype, bg_v, bg_slots, H, D, W.PAGE, wl.num_pages, ovp, ovs)
+    step = 4096
+    for lo in range(0, len(pages), step):
+        pg = pages[lo:lo + step]
+        bg_slots = (pg[:, None] * W.PAGE + np.arange(W.PAGE)[None]).reshape(-1).astype(np.int32)
+        bg_k, bg_v = wl.page_rows(0, pg), wl.page_rows(1, pg)
+        k.store(qtype, dev_bf16(bg_k), dev_bf16(bg_v), dev_i32(bg_slots), kp, ks, vp, vs)
+        oracle.store(qtype, bg_k, bg_slots, H, D, W.PAGE, wl.num_pages, okp, oks)
+        oracle.store(qtype, bg_v, bg_slots, H, D, W.PAGE, wl.num_pages, ovp, ovs)
+        torch.cuda.synchronize()
     del bg_k, bg_v
 
     # the step's new tokens: one fused K+V store call
@@ -74,7 +73,7 @@ def test_mixed_store_then_decode(qtype):
         assert np.array_equal(gpc, op[pg, :, off, :]), "codes differ at new slots"
         assert np.array_equal(host_u16(gs)[pg, :, off, :], os_[pg, :, off, :]), "scales differ"
 
-    # decode the whole batch; check the three sequences
+    # decode the whole batch; every row against the oracle
     q = wl.query()
     say("mixed decode", qtype)
     out, lse = k.paged_decode(qtype, dev_bf16(q), kp, ks, vp, vs, dev_i32(wl.page_table),
@@ -82,12 +81,10 @@ def test_mixed_store_then_decode(qtype):
     torch.cuda.synchronize()
     g_out = bf16_to_f64(host_u16(out)).reshape(-1, D)
     g_lse = lse.cpu().numpy().astype(np.float64).reshape(-1)
-    rows = np.array([b * wl.n_q_heads + h for b in seqs for h in range(wl.n_q_heads)], np.int32)
     o_out, o_lse = oracle.paged_decode(qtype, q, okp, oks, ovp, ovs, wl.page_table, wl.seq_lens,
-                                       H, D, D, W.PAGE, wl.num_pages, wl.sm_scale, rows=rows)
-    for i, b in enumerate(seqs):
-        sl = slice(i * wl.n_q_heads, (i + 1) * wl.n_q_heads)
-        err = rel_err(g_out[rows[sl]], o_out[sl])
-        say("  seq %d (context %d): rel err %.3e" % (b, int(wl.seq_lens[b]), err))
-        assert err <= TOL, (b, err)
-    assert np.abs(g_lse[rows] - o_lse).max() < 1e-2
+                                       H, D, D, W.PAGE, wl.num_pages, wl.sm_scale)
+    err = rel_err(g_out, o_out)
+    worst = max(rel_err(g_out[r], o_out[r]) for r in range(len(o_out)))
+    say("  rel err %.3e (worst row %.3e)" % (err, worst))
+    assert err <= TOL
+    assert np.abs(g_lse - o_lse).max() < 1e-2

@@ -165,8 +165,7 @@ def test_mla_page_permutation_gives_identical_bits():
 
 
 @pytest.mark.parametrize("qtype", ["fp8_e4m3", "fp8_ds_mla"])
-def test_mla_full_size_sampled_rows(qtype):
+def test_mla_full_size_all_rows(qtype):
     """The 163840-token slab with 128 heads, in the launch configuration the
-    benchmark times; the oracle computes a sample of the heads."""
-    wl = W.mla()
-    check(wl, qtype, rows=np.array([0, 1, 37, 64, 100, 127], np.int32))
+    benchmark times; every head against the oracle."""
+    check(W.mla(), qtype)

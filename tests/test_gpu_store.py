@@ -24,7 +24,8 @@ CASTS = ["fp8_e4m3_cast", "fp8_e5m2_cast"]
 
 def tricky_rows(rng, n, H, D):
     """bf16 rows mixing magnitudes from fp16-subnormal scales to saturating
-    ones, all-zero and constant blocks, +-1e4 outliers and exact ties."""
+    ones, all-zero and constant blocks, +-1e4 outliers, +-inf elements and
+    exact ties."""
     x = rng.standard_normal((n, H, D), dtype=np.float32)
     mag = np.exp2(rng.uniform(-30, 28, (n, H, 1))).astype(np.float32)
     x *= np.where(rng.random((n, H, 1)) < 0.5, 1.0, mag)
@@ -35,6 +36,10 @@ def tricky_rows(rng, n, H, D):
     blocks[const] = rng.standard_normal(int(const.sum()), dtype=np.float32)[:, None]
     out = rng.random(x.shape) < 0.002
     x[out] = np.where(rng.random(int(out.sum())) < 0.5, -1e4, 1e4)
+    # infinities saturate: the block's scale is held at 65504, the element
+    # stores +-M (a wrong sign here once came from inf - inf in the quotient)
+    inf = rng.random(x.shape) < 0.0005
+    x[inf] = np.where(rng.random(int(inf.sum())) < 0.5, -np.inf, np.inf)
     bits = W.to_bf16_bits(x)
     # exact ties: block max 448*s (resp. 127*s), others on code midpoints times s
     grid = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
@@ -89,6 +94,30 @@ def test_store_bitexact(qtype, H, D):
             assert np.array_equal(got_s, oks)
         else:
             assert ks is None
+
+
+def test_device_e4m3_encoder_over_every_fp32_in_range():
+    """The device's fp32 -> e4m3 encoder (clamp, then the gfx950 packed RNE
+    conversion; every stored e4m3 code goes through it, including the 656-byte
+    row's quotients by an fp32 scale, which take arbitrary fp32 values) on
+    every fp32 in [-448, 448], against the oracle's encoder.  The conversion
+    is what differs per architecture [PR103 "feat(kvcache): 8-bit KV cache
+    (q8_0 / fp8_e4m3) behind --kv-cache-dtype", review §"A bug on sm_89"]."""
+    k = kvq()
+    top = 0x43E00000  # 448.0f; patterns 0 .. top are the magnitudes in [0, 448]
+    chunk = 1 << 28
+    out = torch.empty(chunk, dtype=torch.uint8, device="cuda")
+    for sign in (0, 0x80000000):
+        for lo in range(0, top + 1, chunk):
+            n = min(chunk, top + 1 - lo)
+            n4 = (n + 3) // 4 * 4  # the last quad may run up to 3 patterns past 448
+            say("e4m3 sweep", hex(sign + lo), n)
+            k.debug_e4m3_encode_range(sign + lo, n4, out[:n4])
+            got = out[:n].cpu().numpy()
+            exp = oracle.e4m3_encode_bits(sign + lo, n)
+            bad = np.nonzero(got != exp)[0]
+            assert bad.size == 0, "bits %#010x: gpu %#04x oracle %#04x (%d mismatches)" % (
+                sign + lo + int(bad[0]), got[bad[0]], exp[bad[0]], bad.size)
 
 
 @pytest.mark.parametrize("qtype", QT8)

@@ -303,6 +303,31 @@ def test_block_max_encodes_to_format_max(qtype):
 
 
 @pytest.mark.parametrize("qtype,M", [("fp8_e4m3", 448), ("q8_0", 127)])
+def test_infinite_elements_saturate(qtype, M):
+    """A block holding +-inf: the quotient max/M is infinite, so the scale is
+    held at the largest fp16 (65504); the infinite element stores +-M and
+    the others their fp32 quotient by 65504, rounded (e4m3 through torch's
+    float8_e4m3fn cast, q8_0 half away from zero in numpy)."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((64, 32)) * np.exp2(rng.uniform(0, 40, (64, 1)))).astype(np.float32)
+    pos = rng.integers(0, 32, 64)
+    x[np.arange(64), pos] = np.where(np.arange(64) % 2 == 0, np.inf, -np.inf)
+    blocks = bf16_bits(x)
+    codes, s_bits = _quantize_blocks(qtype, blocks)
+    assert np.all(s_bits == 0x7BFF)
+    xv = bf16_to_f32(blocks)
+    v = np.clip(xv / np.float32(65504.0), -M, M).astype(np.float32)
+    if qtype == "fp8_e4m3":
+        exp = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    else:
+        exp = (np.sign(v) * np.floor(np.abs(v.astype(np.float64)) + 0.5)).astype(np.int8).view(np.uint8)
+    assert np.array_equal(codes, exp)
+    top = np.where(np.arange(64) % 2 == 0, 0x7E, 0xFE) if qtype == "fp8_e4m3" else \
+        np.where(np.arange(64) % 2 == 0, 127, -127).astype(np.int8).view(np.uint8)
+    assert np.array_equal(codes[np.arange(64), pos], top)
+
+
+@pytest.mark.parametrize("qtype,M", [("fp8_e4m3", 448), ("q8_0", 127)])
 def test_constant_and_zero_blocks(qtype, M):
     rng = np.random.default_rng(7)
     cs = rng.standard_normal(2000).astype(np.float32)
