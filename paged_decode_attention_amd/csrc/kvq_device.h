@@ -88,19 +88,21 @@ __device__ __forceinline__ void decode_dword_bf16x2(uint32_t w, uint32_t* o) {
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // ---- 8-bit float encoding ------------------------------------------------------
-// Four fp32 values -> four e4m3fn codes in one dword (byte i from v_i): the
-// value is clamped to +-448 and rounded to nearest even by the gfx950 packed
-// conversion.  Every e4m3 code the library stores comes from here (the
-// block-scaled quotients, the cast type and the 656-byte row), and the test
-// export kvq_debug_e4m3_encode_range runs it over every fp32 in [-448, 448].
-__device__ __forceinline__ uint32_t e4m3x4_clamped(float v0, float v1, float v2, float v3) {
-  constexpr float M = 448.0f;
-  v0 = fminf(fmaxf(v0, -M), M);
-  v1 = fminf(fmaxf(v1, -M), M);
-  v2 = fminf(fmaxf(v2, -M), M);
-  v3 = fminf(fmaxf(v3, -M), M);
+// Four fp32 values in [-448, 448] -> four e4m3fn codes in one dword (byte i
+// from v_i), rounded to nearest even by the gfx950 packed conversion.  Every
+// e4m3 code the library stores comes from here (the block-scaled quotients,
+// the cast type and the 656-byte row, each clamped by its caller), and the
+// test export kvq_debug_e4m3_encode_range runs it over every fp32 in
+// [-448, 448].
+__device__ __forceinline__ uint32_t e4m3x4_rne(float v0, float v1, float v2, float v3) {
   const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, lo, true);
+}
+// The same after clamping each value to +-448.
+__device__ __forceinline__ uint32_t e4m3x4_clamped(float v0, float v1, float v2, float v3) {
+  constexpr float M = 448.0f;
+  return e4m3x4_rne(fminf(fmaxf(v0, -M), M), fminf(fmaxf(v1, -M), M), fminf(fmaxf(v2, -M), M),
+                    fminf(fmaxf(v3, -M), M));
 }
 
 // Two fp32 -> one bf16 pair (round to nearest even), .x in the low half.

@@ -598,13 +598,21 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
 
     if (nc > 1 && p.fused) {
       // ---- the last item of this (sequence, kv head, head group) merges ---------
-      // The workgroup's partial stores happen before thread 0's release
-      // increment (barrier); the workgroup that sees the final count
-      // acquires them and hands them on with the next barrier.
+      // Ordering (gfx950): the partials went out as agent-scope stores,
+      // which write through the L2 to the cross-XCD coherence point; the
+      // vmcnt(0) wait returns once each is acknowledged there, before the
+      // barrier and thread 0's agent-scope increment.  The workgroup that
+      // reads the final count issues its agent-scope loads (which bypass the
+      // non-coherent caches) only after the increment has returned, so they
+      // see every chunk's partials.  An acquire-release increment gives the
+      // same order through an L2 write-back and invalidate and cost about
+      // 1 us per call.
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0) {
         const int old = __hip_atomic_fetch_add(&p.count[(int64_t)b * units + u], 1,
-                                               __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == nc - 1);
       }
       __syncthreads();

@@ -67,18 +67,17 @@ __device__ __forceinline__ void quantize8(const float* x, float s, uint32_t* out
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float q0 = x[i] * r;
-    // x / s (see the header); the sign is x's (s > 0), also for a -0 element,
-    // which the correction step alone would turn into +0.  Past +-M the
-    // clamp decides and the estimate is kept: for an infinite element the
-    // residual would be inf - inf (NaN), which the clamp turns into -M.
-    const float qc = fmaf(fmaf(-s, q0, x[i]), r, q0);
-    const float q = copysignf(fabsf(q0) > M ? q0 : qc, x[i]);
-    v[i] = fminf(fmaxf(q, -M), M);
+    // x / s (see the header), clamped in magnitude with x's sign (s > 0):
+    // a -0 element stays -0 (the correction step alone would give +0), and
+    // an infinite element, whose residual is inf - inf (NaN), stores +-M
+    // (the minimum of NaN and M is M).
+    const float q = fmaf(fmaf(-s, q0, x[i]), r, q0);
+    v[i] = copysignf(fminf(fabsf(q), M), x[i]);
   }
   if constexpr (QT == QT_FP8) {
 #pragma unroll
     for (int w = 0; w < 2; ++w)
-      out2[w] = e4m3x4_clamped(v[4 * w + 0], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3]);
+      out2[w] = e4m3x4_rne(v[4 * w + 0], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3]);
   } else {
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
@@ -168,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs a, StoreGrid 
             const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(v[0], v[1], 0, false);
             codes[d] = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(v[2], v[3], lo, true);
           } else {
-            codes[d] = e4m3x4_clamped(v[0], v[1], v[2], v[3]);
+            codes[d] = e4m3x4_rne(v[0], v[1], v[2], v[3]);
           }
         }
       } else {
@@ -365,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void debug_e4m3_kernel(uint32_t first, ui
   if (i >= quads) return;
   const uint32_t b = first + 4 * i;
   out[i] = e4m3x4_clamped(__uint_as_float(b), __uint_as_float(b + 1), __uint_as_float(b + 2),
-                          __uint_as_float(b + 3));
+                          __uint_as_float(b + 3));  // the clamp is the identity on [-448, 448]
 }
 
 hipError_t launch_debug_e4m3(uint32_t first, int64_t count, uint8_t* out, hipStream_t s) {
