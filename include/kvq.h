@@ -20,7 +20,8 @@
  * Conventions for every call:
  *   - Pointers marked "device" point to GPU memory the caller allocated and
  *     owns; the library never allocates, frees or synchronizes, and keeps no
- *     state between calls other than the thread-local error message.
+ *     state between calls other than the thread-local error message (and
+ *     kvq_paged_decode_noalloc's fixed device array).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and runs asynchronously; results are valid once the stream reaches it.
  *   - Arguments are validated on the host before anything is launched; a call
@@ -223,6 +224,31 @@ int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
                      int head_dim_qk, int head_dim_v, int page_size, int max_pages,
                      int64_t num_pages, float sm_scale, void* out_bf16, float* lse,
                      void* workspace, size_t workspace_bytes, kvq_stream_t stream);
+
+/* kvq_paged_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The arguments and the result are kvq_paged_decode's, without
+ * the workspace: the split-K partials and arrival counters live in the
+ * library's own array of 64 MiB per device (a static device array, held by
+ * every GPU the library runs on until the process ends; its address is taken
+ * once per device on the first call there).  Each call first clears the
+ * arrival counters its plan uses (a small fill kernel on `stream`), then
+ * decodes.  Calls on one GPU share the array and leave their partials in
+ * it, so calls that overlap on one GPU (other streams, other threads) race;
+ * calls on different GPUs do not.  Shapes whose plan needs more than the
+ * array holds (kvq_paged_decode_workspace_bytes() > 64 MiB: for the 576/512
+ * slab with 128 heads and 10240 pages, a batch above 3; for 16 q / 8 kv heads
+ * of head_dim 128 over 8192 pages, a batch above about 250) are refused with
+ * KVQ_ERR_WORKSPACE before anything is enqueued.  Nothing is allocated.
+ * Errors: as kvq_paged_decode. */
+int kvq_paged_decode_noalloc(kvq_dtype dtype, const void* q, const void* k_pool,
+                             const uint16_t* k_scales, const void* v_pool,
+                             const uint16_t* v_scales, const int32_t* page_table,
+                             int64_t pt_stride, const int32_t* seq_lens,
+                             const int32_t* seq_lens_host, int batch, int n_q_heads,
+                             int n_kv_heads, int head_dim_qk, int head_dim_v, int page_size,
+                             int max_pages, int64_t num_pages, float sm_scale, void* out_bf16,
+                             float* lse, kvq_stream_t stream);
 
 /* Workspace bytes kvq_sparse_mla_decode needs: the gathered rows of every
  * list (codes and scales), their page table and lengths, and the split-K

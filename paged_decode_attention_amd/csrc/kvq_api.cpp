@@ -120,14 +120,16 @@ int check_rows(int dtype, int64_t n_tokens, int n_heads, int head_dim, int page_
   return KVQ_OK;
 }
 
-// The validation and launches of kvq_paged_decode.
+// The validation and launches of kvq_paged_decode; with use_scratch the
+// workspace is the library's own array (kvq_paged_decode_noalloc).
 int decode_call(const char* fn, kvq_dtype dtype, const void* q, const void* k_pool,
                      const uint16_t* k_scales, const void* v_pool, const uint16_t* v_scales,
                      const int32_t* page_table, int64_t pt_stride, const int32_t* seq_lens,
                      const int32_t* seq_lens_host, int batch, int n_q_heads, int n_kv_heads,
                      int head_dim_qk, int head_dim_v, int page_size, int max_pages,
                      int64_t num_pages, float sm_scale, void* out_bf16, float* lse,
-                     void* workspace, size_t workspace_bytes, kvq_stream_t stream) {
+                     void* workspace, size_t workspace_bytes, kvq_stream_t stream,
+                bool use_scratch) {
   if (!known_dtype(dtype)) return fail(KVQ_ERR_ARG, "%s: unknown dtype %d", fn, dtype);
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || max_pages < 1 || head_dim_qk < 1 ||
       head_dim_v < 1 || page_size < 1)
@@ -168,6 +170,15 @@ int decode_call(const char* fn, kvq_dtype dtype, const void* q, const void* k_po
                 "%s: k_pool == v_pool is only supported for the 576/512 slab", fn);
   if (!shared && plan.kind == kvq::DK_MLA)
     return fail(KVQ_ERR_UNSUPPORTED, "%s: the 576/512 shape needs the shared slab", fn);
+  if (use_scratch) {  // the library's own array (kvq_paged_decode_noalloc)
+    if (plan.bytes > kvq::scratch_bytes())
+      return fail(KVQ_ERR_WORKSPACE,
+                  "%s: these shapes need %zu bytes of scratch; the library's array holds %zu", fn,
+                  plan.bytes, kvq::scratch_bytes());
+    hipError_t e = kvq::scratch_pointer(&workspace);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    workspace_bytes = kvq::scratch_bytes();
+  }
   if (!workspace || workspace_bytes < plan.bytes)
     return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn,
                 plan.bytes, workspace ? workspace_bytes : (size_t)0);
@@ -196,6 +207,13 @@ int decode_call(const char* fn, kvq_dtype dtype, const void* q, const void* k_po
   a.workspace = workspace;
   if (seq_lens_host) a.items_hint = host_items(plan, a, seq_lens_host);
   const int cus = num_cus_current();
+  if (use_scratch) {
+    // the array keeps the previous call's contents, whatever its shapes:
+    // clear this plan's arrival counters (a fill kernel, no memset node)
+    hipError_t z = kvq::launch_zero_words(static_cast<char*>(workspace) + plan.off_count,
+                                          (plan.off_ml - plan.off_count) / 4, stream);
+    if (z != hipSuccess) return hip_fail(z, fn);
+  }
   hipError_t e = (plan.kind == kvq::DK_MLA) ? kvq::launch_mla_decode(a, plan, cus, stream)
                  : plan.mfma                 ? kvq::launch_gqa_mfma_decode(a, plan, cus, stream)
                                              : kvq::launch_gqa_decode(a, plan, cus, stream);
@@ -504,7 +522,21 @@ int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
   return decode_call("kvq_paged_decode", dtype, q, k_pool, k_scales, v_pool, v_scales, page_table,
                      pt_stride, seq_lens, seq_lens_host, batch, n_q_heads, n_kv_heads,
                      head_dim_qk, head_dim_v, page_size, max_pages, num_pages, sm_scale, out_bf16,
-                     lse, workspace, workspace_bytes, stream);
+                     lse, workspace, workspace_bytes, stream, false);
+}
+
+int kvq_paged_decode_noalloc(kvq_dtype dtype, const void* q, const void* k_pool,
+                             const uint16_t* k_scales, const void* v_pool,
+                             const uint16_t* v_scales, const int32_t* page_table,
+                             int64_t pt_stride, const int32_t* seq_lens,
+                             const int32_t* seq_lens_host, int batch, int n_q_heads,
+                             int n_kv_heads, int head_dim_qk, int head_dim_v, int page_size,
+                             int max_pages, int64_t num_pages, float sm_scale, void* out_bf16,
+                             float* lse, kvq_stream_t stream) {
+  return decode_call("kvq_paged_decode_noalloc", dtype, q, k_pool, k_scales, v_pool, v_scales,
+                     page_table, pt_stride, seq_lens, seq_lens_host, batch, n_q_heads, n_kv_heads,
+                     head_dim_qk, head_dim_v, page_size, max_pages, num_pages, sm_scale, out_bf16,
+                     lse, nullptr, 0, stream, true);
 }
 
 size_t kvq_extend_attention_workspace_bytes(kvq_dtype dtype, int batch, int n_q_heads,

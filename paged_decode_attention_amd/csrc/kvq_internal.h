@@ -157,6 +157,15 @@ hipError_t launch_gqa_mfma_decode(const DecodeArgs& a, const DecodePlan& p, int 
 hipError_t launch_mla_decode(const DecodeArgs& a, const DecodePlan& p, int num_cus,
                              hipStream_t s);
 
+// ---- the library's own scratch array (kvq_noalloc.hip) ------------------------
+// Size of the per-device array that kvq_paged_decode_noalloc uses as its
+// workspace, its device address on the current device (taken once per device
+// with hipGetSymbolAddress), and a fill kernel that zeroes `words` 32-bit
+// words at p.
+size_t scratch_bytes();
+hipError_t scratch_pointer(void** p);
+hipError_t launch_zero_words(void* p, size_t words, hipStream_t s);
+
 // ---- sparse top-k decode over the MLA slab -------------------------------------
 // The listed rows of every sequence are gathered into a compact slab in the
 // workspace (kk rows per sequence: k rounded up to a page), which the slab

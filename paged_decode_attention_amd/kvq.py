@@ -67,6 +67,9 @@ def _load() -> ctypes.CDLL:
     lib.kvq_extend_attention.argtypes = [I, P, P, I, P, P, P, P, P, I64, P, I, I, I, I, I, I, I64,
                                          c.c_float, P, P, P, c.c_size_t, P]
     lib.kvq_extend_attention.restype = I
+    lib.kvq_paged_decode_noalloc.argtypes = [I, P, P, P, P, P, P, I64, P, P, I, I, I, I, I, I, I,
+                                             I64, c.c_float, P, P, P]
+    lib.kvq_paged_decode_noalloc.restype = I
     lib.kvq_debug_e4m3_encode_range.argtypes = [c.c_uint32, I64, P, P]
     lib.kvq_debug_e4m3_encode_range.restype = I
     lib.kvq_debug_decode_plan.argtypes = [I, I, I, I, I, I, I, I, c.POINTER(I64), I]
@@ -80,8 +83,9 @@ LIB = _load()
 
 # every symbol the public header declares
 EXPORTS = ("kvq_pool_bytes", "kvq_store", "kvq_dequant", "kvq_paged_decode_workspace_bytes",
-           "kvq_paged_decode", "kvq_sparse_mla_decode_workspace_bytes", "kvq_sparse_mla_decode",
-           "kvq_extend_attention_workspace_bytes", "kvq_extend_attention", "kvq_last_error")
+           "kvq_paged_decode", "kvq_paged_decode_noalloc", "kvq_sparse_mla_decode_workspace_bytes",
+           "kvq_sparse_mla_decode", "kvq_extend_attention_workspace_bytes", "kvq_extend_attention",
+           "kvq_last_error")
 # the test exports (kvq_debug.h)
 DEBUG_EXPORTS = ("kvq_debug_e4m3_encode_range", "kvq_debug_decode_plan")
 PLAN_FIELDS = ("kind", "gt", "tn", "n_hg", "step", "min_pages", "cap_pages", "target",
@@ -270,6 +274,33 @@ def paged_decode(dtype, q, k_pool, k_scales, v_pool, v_scales, page_table, seq_l
                               head_dim_v, page_size, max_pages, num_pages, float(sm_scale),
                               _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                               _stream(q.device, stream))
+    _check(rc)
+    return out, lse
+
+
+def paged_decode_noalloc(dtype, q, k_pool, k_scales, v_pool, v_scales, page_table, seq_lens,
+                         sm_scale: float, head_dim_v: int | None = None, out=None, lse=None,
+                         stream=None, seq_lens_host=None):
+    """paged_decode with the library's own scratch array as the workspace
+    (kvq_paged_decode_noalloc); out and lse may be passed in so that the
+    call allocates nothing."""
+    batch, n_q_heads, head_dim_qk = q.shape
+    num_pages, n_kv_heads, page_size, _ = k_pool.shape
+    if head_dim_v is None:
+        head_dim_v = v_pool.shape[3]
+    max_pages = page_table.shape[1]
+    pt_stride = page_table.stride(0) if batch > 1 else max_pages
+    if out is None:
+        out = torch.empty((batch, n_q_heads, head_dim_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((batch, n_q_heads), dtype=torch.float32, device=q.device)
+    _lens, lens_ptr = _host_lens(seq_lens_host)
+    rc = LIB.kvq_paged_decode_noalloc(_dt(dtype), _ptr(q), _ptr(k_pool), _ptr(k_scales),
+                                      _ptr(v_pool), _ptr(v_scales), _ptr(page_table), pt_stride,
+                                      _ptr(seq_lens), lens_ptr, batch, n_q_heads, n_kv_heads,
+                                      head_dim_qk, head_dim_v, page_size, max_pages, num_pages,
+                                      float(sm_scale), _ptr(out), _ptr(lse),
+                                      _stream(q.device, stream))
     _check(rc)
     return out, lse
 
