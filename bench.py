@@ -494,6 +494,8 @@ def main() -> int:
                              "extend", "mla_extend"],
                     help="qwen3 (default) is the decode step this benchmark reports; the others "
                          "time kvq_paged_decode alone on that workload and print their own line")
+    ap.add_argument("--ctx", type=int, default=0,
+                    help="--workload mla: tokens of the sequence (0: the workload's 163840)")
     ap.add_argument("--replicas", type=int, default=0,
                     help="pool copies swept by the decode-only workloads (0: enough for 1 GB)")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
@@ -533,6 +535,8 @@ def main() -> int:
         return decode_only(args, W.extend(new=args.extend_new), qtype, dev)
     if args.workload == "mla_extend":
         return decode_only(args, W.mla_extend(new=args.extend_new), qtype, dev)
+    if args.workload == "mla" and args.ctx:
+        return decode_only(args, W.mla(ctx=args.ctx), qtype, dev)
     if args.workload != "qwen3":
         return decode_only(args, W.BY_NAME[args.workload](), qtype, dev)
     wl = W.qwen3(replicas=args.layers)
