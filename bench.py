@@ -3,20 +3,24 @@
 
 One step = one decode token for every sequence through a 28-layer attention
 stack of the Qwen3-1.7B shape (16 query / 8 KV heads, head_dim 128): for each
-layer, the quantize-on-store of the new token's K and V (one fused kvq_store)
-followed by paged decode attention over that layer's pool (kvq_paged_decode),
-batch 8 x 16384-token contexts, page size 16, random-permutation page tables,
-fp8_e4m3 block-32 codes with fp16 scales.  The 28 layers are 28 distinct
+layer, the quantize-on-store of the new token's K and V and paged decode
+attention over that layer's pool, as one kvq_paged_decode_append call (one
+kernel launch: the work item that attends the new position quantizes and
+writes it), batch 8 x 16384-token contexts, page size 16, random-permutation
+page tables, fp8_e4m3 block-32 codes with fp16 scales.  The same step as two
+calls per layer (kvq_store, then kvq_paged_decode) is timed beside it.  The 28 layers are 28 distinct
 copies of one layer's pool (7.99 GB in all), so every step streams the whole
 KV cache from HBM rather than from the 256 MB Infinity Cache.
 
 Prints one JSON line: `value` is the step's algorithmic bytes (codes + scales
 of every token read, Q, O, page-table entries, and the store's bf16 reads and
-code/scale writes) per second, in GB/s; `roofline` is the decode call (one
-kernel launch: split-K decode with its in-kernel merge) against the 8 TB/s HBM
-peak: its average launch duration from HIP events around replays of a graph
-holding the 28 layers' decode launches back to back (gaps between launches
-included), on the stream the kernels run on; `store_gbps` is
+code/scale writes) per second, in GB/s; `roofline` is the append-decode
+call (one kernel launch: split-K decode with its in-kernel merge and the new
+token's store) against the 8 TB/s HBM peak: its average launch duration from
+HIP events around replays of the step's graph, which holds the 28 layers'
+launches back to back (gaps between launches included), on the stream the
+kernels run on; `decode_call_us` is kvq_paged_decode alone, timed the same
+way; `store_gbps` is
 the quantize-on-store at the mixed workload's size (8192 new tokens x 8 kv
 heads x 128, K and V in one call), timed from graph replays as the decode;
 `cpu_baseline` is the CPU oracle on a
@@ -117,7 +121,7 @@ def write_traffic(src_dir):
     for f in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, f), "rb").read())
     rec = {
-        "kernel": "gqa_decode_kernel<fp8_e4m3, 128, 2>",
+        "kernel": "gqa_decode_kernel<fp8_e4m3, 128, 2, append> (kvq_paged_decode_append)",
         "workload": "qwen3_b8_ctx16384_h16x8_d128 (one layer's pool, batch 8 x 16384 tokens)",
         "source_hash": h.hexdigest()[:16],
         "fetch_size_kib": round(dec_f, 1),
@@ -577,7 +581,7 @@ def main() -> int:
     # every call goes to one stream of the default priority, which a HIP graph
     # can capture
     strm = torch.cuda.Stream(device=dev)
-    stores, decodes = [], []
+    stores, decodes, appends = [], [], []
     for layer in range(L):
         kp, ks, vp, vs = pools[layer]
         stores.append(kvq.PreparedStore(qtype, new_kv[layer][0], new_kv[layer][1], new_slots,
@@ -586,6 +590,10 @@ def main() -> int:
                                stream=strm)
         ws = d.workspace
         decodes.append(d)
+        # the layer's step: store the new token and decode, one launch
+        appends.append(kvq.PreparedDecode(qtype, q, kp, ks, vp, vs, pt, sl, wl.sm_scale,
+                                          workspace=ws, stream=strm, new_k=new_kv[layer][0],
+                                          new_v=new_kv[layer][1]))
 
     dec_bytes = wl.algorithmic_bytes(qtype)
     st_bytes = store_bytes(B, H, D, qtype)
@@ -595,38 +603,37 @@ def main() -> int:
         for layer in range(L):
             if ev is not None:
                 ev[s][layer][0].record(strm)
-            stores[layer]()
+            appends[layer]()
             if ev is not None:
                 ev[s][layer][1].record(strm)
+
+    def step_two_calls():
+        for layer in range(L):
+            stores[layer]()
             decodes[layer]()
-            if ev is not None:
-                ev[s][layer][2].record(strm)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     if args.only == "decode":
         for s_ in range(args.steps):
-            for layer in range(L):
-                decodes[layer]()
+            step()
         torch.cuda.synchronize()
-        log("ran %d decode calls" % (args.steps * L))
+        log("ran %d append-decode calls" % (args.steps * L))
         return 0
 
     K = args.steps
     # (1) each call timed on its own with HIP events on the stream it runs on
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L)]
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)]
           for _ in range(K)]
     torch.cuda.synchronize()
     for s in range(K):
         step(ev, s)
     torch.cuda.synchronize()
-    dec_ms = [ev[s][l][1].elapsed_time(ev[s][l][2]) for s in range(K) for l in range(L)]
-    st_ms = [ev[s][l][0].elapsed_time(ev[s][l][1]) for s in range(K) for l in range(L)]
-    dec_avg = float(np.mean(dec_ms))
-    st_avg = float(np.mean(st_ms))
+    app_avg = float(np.mean([ev[s][l][0].elapsed_time(ev[s][l][1]) for s in range(K)
+                             for l in range(L)]))
     # (2) the step as a serving loop runs it: captured once into a HIP graph
-    # (store and decode of every layer, nothing else) and replayed K times
+    # (every layer's append-decode, nothing else) and replayed K times
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=strm):
         step()
@@ -635,10 +642,18 @@ def main() -> int:
     # exactly K steps, in 5 groups (one event pair each): the median group mean
     ms_step, step_means = timed_replays(graph, K)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    # (2b) the decode launches alone: the L layers' decodes captured back to
-    # back into one graph, replayed K times between two events on their
-    # stream.  The kernel's average launch duration for the roofline (gaps
-    # between launches included; no event between two launches).
+    # (2a) the same step as two calls per layer (kvq_store, then kvq_paged_decode)
+    graph2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph2, stream=strm):
+        step_two_calls()
+    for _ in range(args.warmup):
+        graph2.replay()
+    ms_step2, _ = timed_replays(graph2, K)
+    # (2b) kvq_paged_decode alone: the L layers' decodes captured back to back
+    # into one graph, replayed between two events on their stream (gaps
+    # between launches included; no event between two launches).  The
+    # roofline's kernel is the step's own launch (the step graph above holds
+    # exactly L of them back to back); this is the decode without the store.
     dgraph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(dgraph, stream=strm):
         for layer in range(L):
@@ -671,10 +686,11 @@ def main() -> int:
     sg_ms, _ = timed_replays(sgraph, 5 * K)
     big_us = sg_ms * 1e3 / 8
     big_bytes = store_bytes(int(mslots.numel()), H, D, qtype)
-    achieved = dec_bytes / (dec_graph * 1e-3) / 1e9
-    log("step %.3f ms (graph), decode launch %.2f us (decode-only graph; %.2f us with an event "
-        "pair around each eager call), store call %.2f us" % (ms_step, dec_graph * 1e3,
-                                                             dec_avg * 1e3, st_avg * 1e3))
+    app_graph = ms_step / L  # ms per append-decode launch in the step's graph
+    achieved = (dec_bytes + st_bytes) / (app_graph * 1e-3) / 1e9
+    log("step %.3f ms (graph; %.3f ms as store + decode calls), append-decode launch %.2f us "
+        "(%.2f us with an event pair around each eager call), decode alone %.2f us"
+        % (ms_step, ms_step2, app_graph * 1e3, app_avg * 1e3, dec_graph * 1e3))
 
     res = {
         "metric": METRIC,
@@ -691,7 +707,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": "decode step (replayed as one HIP graph), %d layers x (store 1 new token "
-                        "+ paged decode), batch %d "
+                        "+ paged decode, one kvq_paged_decode_append launch), batch %d "
                         "x %d-token contexts, %d q / %d kv heads, head_dim %d, page 16, "
                         "random-permutation page tables (%s)" % (L, B, int(wl.seq_lens[0]),
                                                                  wl.n_q_heads, H, D, wl.name),
@@ -705,29 +721,31 @@ def main() -> int:
         "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "timing": "median of 5 group means (HIP events on the stream around graph replays): "
-                  "the step over exactly %d steps; the decode launch and the store over 5 x %d "
-                  "replays" % (K, K),
+                  "the step over exactly %d steps (the two-call step likewise); the decode "
+                  "alone and the store over 5 x %d replays" % (K, K),
         "step_ms_group_means": step_means,
+        "step_ms_store_then_decode": round(ms_step2, 4),
+        "append_call_us": round(app_graph * 1e3, 3),
+        "append_call_us_eager_events": round(app_avg * 1e3, 3),
         "decode_call_us": round(dec_graph * 1e3, 3),
-        "decode_call_us_eager_events": round(dec_avg * 1e3, 3),
-        "store_call_us": round(st_avg * 1e3, 3),
         "store_gbps": round(big_bytes / (big_us * 1e-6) / 1e9, 2),
         "store": {"workload": "8192 new tokens x 8 kv heads x 128, K and V in one call, into a "
                               "2^20-slot pool (mixed_b64 new tokens: zero and constant blocks, "
                               "+-1e4 outliers)",
                   "call_us": round(big_us, 3), "bytes": big_bytes,
                   "gbps": round(big_bytes / (big_us * 1e-6) / 1e9, 2),
-                  "pct_of_hbm_peak": round(100 * big_bytes / (big_us * 1e-6) / 1e9 / PEAK_GBPS, 2),
-                  "per_step_store_of_8_tokens_us": round(st_avg * 1e3, 3)},
+                  "pct_of_hbm_peak": round(100 * big_bytes / (big_us * 1e-6) / 1e9 / PEAK_GBPS, 2)},
         "roofline": {
             "bound": "hbm",
-            "kernel": "gqa_decode_kernel<%s, 128, 2> (one launch per kvq_paged_decode)" % qtype,
+            "kernel": "gqa_decode_kernel<%s, 128, 2, append> (one launch per "
+                      "kvq_paged_decode_append: the layer's decode and its new token's store)"
+                      % qtype,
             "achieved": round(achieved, 2),
             "peak": PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBPS, 4),
             "traffic": recorded_traffic() if qtype == "fp8_e4m3" and L == 28 else None,
-            "algorithmic_bytes_per_launch": dec_bytes,
+            "algorithmic_bytes_per_launch": dec_bytes + st_bytes,
         },
     }
     if not args.no_cpu_baseline:

@@ -225,6 +225,50 @@ int kvq_paged_decode(kvq_dtype dtype, const void* q, const void* k_pool,
                      int64_t num_pages, float sm_scale, void* out_bf16, float* lse,
                      void* workspace, size_t workspace_bytes, kvq_stream_t stream);
 
+/* Decode with append: each sequence's new token is stored, then every
+ * sequence is decoded, in one call -- the per-layer work of a decode step
+ * [PR126 "Add fp8 KV-cache quantization (--kv-dtype)" §How it works (the
+ * incoming bf16 k/v rows are converted to the pool type as they are written
+ * to the cache; attention dequantizes on read); PR103 "feat(kvcache): 8-bit
+ * KV cache (q8_0 / fp8_e4m3) behind --kv-cache-dtype" §What (the store
+ * kernel quantizes, the attention kernels read the quantized pool)].
+ *
+ * The result, the pools and the lse are exactly those of
+ *     kvq_store(dtype, new_k, new_v, new_token_stride, slot, batch,
+ *               n_kv_heads, head_dim_qk, page_size, num_pages, k_pool,
+ *               k_scales, v_pool, v_scales, stream);
+ *     kvq_paged_decode(... the same pools, page table, lengths ...);
+ * with slot[b] = page_table[b][(L - 1) / page_size] * page_size + (L - 1) %
+ * page_size for L = seq_lens[b] (the new token is the last position of its
+ * sequence, already counted in seq_lens), and slot[b] = -1 -- nothing stored
+ * -- when L < 1, L > max_pages * page_size, or that page id lies outside
+ * [0, num_pages).
+ *
+ *   new_k, new_v : device bf16 [batch][n_kv_heads][head_dim_qk] with
+ *                  new_token_stride elements between sequences (>=
+ *                  n_kv_heads * head_dim_qk, a multiple of 8), 16-byte
+ *                  aligned.  For the shared MLA slab (k_pool == v_pool) new_v
+ *                  is NULL and new_k holds the 576-wide rows; otherwise new_v
+ *                  is required.
+ *   k_pool, k_scales, v_pool, v_scales : as kvq_paged_decode, written.
+ *   Every other argument: as kvq_paged_decode.
+ * With separate K/V and fewer than 8 query heads per kv head the new rows are
+ * quantized and stored inside the decode launch (by the work item that
+ * attends that position, with the store kernel's arithmetic); the other
+ * shapes enqueue the store kernel, then the decode.  Two sequences whose new
+ * tokens share a slot race, as they would in kvq_store.
+ * Errors: as kvq_paged_decode, and KVQ_ERR_ARG for a null new_k, a new_v
+ * that does not match the pool sharing, or a bad stride or alignment. */
+int kvq_paged_decode_append(kvq_dtype dtype, const void* q, const void* new_k,
+                            const void* new_v, int64_t new_token_stride, void* k_pool,
+                            uint16_t* k_scales, void* v_pool, uint16_t* v_scales,
+                            const int32_t* page_table, int64_t pt_stride, const int32_t* seq_lens,
+                            const int32_t* seq_lens_host, int batch, int n_q_heads,
+                            int n_kv_heads, int head_dim_qk, int head_dim_v, int page_size,
+                            int max_pages, int64_t num_pages, float sm_scale, void* out_bf16,
+                            float* lse, void* workspace, size_t workspace_bytes,
+                            kvq_stream_t stream);
+
 /* kvq_paged_decode for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  The arguments and the result are kvq_paged_decode's, without

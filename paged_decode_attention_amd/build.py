@@ -45,10 +45,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libkvq.so)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src),
-           "-o", obj]
+# Compilation units: (source, object name, defines).  The VALU decode kernels
+# are compiled once per storage type (0 bf16, 1 e4m3, 2 q8_0, 3 e4m3 cast,
+# 4 e5m2 cast), so that their objects build in parallel.
+UNITS = [(src, os.path.splitext(src)[0], []) for src in SOURCES if src != "kvq_decode.hip"] + [
+    ("kvq_decode.hip", "kvq_decode_qt%d" % qt, ["-DKVQ_DECODE_QT=%d" % qt]) for qt in range(5)]
+
+
+def _compile(unit) -> str:
+    src, name, defines = unit
+    obj = os.path.join(BUILD_DIR, name + ".o")
+    cmd = [hipcc(), *FLAGS, *EXTRA_FLAGS.get(src, []), *defines, "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
@@ -57,9 +65,12 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, (os.cpu_count() or 1)))
+    jobs = min(len(UNITS), max(1, (os.cpu_count() or 1)))
+    # the longest units first
+    order = sorted(UNITS, key=lambda u: u[0] not in ("kvq_decode.hip", "kvq_gqa_mfma.hip",
+                                                     "kvq_mla.hip"))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, order))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -120,8 +120,16 @@ int check_rows(int dtype, int64_t n_tokens, int n_heads, int head_dim, int page_
   return KVQ_OK;
 }
 
+// The new tokens of a decode with append (kvq_paged_decode_append).
+struct AppendIn {
+  const void* new_k;
+  const void* new_v;
+  int64_t stride;  // elements between sequences
+};
+
 // The validation and launches of kvq_paged_decode; with use_scratch the
-// workspace is the library's own array (kvq_paged_decode_noalloc).
+// workspace is the library's own array (kvq_paged_decode_noalloc), with app
+// the call first appends each sequence's new token (kvq_paged_decode_append).
 int decode_call(const char* fn, kvq_dtype dtype, const void* q, const void* k_pool,
                      const uint16_t* k_scales, const void* v_pool, const uint16_t* v_scales,
                      const int32_t* page_table, int64_t pt_stride, const int32_t* seq_lens,
@@ -129,7 +137,7 @@ int decode_call(const char* fn, kvq_dtype dtype, const void* q, const void* k_po
                      int head_dim_qk, int head_dim_v, int page_size, int max_pages,
                      int64_t num_pages, float sm_scale, void* out_bf16, float* lse,
                      void* workspace, size_t workspace_bytes, kvq_stream_t stream,
-                bool use_scratch) {
+                bool use_scratch, const AppendIn* app = nullptr) {
   if (!known_dtype(dtype)) return fail(KVQ_ERR_ARG, "%s: unknown dtype %d", fn, dtype);
   if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || max_pages < 1 || head_dim_qk < 1 ||
       head_dim_v < 1 || page_size < 1)
@@ -179,6 +187,19 @@ int decode_call(const char* fn, kvq_dtype dtype, const void* q, const void* k_po
     if (e != hipSuccess) return hip_fail(e, fn);
     workspace_bytes = kvq::scratch_bytes();
   }
+  if (app) {
+    if (!app->new_k) return fail(KVQ_ERR_ARG, "%s: null new_k", fn);
+    if (shared != (app->new_v == nullptr))
+      return fail(KVQ_ERR_ARG,
+                  "%s: new_v must be null exactly when K and V share one slab (k_pool == v_pool)",
+                  fn);
+    if (app->stride < (int64_t)n_kv_heads * head_dim_qk || app->stride % 8 != 0)
+      return fail(KVQ_ERR_ARG,
+                  "%s: new_token_stride %lld must be >= n_kv_heads*head_dim_qk and a multiple of 8",
+                  fn, (long long)app->stride);
+    if (!aligned(app->new_k, 16) || (app->new_v && !aligned(app->new_v, 16)))
+      return fail(KVQ_ERR_ARG, "%s: new_k/new_v must be 16-byte aligned", fn);
+  }
   if (!workspace || workspace_bytes < plan.bytes)
     return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn,
                 plan.bytes, workspace ? workspace_bytes : (size_t)0);
@@ -213,6 +234,36 @@ int decode_call(const char* fn, kvq_dtype dtype, const void* q, const void* k_po
     hipError_t z = kvq::launch_zero_words(static_cast<char*>(workspace) + plan.off_count,
                                           (plan.off_ml - plan.off_count) / 4, stream);
     if (z != hipSuccess) return hip_fail(z, fn);
+  }
+  const bool valu = plan.kind != kvq::DK_MLA && !plan.mfma;
+  if (app && valu) {
+    // the VALU kernel stores and attends the new token in the same launch
+    a.new_kv[0] = static_cast<const uint16_t*>(app->new_k);
+    a.new_kv[1] = static_cast<const uint16_t*>(app->new_v);
+    a.new_stride = app->stride;
+  } else if (app) {
+    // the matrix-core and slab kernels: the append store, then the decode
+    kvq::StoreArgs st;
+    st.qtype = dtype;
+    st.src[0] = static_cast<const uint16_t*>(app->new_k);
+    st.src[1] = static_cast<const uint16_t*>(app->new_v);
+    st.stride = app->stride;
+    st.slots = nullptr;
+    st.n_tokens = batch;
+    st.n_heads = n_kv_heads;
+    st.head_dim = head_dim_qk;
+    st.page_size = page_size;
+    st.num_pages = num_pages;
+    st.pool[0] = static_cast<uint8_t*>(const_cast<void*>(k_pool));
+    st.pool[1] = app->new_v ? static_cast<uint8_t*>(const_cast<void*>(v_pool)) : nullptr;
+    st.scales[0] = const_cast<uint16_t*>(k_scales);
+    st.scales[1] = app->new_v ? const_cast<uint16_t*>(v_scales) : nullptr;
+    st.seq_lens = seq_lens;
+    st.page_table = page_table;
+    st.pt_stride = pt_stride;
+    st.max_pages = max_pages;
+    hipError_t se = kvq::launch_store(st, stream);
+    if (se != hipSuccess) return hip_fail(se, fn);
   }
   hipError_t e = (plan.kind == kvq::DK_MLA) ? kvq::launch_mla_decode(a, plan, cus, stream)
                  : plan.mfma                 ? kvq::launch_gqa_mfma_decode(a, plan, cus, stream)
@@ -537,6 +588,22 @@ int kvq_paged_decode_noalloc(kvq_dtype dtype, const void* q, const void* k_pool,
                      page_table, pt_stride, seq_lens, seq_lens_host, batch, n_q_heads, n_kv_heads,
                      head_dim_qk, head_dim_v, page_size, max_pages, num_pages, sm_scale, out_bf16,
                      lse, nullptr, 0, stream, true);
+}
+
+int kvq_paged_decode_append(kvq_dtype dtype, const void* q, const void* new_k,
+                            const void* new_v, int64_t new_token_stride, void* k_pool,
+                            uint16_t* k_scales, void* v_pool, uint16_t* v_scales,
+                            const int32_t* page_table, int64_t pt_stride, const int32_t* seq_lens,
+                            const int32_t* seq_lens_host, int batch, int n_q_heads,
+                            int n_kv_heads, int head_dim_qk, int head_dim_v, int page_size,
+                            int max_pages, int64_t num_pages, float sm_scale, void* out_bf16,
+                            float* lse, void* workspace, size_t workspace_bytes,
+                            kvq_stream_t stream) {
+  const AppendIn app{new_k, new_v, new_token_stride};
+  return decode_call("kvq_paged_decode_append", dtype, q, k_pool, k_scales, v_pool, v_scales,
+                     page_table, pt_stride, seq_lens, seq_lens_host, batch, n_q_heads, n_kv_heads,
+                     head_dim_qk, head_dim_v, page_size, max_pages, num_pages, sm_scale, out_bf16,
+                     lse, workspace, workspace_bytes, stream, false, &app);
 }
 
 size_t kvq_extend_attention_workspace_bytes(kvq_dtype dtype, int batch, int n_q_heads,

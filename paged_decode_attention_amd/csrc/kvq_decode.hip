@@ -108,9 +108,18 @@ __device__ __forceinline__ Raw<NDW> buf_load(__amdgpu_buffer_rsrc_t r, uint32_t 
   return o;
 }
 
+// The new token of a decode with append, as one wave meets it.
+template <int NDW>
+struct NewRow {
+  int step, row;  // the wave's step and row index holding the token (step -1: none)
+  bool on;        // this lane holds a piece of that row
+  Raw<NDW> k, v;  // the piece's codes (bf16 for a bf16 pool)
+  float ks, vs;   // its block scales (1 for the types without one)
+};
+
 // Wave-uniform description of one work item.
 struct Item {
-  int item, b, u, kvh, nc, t0, nt, np, h0, nsteps;
+  int item, b, u, kvh, hg, nc, t0, nt, np, h0, nsteps;
 };
 
 template <int PPS, int GT>
@@ -123,6 +132,7 @@ __device__ __forceinline__ Item describe(const GqaParams& p, int item_tokens, in
   it.u = rem - chunk * units;
   it.kvh = it.u / p.n_hg;
   const int hg = it.u - it.kvh * p.n_hg;
+  it.hg = hg;
   it.nc = (L + item_tokens - 1) / item_tokens;
   it.t0 = chunk * item_tokens;
   it.nt = min(item_tokens, L - it.t0);
@@ -175,7 +185,13 @@ __device__ __forceinline__ void reduce_scatter_level(float* x) {
 // thread straight from global memory.
 constexpr int kSmallMerge = 16;
 
-template <int QT, int D, int GT>
+// APP: decode with append.  The item that holds a sequence's new token
+// (position length - 1) quantizes the token's K and V rows with the store's
+// own routine (quantize_piece); the wave whose page group holds the token
+// writes its codes and scales to the pools (items of head group 0 only) and
+// uses the same codes in place of whatever its load of that slot returned,
+// so the result never depends on the order of that store and that load.
+template <int QT, int D, int GT, bool APP>
 __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
   using Gm = Geo<QT, D>;
   constexpr int EPL = Gm::EPL, LPT = Gm::LPT, TPL = Gm::TPL, LPP = Gm::LPP, NDW = Gm::NDW;
@@ -234,6 +250,26 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
     }
   };
 
+  // the new token's K and V slices of this lane (bf16 pairs), loaded beside
+  // the query of every item (decode with append)
+  uint32_t nrow[2][EPL / 2];
+  auto load_new = [&](const Item& it) {
+    if constexpr (APP) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint16_t* src = a.new_kv[t] + (int64_t)it.b * a.new_stride + it.kvh * D + d0;
+#pragma unroll
+        for (int e = 0; e < EPL; e += 8) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src + e);
+          nrow[t][e / 2 + 0] = v.x;
+          nrow[t][e / 2 + 1] = v.y;
+          nrow[t][e / 2 + 2] = v.z;
+          nrow[t][e / 2 + 3] = v.w;
+        }
+      }
+    }
+  };
+
   // The work list.  Up to 64 sequences, every wave builds it alone (lane b
   // holds the items before sequence b, and its length): one load, no LDS,
   // no barrier.  Beside that load, the page ids and query of this
@@ -242,11 +278,11 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
   // (the loads are unconditional and in bounds either way).  Larger batches
   // scan seq_lens in LDS.
   const bool small = a.batch <= 64 && (int64_t)a.batch * a.max_pages < (1 << 30);
-  int item_tokens, total, wpfx = 0, wlen = 0, pid_spec = -1;
+  int item_tokens, total, wpfx = 0, wlen = 0, pid_spec = -1, raw_len = 0;
   Item spec;
   spec.b = -1;
   if (small) {
-    const int raw_len = a.seq_lens[min(lane, a.batch - 1)];
+    raw_len = a.seq_lens[min(lane, a.batch - 1)];
     const int full = a.max_pages * kPageSize;
     const int g_tokens = rule_item_tokens(p.rule, (int64_t)a.batch * a.max_pages, units);
     const int g_per_seq = (full + g_tokens - 1) / g_tokens * units;
@@ -255,6 +291,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
     spec = describe<PPS, GT>(p, g_tokens, g_item, g_b, g_item - g_b * g_per_seq, full, wave, units, G);
     pid_spec = load_pids(spec);
     load_q(spec);
+    load_new(spec);
     // the length is first used here, after the speculative loads are issued
     __builtin_amdgcn_sched_barrier(0);
     wlen = lane < a.batch ? min(max(raw_len, 0), a.max_pages * kPageSize) : 0;
@@ -338,8 +375,8 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
 
   // Log2-domain scores of a step's rows (-inf for rows on a masked page or
   // past the item end), their validity and the V scale of each row.
-  auto scores = [&](const Item& it, int pid, int st, const Buf& X, float (*sc)[GT], bool* ok,
-                    float* vsf) {
+  auto scores = [&](const Item& it, int pid, int st, Buf& X, float (*sc)[GT], bool* ok,
+                    float* vsf, const NewRow<NDW>& nr) {
     // scales of this step's pages -> this wave's LDS area -> one per row
     float ksf[ROWS];
     if constexpr (qt_scaled(QT)) {
@@ -365,6 +402,20 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
       for (int r = 0; r < ROWS; ++r) {
         ksf[r] = 1.0f;
         vsf[r] = 1.0f;
+      }
+    }
+    // the new token's row (decode with append): its codes and scales replace
+    // what the load of its slot returned
+    if constexpr (APP) {
+      if (st == nr.step) {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r)
+          if (r == nr.row && nr.on) {
+            X.k[r] = nr.k;
+            X.v[r] = nr.v;
+            ksf[r] = nr.ks;
+            vsf[r] = nr.vs;
+          }
       }
     }
     // row validity: page present and token before the item end (a select,
@@ -476,6 +527,48 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
     if (!hit) {
       pid_cur = load_pids(cur);
       load_q(cur);
+      load_new(cur);
+    }
+    // The new token (decode with append), if this item holds it: the step
+    // and row index where this wave meets it, and its codes and scales.
+    NewRow<NDW> nr;
+    nr.step = -1;
+    if constexpr (APP) {
+      const int raw = small ? __builtin_amdgcn_readlane(raw_len, bq) : a.seq_lens[bq];
+      const int tn = raw - 1;
+      if (raw >= 1 && raw <= a.max_pages * kPageSize && tn >= cur.t0 && tn < cur.t0 + cur.nt) {
+        const int pi = (tn - cur.t0) / kPageSize, grp = pi / PPS;
+        if (grp % kWaves == wave) {  // uniform: the wave that streams its page
+          const int st = grp / kWaves, k = pi - grp * PPS, r = tn % kPageSize;
+          nr.step = st;
+          nr.row = k * LPP + r / TPL;
+          nr.on = tsub == r % TPL;
+          uint16_t sb[2];
+          quantize_piece<QT, EPL>(nrow[0], nr.k.w, &sb[0]);
+          quantize_piece<QT, EPL>(nrow[1], nr.v.w, &sb[1]);
+          nr.ks = qt_scaled(QT) ? f16_bits_to_f32(sb[0]) : 1.0f;
+          nr.vs = qt_scaled(QT) ? f16_bits_to_f32(sb[1]) : 1.0f;
+          const int P = __builtin_amdgcn_readlane(pid_cur, st * PPS + k);
+          if (P >= 0 && cur.hg == 0 && nr.on) {
+            const int64_t row = ((int64_t)P * a.n_kv_heads + cur.kvh) * kPageSize + r;
+            uint8_t* kp = const_cast<uint8_t*>(a.k_pool) + (row * D + d0) * ESZ;
+            uint8_t* vp = const_cast<uint8_t*>(a.v_pool) + (row * D + d0) * ESZ;
+            if constexpr (NDW == 4) {
+              *reinterpret_cast<uint4*>(kp) = make_uint4(nr.k.w[0], nr.k.w[1], nr.k.w[2], nr.k.w[3]);
+              *reinterpret_cast<uint4*>(vp) = make_uint4(nr.v.w[0], nr.v.w[1], nr.v.w[2], nr.v.w[3]);
+            } else {
+              *reinterpret_cast<uint2*>(kp) = make_uint2(nr.k.w[0], nr.k.w[1]);
+              *reinterpret_cast<uint2*>(vp) = make_uint2(nr.v.w[0], nr.v.w[1]);
+            }
+            if constexpr (qt_scaled(QT)) {
+              if ((seg & (32 / EPL - 1)) == 0) {
+                const_cast<uint16_t*>(a.k_scales)[row * NB + (d0 >> 5)] = sb[0];
+                const_cast<uint16_t*>(a.v_scales)[row * NB + (d0 >> 5)] = sb[1];
+              }
+            }
+          }
+        }
+      }
     }
     // Stream the item's steps, kDepth steps' loads in flight (cur.nsteps is
     // a multiple of kDepth).  The softmax reference of each head stays fixed
@@ -491,7 +584,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
       if (pass == 0) {
         float sc0[ROWS][GT], vs0[ROWS];
         bool ok0[ROWS];
-        scores(cur, pid_cur, 0, R[0], sc0, ok0, vs0);
+        scores(cur, pid_cur, 0, R[0], sc0, ok0, vs0, nr);
 #pragma unroll
         for (int h = 0; h < GT; ++h) {
           float t = sc0[0][h];
@@ -513,7 +606,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
         for (int k = 0; k < kDepth; ++k) {
           float sc[ROWS][GT], vsf[ROWS];
           bool ok[ROWS];
-          scores(cur, pid_cur, st + k, R[k], sc, ok, vsf);
+          scores(cur, pid_cur, st + k, R[k], sc, ok, vsf, nr);
           accumulate(R[k], sc, ok, vsf);
           const int sn = st + k + kDepth;
           load_step(cur, pid_cur, sn, sn < cur.nsteps, R[k]);
@@ -720,7 +813,10 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
 template <int QT, int D, int GT>
 hipError_t launch_one(const GqaParams& gp, int grid, hipStream_t s) {
   const size_t dyn = (size_t)(gp.a.batch + 1) * sizeof(int);
-  gqa_decode_kernel<QT, D, GT><<<grid, kThreads, dyn, s>>>(gp);
+  if (gp.a.new_kv[0])
+    gqa_decode_kernel<QT, D, GT, true><<<grid, kThreads, dyn, s>>>(gp);
+  else
+    gqa_decode_kernel<QT, D, GT, false><<<grid, kThreads, dyn, s>>>(gp);
   return hipGetLastError();
 }
 
@@ -744,10 +840,8 @@ hipError_t launch_d(const GqaParams& gp, int grid, hipStream_t s) {
   }
 }
 
-}  // namespace
-
-hipError_t launch_gqa_decode(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
-                             hipStream_t s) {
+template <int QT>
+hipError_t launch_typed(const DecodeArgs& a, const DecodePlan& plan, int num_cus, hipStream_t s) {
   char* ws = static_cast<char*>(a.workspace);
   GqaParams gp;
   gp.a = a;
@@ -771,16 +865,29 @@ hipError_t launch_gqa_decode(const DecodeArgs& a, const DecodePlan& plan, int nu
   if (grid > plan.max_items) grid = plan.max_items;
   if (a.items_hint > 0 && grid > a.items_hint) grid = a.items_hint;  // exact from host lengths
   if (grid < 1) grid = 1;
-  hipError_t e;
-  switch (a.qtype) {
-    case QT_BF16: e = launch_d<QT_BF16>(gp, (int)grid, s); break;
-    case QT_FP8: e = launch_d<QT_FP8>(gp, (int)grid, s); break;
-    case QT_FP8C: e = launch_d<QT_FP8C>(gp, (int)grid, s); break;
-    case QT_BF8C: e = launch_d<QT_BF8C>(gp, (int)grid, s); break;
-    default: e = launch_d<QT_Q8>(gp, (int)grid, s); break;
-  }
+  const hipError_t e = launch_d<QT>(gp, (int)grid, s);
   if (e != hipSuccess || plan.fused_merge) return e;
   return launch_gqa_merge(a, plan, s);
 }
+
+}  // namespace
+
+// The library's build compiles this file once per storage type
+// (-DKVQ_DECODE_QT); compiled alone it defines all five.
+#define KVQ_DEFINE_TYPED(QT)                                                                  \
+  template <>                                                                                \
+  hipError_t launch_gqa_decode_typed<QT>(const DecodeArgs& a, const DecodePlan& plan,        \
+                                         int num_cus, hipStream_t s) {                       \
+    return launch_typed<QT>(a, plan, num_cus, s);                                            \
+  }
+#ifdef KVQ_DECODE_QT
+KVQ_DEFINE_TYPED(KVQ_DECODE_QT)
+#else
+KVQ_DEFINE_TYPED(QT_BF16)
+KVQ_DEFINE_TYPED(QT_FP8)
+KVQ_DEFINE_TYPED(QT_Q8)
+KVQ_DEFINE_TYPED(QT_FP8C)
+KVQ_DEFINE_TYPED(QT_BF8C)
+#endif
 
 }  // namespace kvq

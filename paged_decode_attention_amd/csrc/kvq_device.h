@@ -144,6 +144,110 @@ __device__ __forceinline__ float dpp_xor2(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
 }
 
+// ---- quantize-on-store of one lane's piece of a row ---------------------------------
+// The store kernel and the decode with append both store through these, so an
+// appended row holds the same bytes as a stored one.
+
+// Eight elements of a block with the fp16 scale s (as fp32) -> eight 8-bit
+// codes in two dwords.  The quotient x / s is x * rcp(s) plus one residual
+// correction: x has an 8-bit and s an 11-bit significand, so the exact
+// quotient is either a rounding midpoint of the code grid (at most 5
+// significant bits, reproduced exactly) or at least 2^-18 (relative) away from
+// every midpoint, beyond the corrected quotient's one-ulp error.  The clamp to
+// +-M keeps x's sign (-0 stays -0; an infinite element, whose residual is
+// inf - inf, stores +-M since fminf(NaN, M) is M).  e4m3: round to nearest
+// even by the packed conversion; q8_0: half away from zero.
+template <int QT>
+__device__ __forceinline__ void quantize8(const float* x, float s, uint32_t* out2) {
+  constexpr float M = (QT == QT_Q8) ? 127.0f : 448.0f;
+  if (s == 0.0f) {
+    out2[0] = 0u;
+    out2[1] = 0u;
+    return;
+  }
+  const float r = __builtin_amdgcn_rcpf(s);  // s is a normal fp32 value (an fp16 scale)
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float q0 = x[i] * r;
+    const float q = fmaf(fmaf(-s, q0, x[i]), r, q0);
+    v[i] = copysignf(fminf(fabsf(q), M), x[i]);
+  }
+  if constexpr (QT == QT_FP8) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+      out2[w] = e4m3x4_rne(v[4 * w + 0], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3]);
+  } else {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      uint32_t r = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        int c = (int)roundf(v[4 * w + k]);  // half away from zero, |c| <= 127
+        r |= ((uint32_t)c & 0xffu) << (8 * k);
+      }
+      out2[w] = r;
+    }
+  }
+}
+
+// A lane's E consecutive elements of a row (E/2 bf16 pairs) -> their codes
+// (E/4 dwords; a bf16 pool keeps the E/2 dwords as they are) and, for the
+// block-scaled types, the fp16 scale bits of the 32-element block.  The block
+// spans 32 / E consecutive lanes (a pair for E = 16, four lanes for E = 8),
+// all of which must be active: the block max is a DPP max across them.
+// Scale: IEEE fp32 amax / M, held at 65504 (an infinite max saturates), then
+// fp16 round to nearest even.  Cast types: each element clamped to the
+// format's largest finite magnitude (448 e4m3, 57344 e5m2), then the packed
+// round-to-nearest-even conversion.
+template <int QT, int E>
+__device__ __forceinline__ void quantize_piece(const uint32_t* bf, uint32_t* codes,
+                                               uint16_t* sbits) {
+  static_assert(E == 8 || E == 16, "8 or 16 elements per lane");
+  if constexpr (QT == QT_BF16) {
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) codes[i] = bf[i];
+    *sbits = 0;
+  } else {
+    float x[E];
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) {
+      x[2 * i] = bf16_lo(bf[i]);
+      x[2 * i + 1] = bf16_hi(bf[i]);
+    }
+    if constexpr (!qt_scaled(QT)) {
+      constexpr float M = (QT == QT_BF8C) ? 57344.0f : 448.0f;
+#pragma unroll
+      for (int d = 0; d < E / 4; ++d) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = fminf(fmaxf(x[4 * d + i], -M), M);
+        if constexpr (QT == QT_BF8C) {
+          const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(v[0], v[1], 0, false);
+          codes[d] = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(v[2], v[3], lo, true);
+        } else {
+          codes[d] = e4m3x4_rne(v[0], v[1], v[2], v[3]);
+        }
+      }
+      *sbits = 0;
+    } else {
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(x[i]));
+      amax = fmaxf(amax, dpp_xor1(amax));                        // the block's other lanes
+      if constexpr (E == 8) amax = fmaxf(amax, dpp_xor2(amax));
+      constexpr float M = (QT == QT_Q8) ? 127.0f : 448.0f;
+      float sq = amax / M;           // IEEE fp32 division
+      sq = fminf(sq, 65504.0f);      // a quotient past the fp16 range saturates
+      const _Float16 sh = (_Float16)sq;  // round to nearest even
+      const float s = (float)sh;
+#pragma unroll
+      for (int i = 0; i < E / 8; ++i) quantize8<QT>(x + 8 * i, s, codes + 2 * i);
+      *sbits = __builtin_bit_cast(uint16_t, sh);
+    }
+  }
+}
+
 // ---- division by a runtime constant (unsigned 32-bit, exact) -------------------
 // n / d == umulhi(n, m) >> s for all n < 2^31 with m, s from the usual
 // round-up reciprocal construction.

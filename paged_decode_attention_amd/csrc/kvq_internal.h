@@ -74,6 +74,14 @@ struct StoreArgs {
   int64_t num_pages;
   uint8_t* pool[2];
   uint16_t* scales[2];
+  // Append mode (seq_lens set, slots unused): token b is the new token of
+  // sequence b, stored at position seq_lens[b] - 1 through the page table;
+  // nothing is stored for a length of 0 or past max_pages pages, or for a
+  // masked page.
+  const int32_t* seq_lens = nullptr;
+  const int32_t* page_table = nullptr;
+  int64_t pt_stride = 0;
+  int max_pages = 0;
 };
 
 struct DequantArgs {
@@ -133,6 +141,13 @@ struct DecodeArgs {
   // at most max_new of them per sequence.
   const int32_t* q_start = nullptr;
   int max_new = 0;
+  // Decode with append (kvq_paged_decode_append): the bf16 K and V rows of
+  // each sequence's new token, new_kv[t] + b * new_stride ([n_kv_heads][D]),
+  // are quantized and written to position seq_lens[b] - 1 (as the append
+  // store above) before that position is attended; the pools are then
+  // written, so the pool pointers above are the caller's writable ones.
+  const uint16_t* new_kv[2] = {nullptr, nullptr};
+  int64_t new_stride = 0;
   // Host-side only: the exact number of work items when the caller passed
   // the lengths on the host too (0: unknown); the launch then holds no
   // workgroup beyond it.  The kernels themselves plan from seq_lens.
@@ -148,8 +163,31 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
                  int head_dim_v, int page_size, int max_pages, DecodePlan* plan,
                  const char** why, int ext_new = 0);
 
-hipError_t launch_gqa_decode(const DecodeArgs& a, const DecodePlan& p, int num_cus,
-                             hipStream_t s);
+// The VALU decode kernels of one storage type; kvq_decode.hip is compiled
+// once per type (-DKVQ_DECODE_QT), each object defining its own.
+template <int QT>
+hipError_t launch_gqa_decode_typed(const DecodeArgs& a, const DecodePlan& p, int num_cus,
+                                   hipStream_t s);
+template <>
+hipError_t launch_gqa_decode_typed<QT_BF16>(const DecodeArgs&, const DecodePlan&, int, hipStream_t);
+template <>
+hipError_t launch_gqa_decode_typed<QT_FP8>(const DecodeArgs&, const DecodePlan&, int, hipStream_t);
+template <>
+hipError_t launch_gqa_decode_typed<QT_Q8>(const DecodeArgs&, const DecodePlan&, int, hipStream_t);
+template <>
+hipError_t launch_gqa_decode_typed<QT_FP8C>(const DecodeArgs&, const DecodePlan&, int, hipStream_t);
+template <>
+hipError_t launch_gqa_decode_typed<QT_BF8C>(const DecodeArgs&, const DecodePlan&, int, hipStream_t);
+inline hipError_t launch_gqa_decode(const DecodeArgs& a, const DecodePlan& p, int num_cus,
+                                    hipStream_t s) {
+  switch (a.qtype) {
+    case QT_BF16: return launch_gqa_decode_typed<QT_BF16>(a, p, num_cus, s);
+    case QT_FP8: return launch_gqa_decode_typed<QT_FP8>(a, p, num_cus, s);
+    case QT_FP8C: return launch_gqa_decode_typed<QT_FP8C>(a, p, num_cus, s);
+    case QT_BF8C: return launch_gqa_decode_typed<QT_BF8C>(a, p, num_cus, s);
+    default: return launch_gqa_decode_typed<QT_Q8>(a, p, num_cus, s);
+  }
+}
 // The separate split-K merge of the GQA kernels (plan.fused_merge == false).
 hipError_t launch_gqa_merge(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 hipError_t launch_gqa_mfma_decode(const DecodeArgs& a, const DecodePlan& p, int num_cus,

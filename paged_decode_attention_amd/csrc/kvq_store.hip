@@ -54,44 +54,6 @@ struct StoreGrid {
   uint32_t n_lanes;
 };
 
-template <int QT>
-__device__ __forceinline__ void quantize8(const float* x, float s, uint32_t* out2) {
-  constexpr float M = (QT == QT_Q8) ? 127.0f : 448.0f;
-  if (s == 0.0f) {
-    out2[0] = 0u;
-    out2[1] = 0u;
-    return;
-  }
-  const float r = __builtin_amdgcn_rcpf(s);  // s is a normal fp32 value (an fp16 scale)
-  float v[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float q0 = x[i] * r;
-    // x / s (see the header), clamped in magnitude with x's sign (s > 0):
-    // a -0 element stays -0 (the correction step alone would give +0), and
-    // an infinite element, whose residual is inf - inf (NaN), stores +-M
-    // (the minimum of NaN and M is M).
-    const float q = fmaf(fmaf(-s, q0, x[i]), r, q0);
-    v[i] = copysignf(fminf(fabsf(q), M), x[i]);
-  }
-  if constexpr (QT == QT_FP8) {
-#pragma unroll
-    for (int w = 0; w < 2; ++w)
-      out2[w] = e4m3x4_rne(v[4 * w + 0], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3]);
-  } else {
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      uint32_t r = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        int c = (int)roundf(v[4 * w + k]);  // half away from zero, |c| <= 127
-        r |= ((uint32_t)c & 0xffu) << (8 * k);
-      }
-      out2[w] = r;
-    }
-  }
-}
-
 // Workgroups are dealt to the 8 XCDs in turn (block b runs on XCD b % 8).
 // Give each XCD one contiguous run of logical blocks instead, so that the
 // consecutive tokens of a page -- whose 128-byte scale rows and code rows
@@ -101,6 +63,17 @@ __device__ __forceinline__ void quantize8(const float* x, float s, uint32_t* out
 __device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t n) {
   const uint32_t q = n >> 3, r = n & 7u, x = b & 7u;
   return x * q + (x < r ? x : r) + (b >> 3);
+}
+
+// The slot of a token: from the slot map, or in append mode from the
+// sequence's length and page table (-1: nothing to store).
+__device__ __forceinline__ int32_t token_slot(const StoreArgs& a, int64_t token) {
+  if (!a.seq_lens) return a.slots[token];
+  const int32_t L = a.seq_lens[token];
+  if (L < 1 || (int64_t)L > (int64_t)a.max_pages * a.page_size) return -1;
+  const int32_t P = a.page_table[token * a.pt_stride + (L - 1) / a.page_size];
+  if (P < 0 || (int64_t)P >= a.num_pages) return -1;
+  return P * a.page_size + (L - 1) % a.page_size;
 }
 
 template <int QT>
@@ -119,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs a, StoreGrid 
   const uint32_t r1 = r0 - h * g.per_head.d;  // piece of E elements within the row
   const int nb = a.head_dim >> 5;
 
-  const int32_t slot = in_range ? a.slots[token] : -1;
+  const int32_t slot = in_range ? token_slot(a, token) : -1;
   const int64_t cap = a.num_pages * (int64_t)a.page_size;
   const bool valid = slot >= 0 && (int64_t)slot < cap;
 
@@ -145,45 +118,13 @@ __global__ __launch_bounds__(kThreads) void store_kernel(StoreArgs a, StoreGrid 
     if constexpr (QT == QT_BF16) {
       if (valid) *reinterpret_cast<uint4*>(a.pool[t] + (row * a.head_dim + col) * 2) = raws[t][0];
     } else {
-      float x[16];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const uint32_t w[4] = {raws[t][p].x, raws[t][p].y, raws[t][p].z, raws[t][p].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[8 * p + 2 * i] = bf16_lo(w[i]);
-          x[8 * p + 2 * i + 1] = bf16_hi(w[i]);
-        }
-      }
+      const uint32_t bf[8] = {raws[t][0].x, raws[t][0].y, raws[t][0].z, raws[t][0].w,
+                              raws[t][1].x, raws[t][1].y, raws[t][1].z, raws[t][1].w};
       uint32_t codes[4];
-      if constexpr (!qt_scaled(QT)) {
-        constexpr float M = (QT == QT_BF8C) ? 57344.0f : 448.0f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          float v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = fminf(fmaxf(x[4 * d + i], -M), M);
-          if constexpr (QT == QT_BF8C) {
-            const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(v[0], v[1], 0, false);
-            codes[d] = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(v[2], v[3], lo, true);
-          } else {
-            codes[d] = e4m3x4_rne(v[0], v[1], v[2], v[3]);
-          }
-        }
-      } else {
-        float amax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
-        amax = fmaxf(amax, dpp_xor1(amax));  // the other half of the block
-        constexpr float M = (QT == QT_Q8) ? 127.0f : 448.0f;
-        float sq = amax / M;  // IEEE fp32 division
-        sq = fminf(sq, 65504.0f);  // a quotient past the fp16 range saturates
-        const _Float16 sh = (_Float16)sq;  // round to nearest even
-        const float s = (float)sh;
-        quantize8<QT>(x, s, codes);
-        quantize8<QT>(x + 8, s, codes + 2);
-        if (valid && (r1 & 1u) == 0) a.scales[t][row * nb + (r1 >> 1)] = __builtin_bit_cast(uint16_t, sh);
-      }
+      uint16_t sbits;
+      quantize_piece<QT, 16>(bf, codes, &sbits);
+      if constexpr (qt_scaled(QT))
+        if (valid && (r1 & 1u) == 0) a.scales[t][row * nb + (r1 >> 1)] = sbits;
       if (valid)
         *reinterpret_cast<uint4*>(a.pool[t] + row * a.head_dim + col) =
             make_uint4(codes[0], codes[1], codes[2], codes[3]);
@@ -243,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void store_dsm_kernel(StoreArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t token = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (token >= a.n_tokens) return;  // uniform over the wave
-  const int32_t slot = a.slots[token];
+  const int32_t slot = token_slot(a, token);
   if (slot < 0 || (int64_t)slot >= a.num_pages * (int64_t)a.page_size) return;
   const uint16_t* src = a.src[0] + token * a.stride;
   const uint4 raw = *reinterpret_cast<const uint4*>(src + 8 * lane);
@@ -335,7 +276,12 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t s) {
     StoreArgs sub = a;
     const int64_t n = (a.n_tokens - t0 < max_tokens) ? a.n_tokens - t0 : max_tokens;
     sub.n_tokens = n;
-    sub.slots = a.slots + t0;
+    if (a.seq_lens) {
+      sub.seq_lens = a.seq_lens + t0;
+      sub.page_table = a.page_table + t0 * a.pt_stride;
+    } else {
+      sub.slots = a.slots + t0;
+    }
     for (int t = 0; t < 2; ++t)
       if (sub.src[t]) sub.src[t] = a.src[t] + t0 * a.stride;
     StoreGrid g;

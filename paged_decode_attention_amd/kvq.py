@@ -57,6 +57,9 @@ def _load() -> ctypes.CDLL:
     lib.kvq_paged_decode.argtypes = [I, P, P, P, P, P, P, I64, P, P, I, I, I, I, I, I, I, I64,
                                      c.c_float, P, P, P, c.c_size_t, P]
     lib.kvq_paged_decode.restype = I
+    lib.kvq_paged_decode_append.argtypes = [I, P, P, P, I64, P, P, P, P, P, I64, P, P, I, I, I, I,
+                                            I, I, I, I64, c.c_float, P, P, P, c.c_size_t, P]
+    lib.kvq_paged_decode_append.restype = I
     lib.kvq_sparse_mla_decode_workspace_bytes.argtypes = [I, I, I, I]
     lib.kvq_sparse_mla_decode_workspace_bytes.restype = c.c_size_t
     lib.kvq_sparse_mla_decode.argtypes = [I, P, P, P, P, I64, P, P, I64, I, I, I, I, I, I64,
@@ -83,7 +86,7 @@ LIB = _load()
 
 # every symbol the public header declares
 EXPORTS = ("kvq_pool_bytes", "kvq_store", "kvq_dequant", "kvq_paged_decode_workspace_bytes",
-           "kvq_paged_decode", "kvq_paged_decode_noalloc", "kvq_sparse_mla_decode_workspace_bytes",
+           "kvq_paged_decode", "kvq_paged_decode_append", "kvq_paged_decode_noalloc", "kvq_sparse_mla_decode_workspace_bytes",
            "kvq_sparse_mla_decode", "kvq_extend_attention_workspace_bytes", "kvq_extend_attention",
            "kvq_last_error")
 # the test exports (kvq_debug.h)
@@ -278,6 +281,46 @@ def paged_decode(dtype, q, k_pool, k_scales, v_pool, v_scales, page_table, seq_l
     return out, lse
 
 
+def _new_stride(new_k, batch, n_kv_heads, head_dim_qk) -> int:
+    if new_k.stride(-1) != 1 or (new_k.dim() == 3 and new_k.stride(1) != head_dim_qk):
+        raise ValueError("new_k rows must be contiguous [batch][n_kv_heads][head_dim]")
+    return new_k.stride(0) if batch > 1 else n_kv_heads * head_dim_qk
+
+
+def paged_decode_append(dtype, q, new_k, new_v, k_pool, k_scales, v_pool, v_scales, page_table,
+                        seq_lens, sm_scale: float, head_dim_v: int | None = None, out=None,
+                        lse=None, workspace=None, stream=None, seq_lens_host=None):
+    """Store each sequence's new token (bf16 new_k / new_v [batch][n_kv_heads]
+    [head_dim], position seq_lens[b] - 1), then decode; returns (out, lse).
+    new_v is None for the shared MLA slab."""
+    batch, n_q_heads, head_dim_qk = q.shape
+    num_pages, n_kv_heads, page_size, _ = k_pool.shape
+    if head_dim_v is None:
+        head_dim_v = v_pool.shape[3]
+    max_pages = page_table.shape[1]
+    if page_table.stride(1) != 1:
+        raise ValueError("page_table rows must be contiguous")
+    pt_stride = page_table.stride(0) if batch > 1 else max_pages
+    if out is None:
+        out = torch.empty((batch, n_q_heads, head_dim_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((batch, n_q_heads), dtype=torch.float32, device=q.device)
+    need = workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim_v, max_pages, page_size)
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _lens, lens_ptr = _host_lens(seq_lens_host)
+    rc = LIB.kvq_paged_decode_append(
+        _dt(dtype), _ptr(q), _ptr(new_k), _ptr(new_v),
+        _new_stride(new_k, batch, n_kv_heads, head_dim_qk), _ptr(k_pool), _ptr(k_scales),
+        _ptr(v_pool), _ptr(v_scales), _ptr(page_table), pt_stride, _ptr(seq_lens), lens_ptr,
+        batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, page_size, max_pages, num_pages,
+        float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream(q.device, stream))
+    _check(rc)
+    return out, lse
+
+
 def paged_decode_noalloc(dtype, q, k_pool, k_scales, v_pool, v_scales, page_table, seq_lens,
                          sm_scale: float, head_dim_v: int | None = None, out=None, lse=None,
                          stream=None, seq_lens_host=None):
@@ -416,7 +459,9 @@ class PreparedDecode:
 
     def __init__(self, dtype, q, k_pool, k_scales, v_pool, v_scales, page_table, seq_lens,
                  sm_scale, head_dim_v=None, out=None, lse=None, workspace=None, stream=None,
-                 seq_lens_host=None):
+                 seq_lens_host=None, new_k=None, new_v=None):
+        """With new_k (and new_v, unless the pool is the shared slab) the call
+        is kvq_paged_decode_append: each sequence's new token is stored first."""
         batch, n_q_heads, head_dim_qk = q.shape
         num_pages, n_kv_heads, page_size, _ = k_pool.shape
         head_dim_v = head_dim_v or v_pool.shape[3]
@@ -430,15 +475,21 @@ class PreparedDecode:
             need, dtype=torch.uint8, device=q.device)
         pt_stride = page_table.stride(0) if batch > 1 else max_pages
         lens, lens_ptr = _host_lens(seq_lens_host)
-        self._keep = (q, k_pool, k_scales, v_pool, v_scales, page_table, seq_lens, lens)
-        self.args = (_dt(dtype), _ptr(q), _ptr(k_pool), _ptr(k_scales), _ptr(v_pool),
-                     _ptr(v_scales), _ptr(page_table), pt_stride, _ptr(seq_lens), lens_ptr, batch,
-                     n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, page_size, max_pages,
-                     num_pages, float(sm_scale), _ptr(self.out), _ptr(self.lse),
-                     _ptr(self.workspace), self.workspace.numel(), _stream(q.device, stream))
+        self._keep = (q, k_pool, k_scales, v_pool, v_scales, page_table, seq_lens, lens, new_k,
+                      new_v)
+        head = (_dt(dtype), _ptr(q))
+        if new_k is not None:
+            head += (_ptr(new_k), _ptr(new_v), _new_stride(new_k, batch, n_kv_heads, head_dim_qk))
+        self.fn = LIB.kvq_paged_decode_append if new_k is not None else LIB.kvq_paged_decode
+        self.args = head + (_ptr(k_pool), _ptr(k_scales), _ptr(v_pool),
+                            _ptr(v_scales), _ptr(page_table), pt_stride, _ptr(seq_lens), lens_ptr,
+                            batch, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, page_size,
+                            max_pages, num_pages, float(sm_scale), _ptr(self.out), _ptr(self.lse),
+                            _ptr(self.workspace), self.workspace.numel(),
+                            _stream(q.device, stream))
 
     def __call__(self):
-        _check(LIB.kvq_paged_decode(*self.args))
+        _check(self.fn(*self.args))
 
 
 class PreparedSparse:

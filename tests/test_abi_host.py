@@ -116,6 +116,32 @@ def test_decode_validation():
     assert call(dtype=5) == kvq.ERR_UNSUPPORTED and "656-byte" in kvq.last_error()
 
 
+def test_append_validation():
+    """kvq_paged_decode_append checks the new rows before anything is
+    enqueued (every call here is refused on the host)."""
+    L = kvq.LIB
+
+    def call(nk=256, nv=512, stride=8 * 128, kp=256, vp=512, D=128, Dv=128, Hkv=8, ws=1 << 30,
+             wsp=256):
+        vs = 256 if vp == kp else 512
+        return L.kvq_paged_decode_append(1, 256, nk, nv, stride, kp, 256, vp, vs, 256, 8, 256,
+                                         None, 2, 16, Hkv, D, Dv, 16, 8, 64, 0.1, 256, None, wsp,
+                                         ws, None)
+
+    assert call(nk=None) == kvq.ERR_ARG and "new_k" in kvq.last_error()
+    assert call(nv=None) == kvq.ERR_ARG and "new_v" in kvq.last_error()   # separate pools
+    assert call(stride=100) == kvq.ERR_ARG and "stride" in kvq.last_error()
+    assert call(stride=8 * 128 - 8) == kvq.ERR_ARG
+    assert call(nk=264) == kvq.ERR_ARG and "aligned" in kvq.last_error()
+    # the shared slab takes no new_v
+    assert call(kp=256, vp=256, D=576, Dv=512, Hkv=1, stride=576) == kvq.ERR_ARG
+    assert "new_v" in kvq.last_error()
+    # the decode's own checks still apply (and come first)
+    assert call(D=96, Dv=96) == kvq.ERR_UNSUPPORTED
+    assert call(ws=16, nk=None) == kvq.ERR_ARG
+    assert call(ws=16) == kvq.ERR_WORKSPACE
+
+
 def test_workspace_query_covers_every_storage_type():
     """kvq_paged_decode_workspace_bytes takes no storage type: its answer is
     the largest workspace any type's plan needs for the shapes (the plans
