@@ -658,12 +658,17 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
 
 // ---- split-K merge -------------------------------------------------------------------
 // Block = (sequence b, head h, half of the columns); 16 groups of 32 threads
-// take every 16th chunk, a thread 8 columns, four chunk rows in flight.
+// take every 16th chunk, a thread 8 columns.  The first kAheadRows chunk rows
+// of every thread are requested before anything else, the chunks' (m, l)
+// beside them (wave 0, all of a lane's chunks at once); the weights are
+// formed while those rows arrive.
 // With w_c = 2^(m_c - M) l_c: O = sum_c w_c O_c / sum_c w_c (O_c the chunk's
 // normalized output) and lse = M + log2(sum_c w_c) in log2 units.
 constexpr int kMergeGroups = 16;
 constexpr int kMergeCols = kDv / 2;
 constexpr int kMergeThreads = kMergeGroups * (kMergeCols / 8);
+constexpr int kAheadRows = 8;                          // chunk rows per thread in flight
+constexpr int kMlPerLane = kMlaMaxChunks / 64;         // (m, l) pairs per lane of wave 0
 
 __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaParams p) {
   const DecodeArgs& a = p.a;
@@ -677,16 +682,38 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaParams p) {
   __shared__ __attribute__((aligned(16))) float s_red[kMergeGroups][kMergeCols];
   __shared__ float s_L;
   const int tid = threadIdx.x, lane = tid & 63;
+  const int grp = tid >> 5, j = tid & 31;
+  const int d0 = half * kMergeCols + 8 * j;
+  const uint16_t* src = p.part_out + ((int64_t)first * Hq + h) * kDv + d0;
+  const int64_t cstride = (int64_t)Hq * kDv;
+  // the first rows of this thread's chunks, requested at once
+  u32x4 x0[kAheadRows];
+#pragma unroll
+  for (int k = 0; k < kAheadRows; ++k) {
+    const int c = grp + k * kMergeGroups;
+    x0[k] = c < nc ? *reinterpret_cast<const u32x4*>(src + (int64_t)c * cstride) : u32x4{0, 0, 0, 0};
+  }
   if (tid < 64) {
+    float2 ml[kMlPerLane];
+#pragma unroll
+    for (int k = 0; k < kMlPerLane; ++k) {
+      const int c = lane + 64 * k;
+      ml[k] = c < nc ? *reinterpret_cast<const float2*>(p.part_ml + ((int64_t)(first + c) * Hq + h) * 2)
+                     : make_float2(-INFINITY, 0.0f);
+    }
     float M = -INFINITY;
-    for (int c = lane; c < nc; c += 64) M = fmaxf(M, p.part_ml[((int64_t)(first + c) * Hq + h) * 2]);
+#pragma unroll
+    for (int k = 0; k < kMlPerLane; ++k) M = fmaxf(M, ml[k].x);
     M = stride_max<1>(M);
     float Ls = 0.0f;
-    for (int c = lane; c < nc; c += 64) {
-      const float* ml = p.part_ml + ((int64_t)(first + c) * Hq + h) * 2;
-      const float w = exp2_rel(ml[0], M) * ml[1];
-      s_w[c] = w;
-      Ls += w;
+#pragma unroll
+    for (int k = 0; k < kMlPerLane; ++k) {
+      const int c = lane + 64 * k;
+      if (c < nc) {
+        const float w = exp2_rel(ml[k].x, M) * ml[k].y;
+        s_w[c] = w;
+        Ls += w;
+      }
     }
     Ls = stride_sum<1>(Ls);
     if (lane == 0) {
@@ -696,10 +723,6 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaParams p) {
     }
   }
   __syncthreads();
-  const int grp = tid >> 5, j = tid & 31;
-  const int d0 = half * kMergeCols + 8 * j;
-  const uint16_t* src = p.part_out + ((int64_t)first * Hq + h) * kDv + d0;
-  const int64_t cstride = (int64_t)Hq * kDv;
   float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   auto add = [&](const u32x4& x, float w) {
 #pragma unroll
@@ -708,7 +731,12 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaParams p) {
       v[2 * k + 1] += w * bf16_hi(x[k]);
     }
   };
-  int c = grp;
+#pragma unroll
+  for (int k = 0; k < kAheadRows; ++k) {
+    const int c = grp + k * kMergeGroups;
+    if (c < nc) add(x0[k], s_w[c]);
+  }
+  int c = grp + kAheadRows * kMergeGroups;
   for (; c + 3 * kMergeGroups < nc; c += 4 * kMergeGroups) {
     u32x4 x[4];
 #pragma unroll
