@@ -12,7 +12,8 @@
 // Block = (b, u, head, 32 columns); 32 groups of 8 threads take every 32nd
 // chunk, a thread 4 columns (16 columns per block left half the groups idle
 // at 32 chunks: 7% slower at head_dim 256); the first chunk rows and every chunk's (m, l)
-// are loaded at once, before the weights are formed.  The decode kernels
+// are loaded at once, before the weights are formed; the groups' sums meet
+// by lane moves inside each wave and one LDS exchange across the waves.  The decode kernels
 // merge in their last workgroup instead when the partials of a sequence are
 // few (see plan_decode).
 #include "kvq_attn.h"
@@ -121,14 +122,20 @@ __global__ __launch_bounds__(kThreads) void gqa_merge_kernel(MergeParams p) {
   }
   for (int c = grp + kAhead * kGroups; c < nc; c += kGroups)
     v += s_w[c] * *reinterpret_cast<const f32x4*>(src + (int64_t)c * cstride);
-  s_red[grp][j] = v;
-  __syncthreads();
-  for (int half = kGroups / 2; half >= 1; half >>= 1) {
-    if (grp < half) s_red[grp][j] += s_red[grp + half][j];
-    __syncthreads();
+  // the groups' sums: the 8 groups of a wave (lanes j, j + 8, ..., j + 56)
+  // by a DPP row rotation and the two permlane swaps, then the 4 waves
+  // through LDS (one barrier)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float x = v[q];
+    x += dpp<kRowRor<8>>(x);
+    x = sum_xor32(sum_xor16(x));
+    v[q] = x;
   }
+  if (lane < kLanesPerRow) s_red[tid >> 6][lane] = v;
+  __syncthreads();
   if (tid < kLanesPerRow) {
-    const f32x4 t = s_red[0][tid];
+    const f32x4 t = s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
     const float Ls = s_L;
     const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
     uint16_t* o = a.out + orow * p.D + dchunk * kCols + 4 * tid;
