@@ -152,9 +152,13 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   constexpr int ESZ = Gm::ESZ, NKS = Gm::NKS, NT = Gm::NT, VDW = Gm::VDW, KLD = Gm::KLD;
   constexpr int CODE = Gm::CODE, SCL = Gm::SCL;
   using Raw = PageRaw<QT, D>;
-  // page buffers per wave: NBUF pages' loads in flight while one is computed
-  // (two, so that two waves fit each SIMD at head_dim 256)
-  constexpr int NBUF = 2;
+  // page buffers per wave: NBUF pages' loads in flight while one is computed.
+  // The decode runs one work item per compute unit, so one wave per SIMD:
+  // three buffers (up to 256 VGPRs) keep more bytes in flight (57.0 against
+  // 58.7 us per call for 262144 tokens at head_dim 256, 37.9 against 41.8
+  // for 8 ragged contexts; four were slower than two).  Extend attention
+  // keeps two, so that two waves of its two-tile items fit each SIMD.
+  constexpr int NBUF = EXT ? 2 : 3;
   extern __shared__ int s_prefix[];  // [batch + 1]
   // per-wave (m, l) and O^T accumulators at the end of an item, or the merge's
   // chunk weights
