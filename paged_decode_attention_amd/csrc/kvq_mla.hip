@@ -335,19 +335,9 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
     };
 
     // this wave's 32 query heads as MFMA B operands: qr[ht][ks] holds, for
-    // head 32w + 16ht + (l%16), elements 32ks + 8(l/16) .. +7
+    // head 32w + 16ht + (l%16), elements 32ks + 8(l/16) .. +7 (loaded below,
+    // after the first tile's codes)
     u32x4 qr[2][kNB];
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const int h = 32 * wave + 16 * ht + n16;
-      const uint16_t* qrow = a.q + (orow * Hq + (h < Hq ? h : 0)) * kDqk + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < kNB; ++ks) {
-        u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
-        if (h >= Hq) v = u32x4{0, 0, 0, 0};
-        qr[ht][ks] = v;
-      }
-    }
 
     auto load_tile = [&](int j, MlaRaw<QT>& R) {
       const int t = opaque(tid);
@@ -557,7 +547,23 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
       }
     };
 
+    // The first tile's codes are requested before the query: the query (147
+    // KB per workgroup) takes the longest to arrive, and the first tile is
+    // dequantized while it does.
     MlaRaw<QT> R;
+    load_tile(0, R);
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const int h = 32 * wave + 16 * ht + n16;
+      const uint16_t* qrow = a.q + (orow * Hq + (h < Hq ? h : 0)) * kDqk + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < kNB; ++ks) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
+        if (h >= Hq) v = u32x4{0, 0, 0, 0};
+        qr[ht][ks] = v;
+      }
+    }
+    bool again = false;
     while (true) {  // passes over the item (a second one only after a restart)
 #pragma unroll
       for (int dt = 0; dt < kDv / 16; ++dt) {
@@ -565,7 +571,8 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
         acc[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       lsum[0] = lsum[1] = 0.0f;
-      load_tile(0, R);
+      if (again) load_tile(0, R);
+      again = true;
       __syncthreads();  // earlier reads of both buffers and of the votes are done
       if (tid < 3) s_flag[tid] = 0;
       store_begin(0, R, 0);
