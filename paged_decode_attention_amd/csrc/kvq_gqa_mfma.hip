@@ -163,7 +163,10 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   // per-wave (m, l) and O^T accumulators at the end of an item, or the merge's
   // chunk weights
   constexpr int kC = kN * TN;  // columns of a unit
-  constexpr int kRed = (kW * kC * D > kMergeMaxWeights) ? kW * kC * D : kMergeMaxWeights;
+  // (rows of the combine are D + 1 floats apart: the 16 lanes of a column
+  // group write one element of 16 different rows, on 16 different banks)
+  constexpr int kRow = D + 1;
+  constexpr int kRed = (kW * kC * kRow > kMergeMaxWeights) ? kW * kC * kRow : kMergeMaxWeights;
   __shared__ float s_red[kRed];
   __shared__ float s_ml[kW][kC][2];
   __shared__ float s_hm[kC][2];
@@ -555,7 +558,7 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     // LDS column t kN + n16 (= the unit's column: gt = 16 whenever TN > 1)
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      float* dst = s_red + (wave * kC + t * kN + n16) * D;
+      float* dst = s_red + (wave * kC + t * kN + n16) * kRow;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -582,7 +585,7 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
       const float M = s_hm[h][0];
       float v = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kW; ++w) v += exp2_rel(s_ml[w][h][0], M) * s_red[(w * kC + h) * D + d];
+      for (int w = 0; w < kW; ++w) v += exp2_rel(s_ml[w][h][0], M) * s_red[(w * kC + h) * kRow + d];
       if (nc == 1) {
         const float Ls = s_hm[h][1];
         const int64_t orow = EXT ? query_row(a, b, kvh, col0 + h, G)
