@@ -340,8 +340,11 @@ int kvq_sparse_mla_decode(kvq_dtype dtype, const void* q, const void* slab,
 
 /* Workspace bytes kvq_extend_attention needs (the split-K partials and
  * counters of the matrix-core kernel over max_new_tokens x G query rows per
- * kv head).  0 if the shapes are invalid (see kvq_extend_attention).
- * Host-only. */
+ * kv head).  When the batch's query-row tiles alone give every resident
+ * workgroup several work items (long prefill: batch x n_kv_heads x tile
+ * groups >= 2048), each tile group attends to its whole sequence in one work
+ * item and the workspace holds no partials (a few KB).  0 if the shapes are
+ * invalid (see kvq_extend_attention).  Host-only. */
 size_t kvq_extend_attention_workspace_bytes(kvq_dtype dtype, int batch, int n_q_heads,
                                             int n_kv_heads, int head_dim, int page_size,
                                             int max_pages, int max_new_tokens);

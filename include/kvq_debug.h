@@ -32,7 +32,8 @@ int kvq_debug_e4m3_encode_range(uint32_t first_bits, int64_t count, uint8_t* out
  * columns per tile, tiles per work item, head groups per kv head, pages per
  * item step, fewest pages per item, most pages per item, target item count,
  * upper bound on items, workspace bytes, pages per item (the slab), merge
- * inside the decode kernel (0/1), matrix-core kernel (0/1).  max_new_tokens
+ * inside the decode kernel (0/1), matrix-core kernel (0/1), extend items
+ * over whole sequences with no split-K partials (0/1).  max_new_tokens
  * > 0 plans kvq_extend_attention over separate pools.  Returns the number of
  * values written, or KVQ_ERR_UNSUPPORTED for shapes the planner refuses. */
 int kvq_debug_decode_plan(kvq_dtype dtype, int batch, int n_q_heads, int n_kv_heads,

@@ -364,6 +364,7 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
     // one item per CU; extend attention (many more query rows) two
     const int64_t target = (p.mfma && ext_new > 0 ? 2 : 1) * (int64_t)kPlanCUs;
     const int cap = kMaxItemPages / step * step;
+    // The split plan: items of at most `cap` pages, at least `min_pages`.
     const int64_t for_merge =
         ((int64_t)max_pages * p.gt * p.tn + kMergeMaxWeights - 1) / kMergeMaxWeights;
     int64_t min_pages = ((for_merge > step ? for_merge : step) + step - 1) / step * step;
@@ -374,31 +375,56 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
     while (min_pages <= cap &&
            (max_pages + min_pages - 1) / min_pages * p.gt * p.tn > kMergeMaxWeights)
       min_pages += step;
-    if (min_pages > cap) return no("max_pages %d is too large for the split-K merge", max_pages);
-    p.step = step;
-    p.min_pages = (int)min_pages;
-    p.cap_pages = cap;
-    p.target = (int)target;
-    p.item_pages = (int)min_pages;
+    const bool split_ok = min_pages <= cap;
     // items: at most work / item_pages + one partial item per (sequence, unit);
     // item_pages >= work / target unless capped, and >= min_pages always
-    const int64_t by_min = units * ((max_pages + min_pages - 1) / min_pages);
-    int64_t by_target = ((int64_t)batch * max_pages * seq_units + cap - 1) / cap;
-    if (by_target < target) by_target = target;
-    by_target += units;
-    p.max_items = by_min < by_target ? by_min : by_target;
-    // chunks of one sequence: at most max_pages / min_pages, and at most
-    // about target / seq_units unless the item size is capped
-    int64_t chunks = (max_pages + cap - 1) / cap;
-    if (chunks < target / seq_units + 1) chunks = target / seq_units + 1;
-    if (chunks > (max_pages + min_pages - 1) / min_pages) chunks = (max_pages + min_pages - 1) / min_pages;
-    // the last workgroup merges a sequence's partials itself while they are
-    // small; beyond that a merge kernel spreads the reads over the GPU
-    // (extend attention: many tiles per sequence, so items rarely split; a
-    // merge kernel would launch a block per output row only to find one
-    // chunk)
-    p.fused_merge = ext_new > 0 || head_dim_v < 64 ||
-                    chunks * p.gt * head_dim_v * (int64_t)sizeof(float) <= kFusedMergeMaxBytes;
+    int64_t split_items = 0;
+    if (split_ok) {
+      const int64_t by_min = units * ((max_pages + min_pages - 1) / min_pages);
+      int64_t by_target = ((int64_t)batch * max_pages * seq_units + cap - 1) / cap;
+      if (by_target < target) by_target = target;
+      by_target += units;
+      split_items = by_min < by_target ? by_min : by_target;
+    }
+    const double split_partials =
+        (double)split_items * p.gt * p.tn * (2 + head_dim_v) * sizeof(float);
+    if (ext_new > 0 && units >= kWholeUnitsPerWorkgroup * target &&
+        (!split_ok || split_partials > (double)kWholeMinPartialBytes)) {
+      // Long prefill whose split-K partials would be huge: each (sequence,
+      // unit) is one item over the whole sequence (the kernel streams it in
+      // sub-chunks of kMaxItemPages), so nothing splits and the workspace
+      // holds no partials.  (Slower than the split plan where both fit:
+      // 1892 against 1428 us for 512 new tokens of 8 x 16384.)
+      const int whole = (int)((max_pages + step - 1) / step * step);
+      p.whole = true;
+      p.step = step;
+      p.min_pages = whole;
+      p.cap_pages = whole;
+      p.target = (int)target;
+      p.item_pages = whole;
+      p.max_items = units;
+      p.fused_merge = true;
+    } else {
+      if (!split_ok) return no("max_pages %d is too large for the split-K merge", max_pages);
+      p.step = step;
+      p.min_pages = (int)min_pages;
+      p.cap_pages = cap;
+      p.target = (int)target;
+      p.item_pages = (int)min_pages;
+      p.max_items = split_items;
+      // chunks of one sequence: at most max_pages / min_pages, and at most
+      // about target / seq_units unless the item size is capped
+      int64_t chunks = (max_pages + cap - 1) / cap;
+      if (chunks < target / seq_units + 1) chunks = target / seq_units + 1;
+      if (chunks > (max_pages + min_pages - 1) / min_pages) chunks = (max_pages + min_pages - 1) / min_pages;
+      // the last workgroup merges a sequence's partials itself while they are
+      // small; beyond that a merge kernel spreads the reads over the GPU
+      // (extend attention: many tiles per sequence, so items rarely split; a
+      // merge kernel would launch a block per output row only to find one
+      // chunk)
+      p.fused_merge = ext_new > 0 || head_dim_v < 64 ||
+                      chunks * p.gt * head_dim_v * (int64_t)sizeof(float) <= kFusedMergeMaxBytes;
+    }
   } else {
     return no("head_dim %d/%d is not supported (separate K/V: 32, 64, 128 or 256 with equal "
               "K and V widths; shared slab: 576/512 with one kv head)",
@@ -408,10 +434,12 @@ bool plan_decode(int qtype, int batch, int n_q_heads, int n_kv_heads, int head_d
   p.off_prefix = 0;
   p.off_count = align256((size_t)(batch + 1) * sizeof(int));
   p.off_ml = p.off_count + align256((size_t)batch * n_kv_heads * p.n_hg * sizeof(int));
-  p.off_acc = p.off_ml + align256((size_t)p.max_items * p.gt * p.tn * 2 * sizeof(float));
+  // split-K partials (none when no item splits)
+  const size_t parts = p.whole ? 0 : (size_t)p.max_items;
+  p.off_acc = p.off_ml + align256(parts * p.gt * p.tn * 2 * sizeof(float));
   // split-K partial outputs: fp32 accumulators (GQA) or bf16 normalized rows (MLA)
   const size_t acc_elem = (p.kind == DK_MLA) ? sizeof(uint16_t) : sizeof(float);
-  p.bytes = p.off_acc + align256((size_t)p.max_items * p.gt * p.tn * head_dim_v * acc_elem);
+  p.bytes = p.off_acc + align256(parts * p.gt * p.tn * head_dim_v * acc_elem);
   *plan = p;
   return true;
 }
@@ -835,7 +863,7 @@ int kvq_debug_decode_plan(kvq_dtype dtype, int batch, int n_q_heads, int n_kv_he
     return fail(KVQ_ERR_UNSUPPORTED, "kvq_debug_decode_plan: %s", why);
   const int64_t v[] = {p.kind, p.gt, p.tn, p.n_hg, p.step, p.min_pages, p.cap_pages, p.target,
                        p.max_items, (int64_t)p.bytes, p.item_pages, p.fused_merge ? 1 : 0,
-                       p.mfma ? 1 : 0};
+                       p.mfma ? 1 : 0, p.whole ? 1 : 0};
   const int n = (int)(sizeof v / sizeof v[0]);
   int k = 0;
   for (; out && k < n_out && k < n; ++k) out[k] = v[k];

@@ -79,6 +79,7 @@ struct MfParams {
   int tn;            // column tiles per unit (every wave computes each over its pages)
   ItemRule rule;     // work item size (see plan_items)
   int fused;         // merge split-K partials in the last workgroup (else a merge kernel)
+  int whole;         // extend: items over whole sequences, streamed in sub-chunks
   float scale_log2;  // sm_scale * log2(e)
   int* prefix;       // [batch + 1]
   int* count;        // [batch * units] arrival counters, zero between calls
@@ -146,7 +147,7 @@ __device__ __forceinline__ void transpose4x4(const uint32_t* in, uint32_t* out) 
 // TN: 16-column tiles per unit.  With TN = 2 every wave computes both tiles
 // over its pages, so a page's loads and V dequantization serve 32 query rows
 // (used with full tiles only: gt = 16, so a unit's column h is LDS column h).
-template <int QT, int D, bool EXT, int TN>
+template <int QT, int D, bool EXT, int TN, bool SUB>
 __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   using Gm = MfGeo<QT, D>;
   constexpr int ESZ = Gm::ESZ, NKS = Gm::NKS, NT = Gm::NT, VDW = Gm::VDW, KLD = Gm::KLD;
@@ -229,9 +230,14 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     const int hg = EXT ? u / a.n_kv_heads : u - kvh * p.n_hg;
     const int L = clamped_len(a, b);
     const int nc = (L + item_tokens - 1) / item_tokens;
-    const int t0 = chunk * item_tokens;
-    const int nt = min(item_tokens, L - t0);
-    const int np = (nt + kPageSize - 1) / kPageSize;
+    const int t_item = chunk * item_tokens;
+    const int nt_item = min(item_tokens, L - t_item);
+    // SUB: an extend item may span more pages than a wave's page-id list
+    // holds (a whole sequence per item, see plan_decode); it is streamed in
+    // sub-chunks of at most kMaxItemPages pages, carrying the softmax state
+    // across them.  Otherwise an item is one sub-chunk.
+    constexpr int kSubTokens = kMaxItemPages * kPageSize;
+    const int nsub = SUB ? (nt_item + kSubTokens - 1) / kSubTokens : 1;
     // extend attention: a tile of query rows past the sequence's new tokens
     // has nothing to compute or write (uniform over the block; every chunk
     // of the tile skips, so its split-K counter stays untouched)
@@ -240,35 +246,47 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     // this lane's query rows (one per tile) and the item tokens each may attend
     // to (the decode's: the item's own tokens, a wave-uniform bound)
     int64_t qrow_lane[TN];
-    int col_lim[TN];
+    int col_end[TN];  // the item's tokens each column may attend to, from t_item
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const int col = col0 + t * GT + n16;
       qrow_lane[t] = (n16 < GT) ? (EXT ? query_row(a, b, kvh, col, G)
                                        : (int64_t)b * a.n_q_heads + kvh * G + col)
                                 : -1;
-      col_lim[t] = nt;
+      col_end[t] = nt_item;
       if constexpr (EXT)
-        col_lim[t] = (n16 < GT) ? max(min(nt, query_end(a, b, L, col, G) - t0), 0) : 0;
+        col_end[t] = (n16 < GT) ? max(min(nt_item, query_end(a, b, L, col, G) - t_item), 0) : 0;
     }
-    const int nsteps = (np > wave) ? (np - wave + kW - 1) / kW : 0;  // pages of this wave
 
-    // page ids of this wave's steps: lane k holds the id of step k (page
-    // wave + 4k of the item; at most 64 steps), -1 when masked or absent
-    int pids = -1;
-    if (lane < nsteps) {
-      const int pi = wave + lane * kW;
-      const int v = a.page_table[(int64_t)b * a.pt_stride + t0 / kPageSize + pi];
-      pids = (v >= 0 && (int64_t)v < a.num_pages) ? v : -1;
-    }
+    // The current sub-chunk: its first token t0, its tokens nt, each
+    // column's limit within it, this wave's steps, and their page ids (lane
+    // k holds the id of step k: page wave + 4k of the sub-chunk, at most 64
+    // steps; -1 when masked or absent).  The stream runs a whole number of
+    // NBUF-step rounds (at least one), so every path through it issues the
+    // same loads.
+    int t0, nt, nsteps, nst, pids;
+    int col_lim[TN];
+    auto set_sub = [&](int sub) {
+      t0 = t_item + sub * kSubTokens;
+      nt = min(kSubTokens, nt_item - sub * kSubTokens);
+      const int np = (nt + kPageSize - 1) / kPageSize;
+#pragma unroll
+      for (int t = 0; t < TN; ++t) col_lim[t] = min(max(col_end[t] - sub * kSubTokens, 0), nt);
+      nsteps = (np > wave) ? (np - wave + kW - 1) / kW : 0;  // pages of this wave
+      nst = max((nsteps + NBUF - 1) / NBUF * NBUF, NBUF);
+      pids = -1;
+      if (lane < nsteps) {
+        const int pi = wave + lane * kW;
+        const int v = a.page_table[(int64_t)b * a.pt_stride + t0 / kPageSize + pi];
+        pids = (v >= 0 && (int64_t)v < a.num_pages) ? v : -1;
+      }
+    };
+    set_sub(0);
     // padded steps past the wave's pages are masked (id -1)
     auto pid_of = [&](int st) {
       const int v = __builtin_amdgcn_readlane(pids, min(st, 63));
       return st < nsteps ? v : -1;
     };
-    // the stream runs a whole number of NBUF-step rounds (at least one), so
-    // every path through it issues the same loads
-    const int nst = max((nsteps + NBUF - 1) / NBUF * NBUF, NBUF);
 
     // Q^T operands: qb[t][ks] = the query row of column n16 of tile t,
     // elements 32ks + 8g .. +7 (0 for padding columns)
@@ -505,34 +523,39 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     Raw R[NBUF];
     float M[TN];  // largest score of column n16 of each tile over the wave's pages
     for (int pass = 0;; ++pass) {
+      for (int sub = 0; sub < nsub; ++sub) {
+        if (sub > 0 || (pass > 0 && nsub > 1)) set_sub(sub);
 #pragma unroll
-      for (int k = 0; k < NBUF; ++k) load_page(pid_of(k), R[k]);
-      if (pass == 0) {
-        float s0[TN][4];
-        bool ok0[4];
-        scores(0, pid_of(0), R[0], s0, ok0);
+        for (int k = 0; k < NBUF; ++k) load_page(pid_of(k), R[k]);
+        if (pass == 0 && sub == 0) {
+          float s0[TN][4];
+          bool ok0[4];
+          scores(0, pid_of(0), R[0], s0, ok0);
 #pragma unroll
-        for (int t = 0; t < TN; ++t) {
-          float x = fmaxf(fmaxf(s0[t][0], s0[t][1]), fmaxf(s0[t][2], s0[t][3]));
-          x = max_xor32(max_xor16(x));
-          mref[t] = (x == -INFINITY) ? 0.0f : x;
+          for (int t = 0; t < TN; ++t) {
+            float x = fmaxf(fmaxf(s0[t][0], s0[t][1]), fmaxf(s0[t][2], s0[t][3]));
+            x = max_xor32(max_xor16(x));
+            mref[t] = (x == -INFINITY) ? 0.0f : x;
+          }
         }
-      }
+        if (sub == 0) {
 #pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        lsum[t] = 0.0f;
-        smax[t] = -INFINITY;
+          for (int t = 0; t < TN; ++t) {
+            lsum[t] = 0.0f;
+            smax[t] = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < NT; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      for (int st = 0; st < nst; st += NBUF) {
+            for (int i = 0; i < NT; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+        for (int st = 0; st < nst; st += NBUF) {
 #pragma unroll
-        for (int k = 0; k < NBUF; ++k) {
-          float s[TN][4];
-          bool ok[4];
-          scores(st + k, pid_of(st + k), R[k], s, ok);
-          accumulate(R[k], s, ok);
-          load_page(pid_of(st + k + NBUF), R[k]);
+          for (int k = 0; k < NBUF; ++k) {
+            float s[TN][4];
+            bool ok[4];
+            scores(st + k, pid_of(st + k), R[k], s, ok);
+            accumulate(R[k], s, ok);
+            load_page(pid_of(st + k + NBUF), R[k]);
+          }
         }
       }
       bool redo = false;
@@ -681,12 +704,17 @@ template <int QT, int D>
 hipError_t launch_d(const MfParams& mp, int grid, hipStream_t s) {
   const size_t dyn = (size_t)(mp.a.batch + 1) * sizeof(int);
   if (mp.a.q_start && mp.tn == 2) {
-    if constexpr (D <= 128) gqa_mfma_kernel<QT, D, true, 2><<<grid, kT, dyn, s>>>(mp);
-    else return hipErrorInvalidValue;  // the planner uses two tiles only up to head_dim 128
+    if constexpr (D <= 128) {
+      if (mp.whole) gqa_mfma_kernel<QT, D, true, 2, true><<<grid, kT, dyn, s>>>(mp);
+      else gqa_mfma_kernel<QT, D, true, 2, false><<<grid, kT, dyn, s>>>(mp);
+    } else {
+      return hipErrorInvalidValue;  // the planner uses two tiles only up to head_dim 128
+    }
   } else if (mp.a.q_start) {
-    gqa_mfma_kernel<QT, D, true, 1><<<grid, kT, dyn, s>>>(mp);
+    if (mp.whole) gqa_mfma_kernel<QT, D, true, 1, true><<<grid, kT, dyn, s>>>(mp);
+    else gqa_mfma_kernel<QT, D, true, 1, false><<<grid, kT, dyn, s>>>(mp);
   } else {
-    gqa_mfma_kernel<QT, D, false, 1><<<grid, kT, dyn, s>>>(mp);
+    gqa_mfma_kernel<QT, D, false, 1, false><<<grid, kT, dyn, s>>>(mp);
   }
   return hipGetLastError();
 }
@@ -712,6 +740,7 @@ hipError_t launch_gqa_mfma_decode(const DecodeArgs& a, const DecodePlan& plan, i
   mp.tn = plan.tn;
   mp.rule = ItemRule{plan.step, plan.min_pages, plan.cap_pages, plan.target};
   mp.fused = plan.fused_merge ? 1 : 0;
+  mp.whole = plan.whole ? 1 : 0;
   mp.scale_log2 = a.sm_scale * kLog2e;
   mp.prefix = reinterpret_cast<int*>(ws + plan.off_prefix);
   mp.count = reinterpret_cast<int*>(ws + plan.off_count);

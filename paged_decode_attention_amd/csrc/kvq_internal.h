@@ -33,6 +33,13 @@ constexpr int kMaxItemPages = 256;
 // partials itself when they hold at most this many bytes; otherwise a
 // separate merge kernel runs.
 constexpr int kFusedMergeMaxBytes = 64 * 1024;
+// Extend attention takes one work item per (sequence, kv head, tile group)
+// over the whole sequence when there are at least kWholeUnitsPerWorkgroup
+// such units per resident workgroup (every workgroup then has several items
+// and nothing needs splitting) and the split plan's partials would exceed
+// kWholeMinPartialBytes.
+constexpr int kWholeUnitsPerWorkgroup = 4;
+constexpr int64_t kWholeMinPartialBytes = (int64_t)1 << 30;
 // Chunk weights the merge keeps in LDS: chunks * heads per item.
 constexpr int kMergeMaxWeights = 4096;
 
@@ -116,6 +123,8 @@ struct DecodePlan {
   int step, min_pages, cap_pages, target;
   bool fused_merge;   // merge inside the split kernel (else a merge kernel)
   bool mfma;          // GQA: wide query groups on the matrix-core kernel
+  bool whole;         // extend: one item per (sequence, unit) over the whole
+                      // sequence (no split-K partials in the workspace)
   int64_t max_items;  // upper bound on work items (sizes the workspace)
   size_t off_prefix, off_count, off_ml, off_acc, bytes;  // workspace layout
 };

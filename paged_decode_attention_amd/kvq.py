@@ -92,7 +92,7 @@ EXPORTS = ("kvq_pool_bytes", "kvq_store", "kvq_dequant", "kvq_paged_decode_works
 # the test exports (kvq_debug.h)
 DEBUG_EXPORTS = ("kvq_debug_e4m3_encode_range", "kvq_debug_decode_plan")
 PLAN_FIELDS = ("kind", "gt", "tn", "n_hg", "step", "min_pages", "cap_pages", "target",
-               "max_items", "bytes", "item_pages", "fused_merge", "mfma")
+               "max_items", "bytes", "item_pages", "fused_merge", "mfma", "whole")
 
 
 def last_error() -> str:

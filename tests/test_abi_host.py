@@ -261,3 +261,27 @@ def test_in_kernel_merge_weights_fit_in_lds():
                         assert p["min_pages"] <= p["cap_pages"]
     assert checked > 1000
 
+
+
+def test_extend_long_prefill_plans_whole_sequences():
+    """Extend attention with many query-row tiles (long prefill): once the
+    (sequence, kv head, tile group) units reach four per resident workgroup
+    (2048) and the split plan's partials would pass 1 GiB, each unit is one
+    work item over its whole sequence, so nothing is split and the workspace
+    holds no partials; otherwise sequences split (faster where both fit) and
+    the workspace holds a partial row per item and column."""
+    # 8 sequences x 8 kv heads x ceil(new x 2 / 32) tile groups (head_dim 128, G = 2)
+    for new, whole in ((64, False), (512, False), (2048, False), (4096, True)):
+        p = kvq.debug_plan("fp8_e4m3", 8, 16, 8, 128, 128, 1024, new)
+        units = 8 * 8 * -(-new * 2 // 32)
+        assert units >= 2048 or not p["whole"]
+        assert bool(p["whole"]) == whole, (new, p)
+        ws = kvq.extend_workspace_bytes("fp8_e4m3", 8, 16, 8, 128, 16, 1024, new)
+        assert ws == p["bytes"]
+        if whole:
+            assert p["max_items"] == units and p["min_pages"] >= 1024
+            assert ws < 128 * 1024, ws
+        else:
+            assert ws > 1 << 20, ws
+    # the decode never plans whole sequences
+    assert not kvq.debug_plan("fp8_e4m3", 64, 16, 2, 256, 256, 4096)["whole"]

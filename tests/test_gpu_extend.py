@@ -223,3 +223,37 @@ def test_extend_over_the_mla_slab(qtype):
     assert np.abs(gl[fin] - ol[fin]).max() < 1e-2
     s2 = int(q_start[2])  # 5 new tokens, 3 in the pool: the first 2 see nothing
     assert np.all(g[s2 * 64:(s2 + 2) * 64] == 0)
+
+
+def long_prefill_workload(Hq, Hkv, D, seed, lens, width):
+    return ext_workload(Hq, Hkv, D, lens, width, seed=seed, mask_frac=0.03)
+
+
+# A long-prefill plan: max_new_tokens 4096 gives so many (sequence, kv head,
+# tile group) units that the split plan's partials would pass 1 GiB, so each
+# unit is one work item over its whole sequence (streamed in sub-chunks of
+# 256 pages).  The sequences list fewer new tokens than that (the other tiles
+# have no rows), so the oracle stays cheap; two of them reach 16384 and 9000
+# tokens (4 and 3 sub-chunks), one has its new tokens on both sides of the
+# 4096-token sub-chunk boundary.
+LONG_LENS = [16384, 9000, 4200, 300, 1000, 77, 4096, 2500]
+LONG_NEWS = [40, 17, 200, 300, 33, 77, 9, 64]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(16, 8, 128), (16, 2, 256)])
+def test_extend_long_prefill_whole_sequences(Hq, Hkv, D):
+    """Whole-sequence work items, no split-K partials in the workspace;
+    every row against the oracle."""
+    wl = long_prefill_workload(Hq, Hkv, D, 4096 + D, LONG_LENS, 1030)
+    plan = kvq().debug_plan("fp8_e4m3", wl.batch, Hq, Hkv, D, D, wl.max_pages, 4096)
+    assert plan["whole"] and plan["bytes"] < 1 << 20
+    run(wl, "fp8_e4m3", LONG_NEWS, max_new=4096)
+
+
+def test_extend_long_prefill_scores_hundreds_of_nats_apart():
+    """Whole-sequence items with queries scaled by 150: the largest score of
+    an item can sit in a later sub-chunk, hundreds of nats above the first
+    page's, and the item is streamed again over all its sub-chunks."""
+    wl = long_prefill_workload(16, 8, 128, 4097, LONG_LENS, 1030)
+    *_, o_lse = run(wl, "fp8_e4m3", LONG_NEWS, max_new=4096, q_scale=150.0)
+    assert np.nanmax(o_lse) > 300.0
