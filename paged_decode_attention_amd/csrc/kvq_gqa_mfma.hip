@@ -231,13 +231,12 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
     const int L = clamped_len(a, b);
     const int nc = (L + item_tokens - 1) / item_tokens;
     const int t_item = chunk * item_tokens;
-    const int nt_item = min(item_tokens, L - t_item);
+    int nt_item = min(item_tokens, L - t_item);
     // SUB: an extend item may span more pages than a wave's page-id list
     // holds (a whole sequence per item, see plan_decode); it is streamed in
     // sub-chunks of at most kMaxItemPages pages, carrying the softmax state
     // across them.  Otherwise an item is one sub-chunk.
     constexpr int kSubTokens = kMaxItemPages * kPageSize;
-    const int nsub = SUB ? (nt_item + kSubTokens - 1) / kSubTokens : 1;
     // extend attention: a tile of query rows past the sequence's new tokens
     // has nothing to compute or write (uniform over the block; every chunk
     // of the tile skips, so its split-K counter stays untouched)
@@ -257,6 +256,18 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
       if constexpr (EXT)
         col_end[t] = (n16 < GT) ? max(min(nt_item, query_end(a, b, L, col, G) - t_item), 0) : 0;
     }
+    if constexpr (EXT) {
+      // the item's tokens past every column's causal end are not streamed
+      // (in a prefill, a tile near the start attends to a few pages only); an
+      // item left with none still takes part in its unit's merge
+      int e = col_end[0];
+#pragma unroll
+      for (int t = 1; t < TN; ++t) e = max(e, col_end[t]);
+      // (token counts are exact in fp32)
+      const float ef = stride_max<1>((float)e);
+      nt_item = min(nt_item, (int)__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(ef))));
+    }
+    const int nsub = SUB ? max((nt_item + kSubTokens - 1) / kSubTokens, 1) : 1;
 
     // The current sub-chunk: its first token t0, its tokens nt, each
     // column's limit within it, this wave's steps, and their page ids (lane
