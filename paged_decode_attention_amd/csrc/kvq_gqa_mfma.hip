@@ -47,6 +47,7 @@ namespace {
 constexpr int kW = kDecodeWaves;
 constexpr int kT = 64 * kW;
 constexpr int kN = 16;  // query rows (heads, or new tokens x heads) per MFMA column tile
+constexpr int kSharedTileGroups = 4;  // see launch_d
 
 // Lane j of each row of 16 lanes, to every lane of the row (DPP row_newbcast).
 // j is a constant once the callers' loops are unrolled; the switch folds.
@@ -147,7 +148,10 @@ __device__ __forceinline__ void transpose4x4(const uint32_t* in, uint32_t* out) 
 // TN: 16-column tiles per unit.  With TN = 2 every wave computes both tiles
 // over its pages, so a page's loads and V dequantization serve 32 query rows
 // (used with full tiles only: gt = 16, so a unit's column h is LDS column h).
-template <int QT, int D, bool EXT, int TN, bool SUB>
+// POL: the cache policy of the K/V loads -- non-temporal where each page is
+// read by one work item (the decode; extend with few tile groups per kv
+// head), the default where several items read it and can meet it in the L2.
+template <int QT, int D, bool EXT, int TN, bool SUB, int POL>
 __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   using Gm = MfGeo<QT, D>;
   constexpr int ESZ = Gm::ESZ, NKS = Gm::NKS, NT = Gm::NT, VDW = Gm::VDW, KLD = Gm::KLD;
@@ -336,9 +340,9 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
       const auto rk = page_rsrc(a.k_pool + row0 * D * ESZ, code_bytes);
       const auto rv = page_rsrc(a.v_pool + row0 * D * ESZ, code_bytes);
 #pragma unroll
-      for (int m = 0; m < KLD; ++m) bload<4, kNonTemporal>(rk, koff + 64 * m, R.k[m]);
+      for (int m = 0; m < KLD; ++m) bload<4, POL>(rk, koff + 64 * m, R.k[m]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) bload<VDW, kNonTemporal>(rv, voff + r * D * ESZ, R.v[r]);
+      for (int r = 0; r < 4; ++r) bload<VDW, POL>(rv, voff + r * D * ESZ, R.v[r]);
       if constexpr (qt_scaled(QT)) {
         const auto rks = page_rsrc(a.k_scales + row0 * NKS, pid >= 0 ? SCL : 0);
         const auto rvs = page_rsrc(a.v_scales + row0 * NKS, pid >= 0 ? SCL : 0);
@@ -714,18 +718,28 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
 template <int QT, int D>
 hipError_t launch_d(const MfParams& mp, int grid, hipStream_t s) {
   const size_t dyn = (size_t)(mp.a.batch + 1) * sizeof(int);
+  // Extend: with at least kSharedTileGroups tile groups per kv head, every
+  // page is read by that many work items on one XCD, and loads with the
+  // default policy let them meet it in the L2 (64 new tokens, 4 groups:
+  // 209 against 225 us, HBM traffic 1.36x instead of 2.08x); with fewer the
+  // non-temporal loads are faster (8 new tokens: 69 against 75 us).  Whole-
+  // sequence items come from long prefills, with many groups.
+  constexpr int NT = kNonTemporal;
+  const bool shared = mp.n_hg >= kSharedTileGroups;
   if (mp.a.q_start && mp.tn == 2) {
     if constexpr (D <= 128) {
-      if (mp.whole) gqa_mfma_kernel<QT, D, true, 2, true><<<grid, kT, dyn, s>>>(mp);
-      else gqa_mfma_kernel<QT, D, true, 2, false><<<grid, kT, dyn, s>>>(mp);
+      if (mp.whole) gqa_mfma_kernel<QT, D, true, 2, true, 0><<<grid, kT, dyn, s>>>(mp);
+      else if (shared) gqa_mfma_kernel<QT, D, true, 2, false, 0><<<grid, kT, dyn, s>>>(mp);
+      else gqa_mfma_kernel<QT, D, true, 2, false, NT><<<grid, kT, dyn, s>>>(mp);
     } else {
       return hipErrorInvalidValue;  // the planner uses two tiles only up to head_dim 128
     }
   } else if (mp.a.q_start) {
-    if (mp.whole) gqa_mfma_kernel<QT, D, true, 1, true><<<grid, kT, dyn, s>>>(mp);
-    else gqa_mfma_kernel<QT, D, true, 1, false><<<grid, kT, dyn, s>>>(mp);
+    if (mp.whole) gqa_mfma_kernel<QT, D, true, 1, true, 0><<<grid, kT, dyn, s>>>(mp);
+    else if (shared) gqa_mfma_kernel<QT, D, true, 1, false, 0><<<grid, kT, dyn, s>>>(mp);
+    else gqa_mfma_kernel<QT, D, true, 1, false, NT><<<grid, kT, dyn, s>>>(mp);
   } else {
-    gqa_mfma_kernel<QT, D, false, 1, false><<<grid, kT, dyn, s>>>(mp);
+    gqa_mfma_kernel<QT, D, false, 1, false, NT><<<grid, kT, dyn, s>>>(mp);
   }
   return hipGetLastError();
 }
