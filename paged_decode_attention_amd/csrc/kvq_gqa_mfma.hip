@@ -721,7 +721,7 @@ hipError_t launch_d(const MfParams& mp, int grid, hipStream_t s) {
   // Extend: with at least kSharedTileGroups tile groups per kv head, every
   // page is read by that many work items on one XCD, and loads with the
   // default policy let them meet it in the L2 (64 new tokens, 4 groups:
-  // 209 against 225 us, HBM traffic 1.36x instead of 2.08x); with fewer the
+  // 207 against 225 us, HBM traffic 1.44x instead of 2.08x); with fewer the
   // non-temporal loads are faster (8 new tokens: 69 against 75 us).  Whole-
   // sequence items come from long prefills, with many groups.
   constexpr int NT = kNonTemporal;
