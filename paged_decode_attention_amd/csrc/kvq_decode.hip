@@ -115,6 +115,8 @@ struct NewRow {
   bool on;        // this lane holds a piece of that row
   Raw<NDW> k, v;  // the piece's codes (bf16 for a bf16 pool)
   float ks, vs;   // its block scales (1 for the types without one)
+  int64_t dst;    // the pool row this lane writes after the stream (-1: none)
+  uint16_t sk, sv;
 };
 
 // Wave-uniform description of one work item.
@@ -533,6 +535,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
     // and row index where this wave meets it, and its codes and scales.
     NewRow<NDW> nr;
     nr.step = -1;
+    nr.dst = -1;
     if constexpr (APP) {
       const int raw = small ? __builtin_amdgcn_readlane(raw_len, bq) : a.seq_lens[bq];
       const int tn = raw - 1;
@@ -549,24 +552,10 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
           nr.ks = qt_scaled(QT) ? f16_bits_to_f32(sb[0]) : 1.0f;
           nr.vs = qt_scaled(QT) ? f16_bits_to_f32(sb[1]) : 1.0f;
           const int P = __builtin_amdgcn_readlane(pid_cur, st * PPS + k);
-          if (P >= 0 && cur.hg == 0 && nr.on) {
-            const int64_t row = ((int64_t)P * a.n_kv_heads + cur.kvh) * kPageSize + r;
-            uint8_t* kp = const_cast<uint8_t*>(a.k_pool) + (row * D + d0) * ESZ;
-            uint8_t* vp = const_cast<uint8_t*>(a.v_pool) + (row * D + d0) * ESZ;
-            if constexpr (NDW == 4) {
-              *reinterpret_cast<uint4*>(kp) = make_uint4(nr.k.w[0], nr.k.w[1], nr.k.w[2], nr.k.w[3]);
-              *reinterpret_cast<uint4*>(vp) = make_uint4(nr.v.w[0], nr.v.w[1], nr.v.w[2], nr.v.w[3]);
-            } else {
-              *reinterpret_cast<uint2*>(kp) = make_uint2(nr.k.w[0], nr.k.w[1]);
-              *reinterpret_cast<uint2*>(vp) = make_uint2(nr.v.w[0], nr.v.w[1]);
-            }
-            if constexpr (qt_scaled(QT)) {
-              if ((seg & (32 / EPL - 1)) == 0) {
-                const_cast<uint16_t*>(a.k_scales)[row * NB + (d0 >> 5)] = sb[0];
-                const_cast<uint16_t*>(a.v_scales)[row * NB + (d0 >> 5)] = sb[1];
-              }
-            }
-          }
+          if (P >= 0 && cur.hg == 0 && nr.on)
+            nr.dst = ((int64_t)P * a.n_kv_heads + cur.kvh) * kPageSize + r;
+          nr.sk = sb[0];
+          nr.sv = sb[1];
         }
       }
     }
@@ -621,6 +610,29 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(GqaParams p) {
       if (!__builtin_amdgcn_ballot_w64(redo)) break;
 #pragma unroll
       for (int h = 0; h < GT; ++h) mref[h] = (M[h] == -INFINITY) ? 0.0f : M[h];
+    }
+    // the new row goes to the pool after the stream (its codes were used from
+    // registers): stores issued earlier would sit in the load counter ahead
+    // of the stream's first steps
+    if constexpr (APP) {
+      if (nr.dst >= 0) {
+        const int64_t row = nr.dst;
+        uint8_t* kp = const_cast<uint8_t*>(a.k_pool) + (row * D + d0) * ESZ;
+        uint8_t* vp = const_cast<uint8_t*>(a.v_pool) + (row * D + d0) * ESZ;
+        if constexpr (NDW == 4) {
+          *reinterpret_cast<uint4*>(kp) = make_uint4(nr.k.w[0], nr.k.w[1], nr.k.w[2], nr.k.w[3]);
+          *reinterpret_cast<uint4*>(vp) = make_uint4(nr.v.w[0], nr.v.w[1], nr.v.w[2], nr.v.w[3]);
+        } else {
+          *reinterpret_cast<uint2*>(kp) = make_uint2(nr.k.w[0], nr.k.w[1]);
+          *reinterpret_cast<uint2*>(vp) = make_uint2(nr.v.w[0], nr.v.w[1]);
+        }
+        if constexpr (qt_scaled(QT)) {
+          if ((seg & (32 / EPL - 1)) == 0) {
+            const_cast<uint16_t*>(a.k_scales)[row * NB + (d0 >> 5)] = nr.sk;
+            const_cast<uint16_t*>(a.v_scales)[row * NB + (d0 >> 5)] = nr.sv;
+          }
+        }
+      }
     }
     // a head with no valid row here contributes nothing to the merges
     float m[GT];
