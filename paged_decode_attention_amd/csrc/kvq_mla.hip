@@ -559,15 +559,29 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
     // dequantized while it does.
     MlaRaw<QT> R;
     load_tile(0, R);
+    {
+      // coalesced: lane L reads 16 bytes of head L / 4 (piece L % 4 of each
+      // 64-byte k span); the fragment lane L needs is held by lane
+      // 4 (L % 16) + L / 16
+      const int src_lane = 4 * n16 + g;
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const int h = 32 * wave + 16 * ht + n16;
-      const uint16_t* qrow = a.q + (orow * Hq + (h < Hq ? h : 0)) * kDqk + 8 * g;
+      for (int ht = 0; ht < 2; ++ht) {
+        const int hl = 32 * wave + 16 * ht + (lane >> 2);
+        const uint16_t* qrow = a.q + (orow * Hq + (hl < Hq ? hl : 0)) * kDqk + 8 * (lane & 3);
 #pragma unroll
-      for (int ks = 0; ks < kNB; ++ks) {
-        u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
-        if (h >= Hq) v = u32x4{0, 0, 0, 0};
-        qr[ht][ks] = v;
+        for (int ks = 0; ks < kNB; ++ks) qr[ht][ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
+      }
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        const bool dead = 32 * wave + 16 * ht + n16 >= Hq;
+#pragma unroll
+        for (int ks = 0; ks < kNB; ++ks) {
+          u32x4 v;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * src_lane, (int)qr[ht][ks][c]);
+          if (dead) v = u32x4{0, 0, 0, 0};
+          qr[ht][ks] = v;
+        }
       }
     }
     bool again = false;
