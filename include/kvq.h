@@ -294,10 +294,10 @@ int kvq_paged_decode_noalloc(kvq_dtype dtype, const void* q, const void* k_pool,
                              int max_pages, int64_t num_pages, float sm_scale, void* out_bf16,
                              float* lse, kvq_stream_t stream);
 
-/* Workspace bytes kvq_sparse_mla_decode needs: the gathered rows of every
- * list (codes and scales), their page table and lengths, and the split-K
- * partials of the slab decode over them.  0 if the shapes are invalid (see
- * kvq_sparse_mla_decode).  Host-only. */
+/* Workspace bytes kvq_sparse_mla_decode needs: the split-K partials of the
+ * slab decode over the lists (each list split into work items of up to 1024
+ * entries).  0 if the shapes are invalid (see kvq_sparse_mla_decode).
+ * Host-only. */
 size_t kvq_sparse_mla_decode_workspace_bytes(kvq_dtype dtype, int batch, int n_q_heads,
                                              int topk);
 
@@ -327,8 +327,8 @@ size_t kvq_sparse_mla_decode_workspace_bytes(kvq_dtype dtype, int batch, int n_q
  *   workspace : device, >= kvq_sparse_mla_decode_workspace_bytes(), 256-byte
  *               aligned; overwritten by every call (no zeroing needed).
  * Supported: topk 1..2048, n_q_heads a multiple of 16 up to 128, batch up to
- * 1024, page_size 16.  The listed rows are gathered into the workspace (codes
- * moved unchanged) and attended to by the slab decode.  Errors: KVQ_ERR_ARG,
+ * 1024, page_size 16.  The slab decode reads the listed rows in place (an
+ * entry not taken is a masked token).  Errors: KVQ_ERR_ARG,
  * KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP; validation completes
  * before any launch. */
 int kvq_sparse_mla_decode(kvq_dtype dtype, const void* q, const void* slab,

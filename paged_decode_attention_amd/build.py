@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
 
 SOURCES = ["kvq_api.cpp", "kvq_store.hip", "kvq_decode.hip", "kvq_gqa_mfma.hip", "kvq_merge.hip", "kvq_mla.hip",
-           "kvq_sparse.hip", "kvq_noalloc.hip"]
+           "kvq_noalloc.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

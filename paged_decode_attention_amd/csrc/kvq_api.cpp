@@ -452,19 +452,15 @@ bool plan_sparse(int qtype, int batch, int n_q_heads, int k, SparseLayout* lay,
     *why = msg;
     return false;
   }
+  // The slab decode plans over the lists as sequences of k entries (k
+  // rounded up to whole pages): item size, item count and the split-K
+  // partials, which are all the workspace holds.
   SparseLayout L{};
   L.kk = (k + kPageSize - 1) / kPageSize * kPageSize;
-  const int gpages = L.kk / kPageSize;
-  if (!plan_decode(qtype, batch, n_q_heads, 1, kMlaDqk, kMlaDv, kPageSize, gpages, &L.dense, why))
+  if (!plan_decode(qtype, batch, n_q_heads, 1, kMlaDqk, kMlaDv, kPageSize, L.kk / kPageSize,
+                   &L.dense, why))
     return false;
-  L.row_bytes = (qtype == KVQ_FP8_DS_MLA) ? kDsmRow : kMlaDqk * (qtype == KVQ_BF16 ? 2 : 1);
-  const size_t rows = (size_t)batch * L.kk;
-  L.off_dense = 0;
-  L.off_slab = align256(L.dense.bytes);
-  L.off_scales = L.off_slab + align256(rows * L.row_bytes);
-  L.off_pt = L.off_scales + align256(scaled(qtype) ? rows * (kMlaDqk / KVQ_BLOCK) * 2 : 0);
-  L.off_len = L.off_pt + align256((size_t)batch * gpages * sizeof(int32_t));
-  L.bytes = L.off_len + align256((size_t)batch * sizeof(int32_t));
+  L.bytes = L.dense.bytes;
   *lay = L;
   return true;
 }
@@ -799,43 +795,29 @@ int kvq_sparse_mla_decode(kvq_dtype dtype, const void* q, const void* slab,
                 lay.bytes, workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256))
     return fail(KVQ_ERR_WORKSPACE, "kvq_sparse_mla_decode: workspace must be 256-byte aligned");
-  kvq::SparseArgs s;
-  s.topk = topk_idx;
-  s.topk_stride = topk_stride;
-  s.k = topk;
-  s.page_table = page_table;
-  s.pt_stride = pt_stride;
-  s.seq_lens = seq_lens;
-  s.max_pages = max_pages;
-  s.num_pages = num_pages;
-  s.slab = static_cast<const uint8_t*>(slab);
-  s.scales = scaled(dtype) ? scales : nullptr;
-  s.workspace = workspace;
-  hipError_t e = kvq::launch_sparse_gather(s, lay, batch, stream);
-  if (e != hipSuccess) return hip_fail(e, "kvq_sparse_mla_decode");
-  char* ws = static_cast<char*>(workspace);
-  const int gpages = lay.kk / kvq::kPageSize;
   kvq::DecodeArgs a;
   a.qtype = dtype;
   a.q = static_cast<const uint16_t*>(q);
-  a.k_pool = a.v_pool = reinterpret_cast<const uint8_t*>(ws + lay.off_slab);
-  a.k_scales = a.v_scales = scaled(dtype) ? reinterpret_cast<const uint16_t*>(ws + lay.off_scales)
-                                          : nullptr;
-  a.page_table = reinterpret_cast<const int32_t*>(ws + lay.off_pt);
-  a.pt_stride = gpages;
-  a.seq_lens = reinterpret_cast<const int32_t*>(ws + lay.off_len);
+  a.k_pool = a.v_pool = static_cast<const uint8_t*>(slab);
+  a.k_scales = a.v_scales = scaled(dtype) ? scales : nullptr;
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.seq_lens = seq_lens;
   a.batch = batch;
   a.n_q_heads = n_q_heads;
   a.n_kv_heads = 1;
   a.head_dim_qk = kvq::kMlaDqk;
   a.head_dim_v = kvq::kMlaDv;
-  a.max_pages = gpages;
-  a.num_pages = (int64_t)batch * gpages;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
   a.sm_scale = sm_scale;
   a.out = static_cast<uint16_t*>(out_bf16);
   a.lse = lse;
-  a.workspace = ws + lay.off_dense;
-  e = kvq::launch_mla_decode(a, lay.dense, num_cus_current(), stream);
+  a.workspace = workspace;
+  a.topk = topk_idx;
+  a.topk_stride = topk_stride;
+  a.topk_k = topk;
+  hipError_t e = kvq::launch_mla_decode(a, lay.dense, num_cus_current(), stream);
   if (e != hipSuccess) return hip_fail(e, "kvq_sparse_mla_decode");
   return ok();
 }

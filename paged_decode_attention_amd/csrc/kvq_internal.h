@@ -161,6 +161,12 @@ struct DecodeArgs {
   // the lengths on the host too (0: unknown); the launch then holds no
   // workgroup beyond it.  The kernels themselves plan from seq_lens.
   int64_t items_hint = 0;
+  // Sparse decode over the slab (null otherwise): sequence b attends to the
+  // positions listed at topk[b * topk_stride + i], i < topk_k, instead of
+  // its first seq_lens[b] positions.
+  const int32_t* topk = nullptr;
+  int64_t topk_stride = 0;
+  int topk_k = 0;
 };
 
 constexpr int kExtendMaxNew = 65536;  // new tokens per sequence, extend attention
@@ -219,28 +225,14 @@ hipError_t launch_zero_words(void* p, size_t words, hipStream_t s);
 // decode then attends to in full.
 constexpr int kSparseMaxK = 2048;
 
-struct SparseArgs {
-  const int32_t* topk;
-  int64_t topk_stride;
-  int k;
-  const int32_t* page_table;
-  int64_t pt_stride;
-  const int32_t* seq_lens;
-  int max_pages;
-  int64_t num_pages;
-  const uint8_t* slab;
-  const uint16_t* scales;  // null for the types without a scale buffer
-  void* workspace;
-};
-
+// The sparse decode: the slab kernel's plan over lists of k entries (k
+// rounded up to a page), which is also the whole workspace.
 struct SparseLayout {
-  int kk, row_bytes;
-  DecodePlan dense;  // the slab decode over the compact sequences
-  size_t off_dense, off_slab, off_scales, off_pt, off_len, bytes;
+  int kk;
+  DecodePlan dense;
+  size_t bytes;
 };
 
 bool plan_sparse(int qtype, int batch, int n_q_heads, int k, SparseLayout* lay, const char** why);
-hipError_t launch_sparse_gather(const SparseArgs& s, const SparseLayout& lay, int batch,
-                                hipStream_t stream);
 
 }  // namespace kvq

@@ -33,6 +33,14 @@
 // sequence that fits one item is written directly; otherwise each item
 // stores its normalized output (bf16) and (m, l) for every head, and
 // mla_merge_kernel combines them.
+//
+// Sparse top-k decode ([PR25] SPARSE_MLA_DECODE: K listed tokens per query;
+// [PR113] §Testing: masked (-1) columns) is the same kernel with the list in
+// place of the sequence: softmax attention over a set of rows does not depend
+// on their order, so entry i of a list is token i of a sequence of K tokens,
+// read from the slab row its position maps to through the page table, and an
+// entry outside the sequence or on a missing page is a masked token.  Every
+// list has K entries, so the items need no lengths from the device.
 #include <type_traits>
 
 #include "kvq_attn.h"
@@ -179,6 +187,7 @@ struct MlaRaw {
   uint32_t vs[4];
   uint32_t r[MlaGeo<QT>::RW];
   uint32_t rs;
+  uint32_t okm;  // sparse lists: bit i for token 4*q4 + i, bit 4 for rope token rt (listed row present)
 };
 
 // The slab's code loads use the default cache policy: unlike the
@@ -257,7 +266,29 @@ __device__ __forceinline__ int64_t mla_row(const DecodeArgs& a, int v) {
   return i < a.q_start[s + 1] - a.q_start[s] ? (int64_t)a.q_start[s] + i : -1;
 }
 
-template <int QT>
+// Global loads of N dwords at a byte address (the sparse lists' rows, each
+// at its own address); the default cache policy, as kSlabLoadPolicy.
+template <int N>
+__device__ __forceinline__ void glb_load_dw(const uint8_t* ptr, uint32_t* o) {
+  if constexpr (N == 8) {
+    glb_load_dw<4>(ptr, o);
+    glb_load_dw<4>(ptr + 16, o + 4);
+  } else if constexpr (N == 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ptr);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  } else {
+    static_assert(N == 2, "load width");
+    const u32x2 v = *reinterpret_cast<const u32x2*>(ptr);
+    o[0] = v.x; o[1] = v.y;
+  }
+}
+
+// SP: a sparse list per sequence (a.topk).  The list's entries take the
+// places of the sequence's positions: every sequence has topk_k of them, in
+// ceil(topk_k / item_tokens) items; an entry's row in the slab is looked up
+// once per item (the position through the page table, into s_rows), and an
+// entry that is not taken is a masked token.
+template <int QT, bool SP>
 __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
   using Gm = MlaGeo<QT>;
   constexpr int ESZ = Gm::ESZ, ROWB = Gm::ROWB, PAGEB = Gm::PAGEB, SCLB = Gm::SCLB;
@@ -271,7 +302,9 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
   auto vbuf = [&](int buf) { return s_tiles + 2 * kTile * kKS + buf * kVtElems; };
   __shared__ int s_wave[kW];
   __shared__ int s_flag[3];  // per-tile restart votes, rotating
-  extern __shared__ int s_prefix[];  // [batch + 1]
+  extern __shared__ int s_prefix[];  // [batch + 1] (SP: unused)
+  // SP: slab row of each of the item's entries (-1: not taken)
+  __shared__ int s_rows[SP ? kMlaMaxItemPages * kPageSize : 1];
 
   const DecodeArgs& a = p.a;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -279,19 +312,28 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
   const int n16 = lane & 15, g = lane >> 4;
   const int Hq = a.n_q_heads;
 
-  build_prefix_with<kT>(a, p.item_tokens, 1, s_prefix, s_wave,
-                        [&](int v) { return mla_len(a, v); });
-  const int total = s_prefix[a.batch];
-  if (blockIdx.x == 0)
-    for (int b = tid; b <= a.batch; b += kT) p.prefix[b] = s_prefix[b];
-  // a sequence with no valid length has no items: its output is 0, lse -inf
-  for (int b = blockIdx.x; b < a.batch; b += gridDim.x) {
-    if (s_prefix[b] != s_prefix[b + 1]) continue;
-    const int64_t row = mla_row(a, b);
-    if (row < 0) continue;  // no such new token
-    for (int i = tid; i < Hq * kDv; i += kT) a.out[row * Hq * kDv + i] = 0;
-    if (a.lse)
-      for (int h = tid; h < Hq; h += kT) a.lse[row * Hq + h] = -INFINITY;
+  // SP: every list has the same number of entries, so the same item count
+  const int sp_items = SP ? (a.topk_k + p.item_tokens - 1) / p.item_tokens : 0;
+  int total;
+  if constexpr (SP) {
+    total = a.batch * sp_items;
+    if (blockIdx.x == 0)
+      for (int b = tid; b <= a.batch; b += kT) p.prefix[b] = b * sp_items;
+  } else {
+    build_prefix_with<kT>(a, p.item_tokens, 1, s_prefix, s_wave,
+                          [&](int v) { return mla_len(a, v); });
+    total = s_prefix[a.batch];
+    if (blockIdx.x == 0)
+      for (int b = tid; b <= a.batch; b += kT) p.prefix[b] = s_prefix[b];
+    // a sequence with no valid length has no items: its output is 0, lse -inf
+    for (int b = blockIdx.x; b < a.batch; b += gridDim.x) {
+      if (s_prefix[b] != s_prefix[b + 1]) continue;
+      const int64_t row = mla_row(a, b);
+      if (row < 0) continue;  // no such new token
+      for (int i = tid; i < Hq * kDv; i += kT) a.out[row * Hq * kDv + i] = 0;
+      if (a.lse)
+        for (int h = tid; h < Hq; h += kT) a.lse[row * Hq + h] = -INFINITY;
+    }
   }
 
   // ---- tile geometry ----------------------------------------------------------------
@@ -314,14 +356,20 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     // ---- describe the item (uniform over the block) ------------------------------
-    int lo = 0, hi = a.batch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_prefix[mid] <= item) lo = mid; else hi = mid - 1;
+    int b, chunk;
+    if constexpr (SP) {
+      b = item / sp_items;
+      chunk = item - b * sp_items;
+    } else {
+      int lo = 0, hi = a.batch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_prefix[mid] <= item) lo = mid; else hi = mid - 1;
+      }
+      b = lo;
+      chunk = item - s_prefix[b];
     }
-    const int b = lo;
-    const int chunk = item - s_prefix[b];
-    const int L = mla_len(a, b);
+    const int L = SP ? a.topk_k : mla_len(a, b);
     const int64_t orow = mla_row(a, b);  // valid: b has work
     const int nc = (L + p.item_tokens - 1) / p.item_tokens;
     const int t0 = chunk * p.item_tokens;
@@ -331,7 +379,7 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
 
     // page ids of the item: lane k holds page column t0/16 + k; masked -> -1
     int pid = -1;
-    if (lane < npages) {
+    if (!SP && lane < npages) {
       const int v = a.page_table[(int64_t)mla_pt_row(a, b) * a.pt_stride + t0 / kPageSize + lane];
       pid = (v >= 0 && (int64_t)v < a.num_pages) ? v : -1;
     }
@@ -346,6 +394,23 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
     // after the first tile's codes)
     u32x4 qr[2][kNB];
 
+    if constexpr (SP) {
+      // the slab row of each entry of the item: taken when 0 <= position <
+      // the sequence's length and its page is present (the earlier readers
+      // of s_rows are past the previous item's last tile barrier)
+      const int Ls = clamped_len(a, b);
+      for (int e = tid; e < nt; e += kT) {
+        const int pos = a.topk[(int64_t)b * a.topk_stride + t0 + e];
+        int row = -1;
+        if (pos >= 0 && pos < Ls) {
+          const int pg = a.page_table[(int64_t)b * a.pt_stride + pos / kPageSize];
+          if (pg >= 0 && (int64_t)pg < a.num_pages) row = pg * kPageSize + pos % kPageSize;
+        }
+        s_rows[e] = row;
+      }
+      __syncthreads();
+    }
+
     auto load_tile = [&](int j, MlaRaw<QT>& R) {
       const int t = opaque(tid);
       const int l = t & 63, q = 2 * (t >> 6) + ((l >> 3) & 1), u = (l & 7) | ((l >> 4) << 3);
@@ -355,6 +420,41 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
       const uint32_t roff = (uint32_t)((rt & (kPageSize - 1)) * ROWB +
                                        (QT == QT_DSM ? kDsmLatent + 16 + 16 * p8 : (kDv + 8 * p8) * ESZ));
       const uint32_t rsoff = (uint32_t)((rt & (kPageSize - 1)) * kNB * 2 + (kDv / 32) * 2);
+      if constexpr (SP) {
+        // each token at its own row (row 0 stands in for an entry not taken)
+        const int base = kTile * j;
+        int rr[4];
+        uint32_t okm = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = base + 4 * q + i;
+          const int r = e < nt ? s_rows[e] : -1;
+          okm |= (r >= 0 ? 1u : 0u) << i;
+          rr[i] = max(r, 0);
+        }
+        const int er = base + rt;
+        const int rrow = er < nt ? s_rows[er] : -1;
+        okm |= (rrow >= 0 ? 1u : 0u) << 4;
+        const int64_t rb = (int64_t)max(rrow, 0);
+        R.okm = okm;
+        const uint8_t* slab = a.k_pool;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) glb_load_dw<VW>(slab + (int64_t)rr[i] * ROWB + u * 16 * ESZ, R.v[i]);
+        glb_load_dw<RW>(slab + rb * ROWB + (roff - (uint32_t)((rt & (kPageSize - 1)) * ROWB)), R.r);
+        if constexpr (QT == QT_DSM) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            R.vs[i] = *reinterpret_cast<const uint32_t*>(slab + (int64_t)rr[i] * ROWB + kDsmLatent + 4 * (u >> 3));
+        }
+        if constexpr (qt_scaled(QT)) {
+          const uint8_t* sc = reinterpret_cast<const uint8_t*>(a.k_scales);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            R.vs[i] = *reinterpret_cast<const uint32_t*>(sc + (int64_t)rr[i] * (kNB * 2) + (u >> 2) * 4);
+          R.rs = *reinterpret_cast<const uint32_t*>(sc + rb * (kNB * 2) + (kDv / 32) * 2);
+        }
+        return;
+      }
       const int P = max(__builtin_amdgcn_readfirstlane(page_of(j, wpage)), 0);
       const auto rc = page_rsrc(a.k_pool + (int64_t)P * PAGEB, PAGEB);
 #pragma unroll
@@ -400,14 +500,14 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
       st.vb = lds_addr(vbuf(buf)) + (uint32_t)(vt_index(16 * u, 4 * q) * 2);
       st.rb = lds_addr(kbuf(buf)) + (uint32_t)(row_r * kKS * 2 + (kDv + 8 * p8) * 2);
       st.h0 = (u >> 2) & 1;
-      const bool page_ok = page_of(j, wpage) >= 0;
+      const bool page_ok = SP || page_of(j, wpage) >= 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        st.ok[i] = page_ok && (kTile * j + 4 * q + i < nt);
+        st.ok[i] = page_ok && (kTile * j + 4 * q + i < nt) && (!SP || ((R.okm >> i) & 1u));
         st.sv[i] = (QT == QT_DSM) ? __uint_as_float(R.vs[i])
                    : qt_scaled(QT) ? scale_half(R.vs[i], ((u >> 1) & 1) * 16) : 1.0f;
       }
-      st.okr = page_ok && (kTile * j + rt < nt);
+      st.okr = page_ok && (kTile * j + rt < nt) && (!SP || ((R.okm >> 4) & 1u));
     };
     auto store_step = [&](auto sc, const MlaRaw<QT>& R) {
       constexpr int S = decltype(sc)::value;
@@ -497,8 +597,16 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
       }
       mfma16_v_settle(S[0][0], S[0][1], S[1][0], S[1][1]);
       // lane group g holds tokens 8g + 4tt + r: page 0 for g < 2
-      const bool ok0 = page_of(j, 0) >= 0, ok1 = page_of(j, 1) >= 0;
-      const bool pok = (g < 2) ? ok0 : ok1;
+      bool pok;
+      uint64_t tmask = 0;  // SP: the tile's listed rows present
+      if constexpr (SP) {
+        const int e = kTile * j + lane;
+        tmask = __builtin_amdgcn_ballot_w64(lane < kTile && e < nt && s_rows[e] >= 0);
+        pok = true;
+      } else {
+        const bool ok0 = page_of(j, 0) >= 0, ok1 = page_of(j, 1) >= 0;
+        pok = (g < 2) ? ok0 : ok1;
+      }
       u32x4 pk[2];
       bool over = false;
 #pragma unroll
@@ -509,7 +617,7 @@ __global__ __launch_bounds__(kT) void mla_decode_kernel(MlaParams p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int tok = kTile * j + 8 * g + 4 * tt + r;
-            const bool ok = pok && tok < nt;
+            const bool ok = SP ? ((tmask >> (8 * g + 4 * tt + r)) & 1u) != 0 : (pok && tok < nt);
             const float v = ok ? S[tt][ht][r] * p.scale_log2 : -INFINITY;
             sc[4 * tt + r] = v;
             t = fmaxf(t, v);
@@ -789,8 +897,12 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(MlaParams p) {
 
 template <int QT>
 hipError_t launch_q(const MlaParams& mp, int grid, int merge_grid, hipStream_t s) {
-  const size_t dyn = (size_t)(mp.a.batch + 1) * sizeof(int);
-  mla_decode_kernel<QT><<<grid, kT, dyn, s>>>(mp);
+  if (mp.a.topk) {
+    mla_decode_kernel<QT, true><<<grid, kT, 0, s>>>(mp);
+  } else {
+    const size_t dyn = (size_t)(mp.a.batch + 1) * sizeof(int);
+    mla_decode_kernel<QT, false><<<grid, kT, dyn, s>>>(mp);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || merge_grid == 0) return e;
   mla_merge_kernel<<<merge_grid, kMergeThreads, 0, s>>>(mp);
@@ -813,7 +925,8 @@ hipError_t launch_mla_decode(const DecodeArgs& a, const DecodePlan& plan, int nu
   if (grid > plan.max_items) grid = plan.max_items;
   if (a.items_hint > 0 && grid > a.items_hint) grid = a.items_hint;  // exact from host lengths
   if (grid < 1) grid = 1;
-  const int64_t max_chunks = (a.max_pages + plan.item_pages - 1) / plan.item_pages;
+  const int64_t max_chunks = a.topk ? (a.topk_k + mp.item_tokens - 1) / mp.item_tokens
+                                    : (a.max_pages + plan.item_pages - 1) / plan.item_pages;
   const int merge_grid = (max_chunks > 1) ? a.batch * a.n_q_heads * 2 : 0;
   switch (a.qtype) {
     case QT_BF16: return launch_q<QT_BF16>(mp, (int)grid, merge_grid, s);
