@@ -107,3 +107,14 @@ def test_sparse_full_size_slab():
     rng = np.random.default_rng(256)
     topk = np.stack([rng.choice(int(L), 256, replace=False) for L in wl.seq_lens]).astype(np.int32)
     run(wl, "fp8_e4m3", topk)
+
+
+def test_sparse_longest_lists_in_the_largest_items():
+    """130 lists of the most entries a call takes (2048), 16 heads: 130 x 64
+    tiles over 256 workgroups asks for 33 tiles per work item, so items
+    reach their cap of 1024 entries; each list is two items, and an item's
+    row list fills the kernel's LDS array."""
+    lens = np.random.default_rng(9).integers(0, 2500, 130)
+    lens[3] = 0
+    wl = mla_workload(16, lens.tolist(), 160, seed=9, mask_frac=0.1)
+    run(wl, "fp8_e4m3", make_lists(np.random.default_rng(2048), wl, 2048))
