@@ -84,9 +84,9 @@ def test_captured_step_replays_match_eager():
 
 def test_captured_extend_and_sparse_replay_match_eager():
     """Extend attention (split units merged by their last workgroup, whose
-    arrival counters reset themselves) and the sparse MLA decode (gather, slab
-    decode, merge) captured once and replayed: every replay reproduces the
-    eager outputs bit for bit."""
+    arrival counters reset themselves) and the sparse MLA decode (the slab
+    decode over the listed rows, then the merge) captured once and replayed:
+    every replay reproduces the eager outputs bit for bit."""
     k = kvq()
     torch.cuda.synchronize()
     strm = torch.cuda.Stream()
