@@ -151,6 +151,14 @@ __device__ __forceinline__ void transpose4x4(const uint32_t* in, uint32_t* out) 
 // POL: the cache policy of the K/V loads -- non-temporal where each page is
 // read by one work item (the decode; extend with few tile groups per kv
 // head), the default where several items read it and can meet it in the L2.
+// Two consecutive floats with one agent-scope 8-byte load (the split-K
+// partials written by other workgroups).
+__device__ __forceinline__ float2 load_agent2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
 template <int QT, int D, bool EXT, int TN, bool SUB, int POL>
 __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
   using Gm = MfGeo<QT, D>;
@@ -690,48 +698,63 @@ __global__ __launch_bounds__(kT) void gqa_mfma_kernel(MfParams p) {
       }
       __syncthreads();
       if (s_last) {
+        // Each thread merges kE consecutive elements of one column straight
+        // from global memory (agent-scope loads, as the partials were
+        // stored): every chunk's m for the maximum and the first kG chunks'
+        // (m, l) and rows are requested together, later chunks kG at a time.
+        // No LDS, no barrier.
         const int first = s_prefix[b] + u;  // item of chunk c: first + c * units
-        for (int idx = tid; idx < nc * GTU; idx += kT) {
-          const int c = idx / GTU, h = idx - c * GTU;
-          s_red[idx] = load_agent(&p.part_ml[((int64_t)(first + c * units) * GTU + h) * 2]);
-        }
-        __syncthreads();
-        for (int h = wave; h < GTU; h += kW) {
+        const int64_t cstride = (int64_t)units * GTU * D;  // floats between chunks' rows
+        const int64_t mstride = (int64_t)units * GTU * 2;  // ... and (m, l) pairs
+        constexpr int kE = 16, kG = 4;
+        for (int w0 = tid; w0 < GTU * (D / kE); w0 += kT) {
+          const int h = w0 / (D / kE), d0 = (w0 - h * (D / kE)) * kE;
+          const float* ml = p.part_ml + ((int64_t)first * GTU + h) * 2;
+          const float* src = p.part_acc + ((int64_t)first * GTU + h) * D + d0;
+          float2 mlc[kG], x[kG][kE / 2];
+          auto load_group = [&](int c0) {
+#pragma unroll
+            for (int j = 0; j < kG; ++j) {
+              const bool in = c0 + j < nc;
+              mlc[j] = in ? load_agent2(ml + (c0 + j) * mstride) : make_float2(-INFINITY, 0.0f);
+#pragma unroll
+              for (int q = 0; q < kE / 2; ++q)
+                x[j][q] = in ? load_agent2(src + (c0 + j) * cstride + 2 * q) : make_float2(0.0f, 0.0f);
+            }
+          };
+          load_group(0);
           float M = -INFINITY;
-          for (int c = lane; c < nc; c += 64) M = fmaxf(M, s_red[c * GTU + h]);
-          M = stride_max<1>(M);
-          float Ls = 0.0f;
-          for (int c = lane; c < nc; c += 64) {
-            const float w = exp2_rel(s_red[c * GTU + h], M);
-            Ls += w * load_agent(&p.part_ml[((int64_t)(first + c * units) * GTU + h) * 2 + 1]);
-            s_red[c * GTU + h] = w;
-          }
-          Ls = stride_sum<1>(Ls);
-          if (lane == 0) {
-            s_hm[h][0] = M;
-            s_hm[h][1] = Ls;
-          }
-        }
-        __syncthreads();
-        for (int idx = tid; idx < GTU * D; idx += kT) {
-          const int h = idx / D, d = idx - h * D;
-          const float* src = p.part_acc + ((int64_t)first * GTU + h) * D + d;
-          const int64_t cstride = (int64_t)units * GTU * D;
-          float v = 0.0f;
           for (int c0 = 0; c0 < nc; c0 += 16) {
-            float x[16];
+            float mc[16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) x[j] = (c0 + j < nc) ? load_agent(src + (c0 + j) * cstride) : 0.0f;
+            for (int j = 0; j < 16; ++j) mc[j] = (c0 + j < nc) ? load_agent(ml + (c0 + j) * mstride) : -INFINITY;
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-              if (c0 + j < nc) v += s_red[(c0 + j) * GTU + h] * x[j];
+            for (int j = 0; j < 16; ++j) M = fmaxf(M, mc[j]);
           }
-          const float M = s_hm[h][0], Ls = s_hm[h][1];
+          float v[kE], Ls = 0.0f;
+#pragma unroll
+          for (int e = 0; e < kE; ++e) v[e] = 0.0f;
+          for (int c0 = 0; c0 < nc; c0 += kG) {
+            if (c0 > 0) load_group(c0);
+#pragma unroll
+            for (int j = 0; j < kG; ++j) {
+              const float w = exp2_rel(mlc[j].x, M);  // 0 past the last chunk (m = -inf)
+              Ls += w * mlc[j].y;
+#pragma unroll
+              for (int q = 0; q < kE / 2; ++q) {
+                v[2 * q] += w * x[j][q].x;
+                v[2 * q + 1] += w * x[j][q].y;
+              }
+            }
+          }
           const int64_t orow = EXT ? query_row(a, b, kvh, col0 + h, G)
                                    : (int64_t)b * a.n_q_heads + kvh * G + col0 + h;
           if (orow >= 0) {
-            a.out[orow * D + d] = (uint16_t)bf16_rne(Ls > 0.0f ? v / Ls : 0.0f);
-            if (d == 0 && a.lse)
+            uint32_t* o = reinterpret_cast<uint32_t*>(a.out + orow * D + d0);
+#pragma unroll
+            for (int q = 0; q < kE / 2; ++q)
+              o[q] = pack_bf16x2(Ls > 0.0f ? v[2 * q] / Ls : 0.0f, Ls > 0.0f ? v[2 * q + 1] / Ls : 0.0f);
+            if (d0 == 0 && a.lse)
               a.lse[orow] = (M == -INFINITY) ? -INFINITY : (M + log2f(Ls)) * kLn2;
           }
         }
